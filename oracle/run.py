@@ -1,0 +1,114 @@
+"""Expected results of one decode step, from the seeded inputs.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+Takes the dict made by ``workloads.make_inputs`` and computes, in fp64:
+the query (projection or given), the cache contents after the step's append
+(prefilled tokens plus the new token at position prefill_len), and the
+attention output for the requested sequences. FP8 caches are quantised with
+this package's own codec.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from . import layout, mfa
+
+DEFAULT_EPS = 1e-6
+
+
+def query(inp: Dict, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """q [B][H][d] in fp64."""
+    w = inp["workload"]
+    if w.has_qproj:
+        a = w.act_dtype
+        return mfa.query_projection(
+            mfa.stored_to_f64(inp["x"], a), mfa.stored_to_f64(inp["w_qdown"], a),
+            np.asarray(inp["g"], dtype=np.float64), mfa.stored_to_f64(inp["w_qup"], a),
+            w.heads, w.head_dim, eps)
+    return mfa.stored_to_f64(inp["q"], w.act_dtype).reshape(w.batch, w.heads, w.head_dim)
+
+
+def sequence_tokens(inp: Dict, b: int):
+    """Stored logical K and V rows (prefill + appended token) of sequence b."""
+    o = inp["ctx_offsets"]
+    k = np.concatenate([inp["k_ctx"][o[b]:o[b + 1]], inp["k_new"][b:b + 1]])
+    v = np.concatenate([inp["v_ctx"][o[b]:o[b + 1]], inp["v_new"][b:b + 1]])
+    return k, v
+
+
+def sequence_kv_f64(inp: Dict, b: int):
+    """fp64 values the attention of sequence b sees, plus (for FP8) the codes
+    and scales: returns (k, v, extra) with extra = (kc, ks, vc, vs) or None."""
+    w = inp["workload"]
+    k, v = sequence_tokens(inp, b)
+    if w.kv_dtype == "fp8":
+        kf = mfa.bf16_bits_to_f64(k)
+        vf = mfa.bf16_bits_to_f64(v)
+        kc, ks = mfa.quantize_tokens(kf)
+        vc, vs = mfa.quantize_tokens(vf)
+        return (mfa.dequantize_tokens(kc, ks), mfa.dequantize_tokens(vc, vs),
+                (kc, ks, vc, vs))
+    return mfa.stored_to_f64(k, w.kv_dtype), mfa.stored_to_f64(v, w.kv_dtype), None
+
+
+def physical_cache(inp: Dict, seqs: Sequence[int]):
+    """Token-major fp64 physical caches holding the given sequences (zeros
+    elsewhere), filled through the block table (or the contiguous mapping)."""
+    w = inp["workload"]
+    nrows = inp["num_blocks"] * mfa.BLOCK_TOKENS
+    kc = np.zeros((nrows, w.head_dim))
+    vc = np.zeros((nrows, w.head_dim))
+    for b in seqs:
+        k, v, _ = sequence_kv_f64(inp, b)
+        mfa.scatter_tokens(kc, b, 0, k, inp["block_table"], inp["max_blocks_per_seq"])
+        mfa.scatter_tokens(vc, b, 0, v, inp["block_table"], inp["max_blocks_per_seq"])
+    return kc, vc
+
+
+def decode_step(inp: Dict, seqs: Optional[Sequence[int]] = None,
+                sm_scale: Optional[float] = None, eps: float = DEFAULT_EPS) -> Dict:
+    """q for all sequences and the attention output for ``seqs``."""
+    w = inp["workload"]
+    if seqs is None:
+        seqs = list(range(w.batch))
+    if sm_scale is None:
+        sm_scale = mfa.default_sm_scale(w.head_dim)
+    q = query(inp, eps)
+    kc, vc = physical_cache(inp, seqs)
+    o = mfa.decode_attention(q, kc, vc, inp["block_table"], inp["max_blocks_per_seq"],
+                             inp["seq_lens"], sm_scale, seqs=seqs)
+    return {"q": q, "o": o, "seqs": list(seqs)}
+
+
+def expected_cache_bytes(inp: Dict, seqs: Sequence[int]):
+    """Stored K/V (and FP8 scales) of the given sequences after the append, in
+    the library's documented block layout. Returns a dict of arrays indexed by
+    physical block, and the list of blocks the sequences own."""
+    w = inp["workload"]
+    nrows = inp["num_blocks"] * mfa.BLOCK_TOKENS
+    d = w.head_dim
+    store = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.kv_dtype]
+    krows = np.zeros((nrows, d), dtype=store)
+    vrows = np.zeros((nrows, d), dtype=store)
+    ks = np.zeros(nrows, dtype=np.float32)
+    vs = np.zeros(nrows, dtype=np.float32)
+    owned = []
+    for b in seqs:
+        L = int(inp["seq_lens"][b])
+        rows = mfa.physical_rows(b, L, inp["block_table"], inp["max_blocks_per_seq"])
+        owned.extend(sorted(set((rows // mfa.BLOCK_TOKENS).tolist())))
+        k, v = sequence_tokens(inp, b)
+        if w.kv_dtype == "fp8":
+            _, _, (kcodes, kscale, vcodes, vscale) = sequence_kv_f64(inp, b)
+            krows[rows], vrows[rows] = kcodes, vcodes
+            ks[rows], vs[rows] = kscale, vscale
+        else:
+            krows[rows], vrows[rows] = k, v
+    res = {"k": layout.k_blocks(krows), "v": layout.v_blocks(vrows)}
+    if w.kv_dtype == "fp8":
+        res["k_scale"] = layout.scale_blocks(ks)
+        res["v_scale"] = layout.scale_blocks(vs)
+    return res, owned

@@ -1,0 +1,333 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``check_*`` takes a namespace of oracle functions and returns a list of
+failure messages (empty = pinned). ``test_oracle.py`` runs them on the real
+oracle; ``test_oracle_mutants.py`` runs them on copies with a planted mistake
+and expects at least one failure, which shows that the pins would catch it.
+
+What pins what:
+* attention  -- pure-Python brute force; one token returns V exactly; constant
+  K returns the mean of V; two tokens follow the logistic closed form; a
+  dominant logit returns that token's V; a common shift of K along q leaves
+  the output unchanged; zero scale gives the mean of V; reordering tokens
+  changes nothing beyond rounding.
+* gather     -- a hand-worked block-table example; permuted physical blocks
+  give a bit-identical output.
+* split / combine -- any split count (with empty chunks) reproduces the
+  unsplit brute-force result; two hand-built partials merge by closed form.
+* rmsnorm / query projection -- output RMS equals 1 before the gain; scale
+  invariance; constant input gives the gain; identity down-projection reduces
+  to W_up x / rms(x); pure-Python brute force; head h owns columns h*d..h*d+d-1.
+* e4m3 -- torch's float8_e4m3fn decode of all 256 codes; anchor values of the
+  OCP format; round trip of every finite value; midpoints round to even;
+  torch's RNE cast on random values.
+* quantisation -- the amax element encodes to +-448; error within half an
+  e4m3 step times the scale; zero rows; sign kept.
+* cost -- the page's intensity 128 at 8-bit KV and effective rank 16,384.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import types
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def real_oracle():
+    from oracle import brute, cost, e4m3, mfa
+    return types.SimpleNamespace(
+        softmax_attention=mfa.softmax_attention,
+        physical_rows=mfa.physical_rows,
+        decode_attention=mfa.decode_attention,
+        scatter_tokens=mfa.scatter_tokens,
+        split_partials=mfa.split_partials,
+        combine=mfa.combine,
+        rmsnorm=mfa.rmsnorm,
+        query_projection=mfa.query_projection,
+        quantize_tokens=mfa.quantize_tokens,
+        dequantize_tokens=mfa.dequantize_tokens,
+        e4m3_decode=e4m3.decode,
+        e4m3_encode=e4m3.encode_rne,
+        arithmetic_intensity=cost.arithmetic_intensity,
+        effective_rank=cost.effective_rank,
+        kv_bytes_per_token=cost.kv_bytes_per_token,
+        brute=brute,
+    )
+
+
+def _close(a, b, tol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return a.shape == b.shape and np.all(np.abs(a - b) <= tol * (1.0 + np.abs(b)))
+
+
+# ---------------------------------------------------------------- attention
+def check_attention(O):
+    fails = []
+    rng = np.random.default_rng(1234)
+    # brute force on tiny random cases
+    for trial in range(12):
+        H = int(rng.integers(1, 5))
+        d = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 17))
+        dv = int(rng.integers(1, 9))
+        q = rng.standard_normal((H, d)) * 2
+        k = rng.standard_normal((L, d))
+        v = rng.standard_normal((L, dv))
+        sc = float(rng.uniform(0.1, 1.5))
+        got = O.softmax_attention(q, k, v, sc)
+        want = O.brute.attention(q.tolist(), k.tolist(), v.tolist(), sc)
+        if not _close(got, want, 1e-12):
+            fails.append(f"brute force mismatch H={H} d={d} L={L}")
+            break
+    # one token: exactly V for every head
+    q = rng.standard_normal((4, 8)); k = rng.standard_normal((1, 8)); v = rng.standard_normal((1, 8))
+    got = O.softmax_attention(q, k, v, 0.35)
+    if not np.array_equal(got, np.repeat(v, 4, axis=0)):
+        fails.append("L=1 does not return V exactly")
+    # constant K: mean of V
+    k = np.repeat(rng.standard_normal((1, 8)), 9, axis=0)
+    v = rng.standard_normal((9, 5))
+    got = O.softmax_attention(q, k, v, 0.7)
+    if not _close(got, np.repeat(v.mean(axis=0, keepdims=True), 4, axis=0), 1e-13):
+        fails.append("constant K does not give mean of V")
+    # two tokens: o = sigma(delta) v0 + (1 - sigma(delta)) v1
+    q = rng.standard_normal((3, 6)); k = rng.standard_normal((2, 6)); v = rng.standard_normal((2, 4))
+    sc = 0.5
+    got = O.softmax_attention(q, k, v, sc)
+    for h in range(3):
+        delta = sc * (q[h] @ k[0] - q[h] @ k[1])
+        a = 1.0 / (1.0 + math.exp(-delta))
+        if not _close(got[h], a * v[0] + (1 - a) * v[1], 1e-13):
+            fails.append("two-token logistic closed form fails")
+            break
+    # dominant logit: output equals that token's V
+    d = 8
+    k = np.zeros((5, d)); k[3, 0] = 1.0
+    q = np.zeros((2, d)); q[:, 0] = 2000.0
+    v = rng.standard_normal((5, 3))
+    got = O.softmax_attention(q, k, v, 1.0)
+    if not np.array_equal(got, np.repeat(v[3:4], 2, axis=0)):
+        fails.append("dominant logit does not select its V row")
+    # shifting every key by the same vector: logits of a head shift uniformly
+    q = rng.standard_normal((3, 6)); k = rng.standard_normal((7, 6)); v = rng.standard_normal((7, 6))
+    shift = rng.standard_normal(6)
+    a = O.softmax_attention(q, k, v, 0.4)
+    b = O.softmax_attention(q, k + shift, v, 0.4)
+    if not _close(a, b, 1e-12):
+        fails.append("common key shift changes the output")
+    # zero scale: uniform weights, mean of V
+    got = O.softmax_attention(q, k, v, 0.0)
+    if not _close(got, np.repeat(v.mean(axis=0, keepdims=True), 3, axis=0), 1e-13):
+        fails.append("zero scale does not give mean of V")
+    # token order does not matter
+    perm = rng.permutation(7)
+    b = O.softmax_attention(q, k[perm], v[perm], 0.4)
+    if not _close(a, b, 1e-12):
+        fails.append("token permutation changes the output")
+    return fails
+
+
+# ---------------------------------------------------------------- gather
+def check_gather(O):
+    fails = []
+    with open(os.path.join(GOLDEN, "gather_example.json")) as f:
+        ex = json.load(f)
+    bt = np.array(ex["block_table"], dtype=np.int32)
+    for c in ex["cases"]:
+        rows = O.physical_rows(c["seq"], c["length"], bt, ex["max_blocks_per_seq"])
+        if "rows" in c and rows.tolist() != c["rows"]:
+            fails.append(f"gather example rows {c}")
+        if "tokens" in c and rows[c["tokens"]].tolist() != c["rows_at_tokens"]:
+            fails.append(f"gather example tokens {c}")
+    cg = ex["contiguous"]
+    for c in cg["cases"]:
+        rows = O.physical_rows(c["seq"], c["length"], None, cg["max_blocks_per_seq"])
+        if rows[c["tokens"]].tolist() != c["rows_at_tokens"]:
+            fails.append(f"contiguous example {c}")
+    # permuted physical blocks: identical output
+    rng = np.random.default_rng(7)
+    B, H, d, L = 3, 4, 8, 150
+    nblk = 3
+    q = rng.standard_normal((B, H, d))
+    kl = rng.standard_normal((B, L, d))
+    vl = rng.standard_normal((B, L, d))
+    outs = []
+    for trial in range(2):
+        perm = rng.permutation(B * nblk).astype(np.int32)
+        bt = perm.reshape(B, nblk)
+        kc = np.zeros((B * nblk * 64, d)); vc = np.zeros_like(kc)
+        for b in range(B):
+            O.scatter_tokens(kc, b, 0, kl[b], bt, nblk)
+            O.scatter_tokens(vc, b, 0, vl[b], bt, nblk)
+        outs.append(O.decode_attention(q, kc, vc, bt, nblk, [L] * B, 0.3))
+    if not np.array_equal(outs[0], outs[1]):
+        fails.append("permuted physical blocks change the output")
+    direct = np.stack([O.brute.attention(q[b].tolist(), kl[b].tolist(), vl[b].tolist(), 0.3)
+                       for b in range(B)])
+    if not _close(outs[0], direct, 1e-12):
+        fails.append("paged attention differs from brute force on logical rows")
+    return fails
+
+
+# ---------------------------------------------------------------- split / combine
+def check_combine(O):
+    fails = []
+    rng = np.random.default_rng(99)
+    H, d, L = 3, 5, 37
+    q = rng.standard_normal((H, d)) * 1.5
+    k = rng.standard_normal((L, d)); v = rng.standard_normal((L, d))
+    want = np.array(O.brute.attention(q.tolist(), k.tolist(), v.tolist(), 0.6))
+    for S, chunk in ((1, 64), (2, 19), (3, 13), (32, 2), (32, 64)):
+        parts = O.split_partials(q, k, v, 0.6, chunk, S)
+        got = O.combine(parts)
+        if not _close(got, want, 1e-12):
+            fails.append(f"split S={S} chunk={chunk} differs from unsplit")
+    # hand-built: two partials of one head
+    o1, m1, l1 = np.array([[2.0, 4.0]]), np.array([1.0]), np.array([2.0])
+    o2, m2, l2 = np.array([[1.0, -1.0]]), np.array([3.0]), np.array([1.0])
+    e = math.exp(-2.0)
+    want = (e * o1[0] + o2[0]) / (e * 2.0 + 1.0)
+    empty = (np.zeros((1, 2)), np.array([-np.inf]), np.zeros(1))
+    got = O.combine([(o1, m1, l1), empty, (o2, m2, l2)])
+    if not _close(got[0], want, 1e-14):
+        fails.append("two-partial closed form fails")
+    return fails
+
+
+# ---------------------------------------------------------------- rmsnorm / qproj
+def check_qproj(O):
+    fails = []
+    rng = np.random.default_rng(5)
+    c = rng.standard_normal((3, 16)) * 3
+    n1 = O.rmsnorm(c, np.ones(16), 0.0)
+    if not _close(np.sqrt(np.mean(n1 * n1, axis=1)), np.ones(3), 1e-14):
+        fails.append("RMS of normalised rows is not 1")
+    g = 1 + 0.1 * rng.standard_normal(16)
+    if not _close(O.rmsnorm(c * 7.5, g, 0.0), O.rmsnorm(c, g, 0.0), 1e-14):
+        fails.append("rmsnorm not scale invariant")
+    if not _close(O.rmsnorm(np.full((1, 16), -2.5), g, 0.0)[0], -g, 1e-14):
+        fails.append("constant row does not give -g")
+    # identity down-projection, unit gain: q = W_up x / rms(x)
+    r, H, d = 8, 2, 3
+    x = rng.standard_normal((2, r))
+    wu = rng.standard_normal((H * d, r))
+    q = O.query_projection(x, np.eye(r), np.ones(r), wu, H, d, 0.0)
+    for b in range(2):
+        want = wu @ (x[b] / (np.linalg.norm(x[b]) / math.sqrt(r)))
+        if not _close(q[b].reshape(-1), want, 1e-13):
+            fails.append("identity down-projection closed form fails")
+            break
+    # brute force with real shapes (tiny) and eps
+    Dm, r, H, d = 6, 4, 2, 3
+    x = rng.standard_normal((2, Dm)); wd = rng.standard_normal((r, Dm))
+    g = 1 + 0.1 * rng.standard_normal(r); wu = rng.standard_normal((H * d, r))
+    got = O.query_projection(x, wd, g, wu, H, d, 1e-3)
+    want = np.array(O.brute.query_projection(x.tolist(), wd.tolist(), g.tolist(), wu.tolist(),
+                                             H, d, 1e-3))
+    if not _close(got, want, 1e-12):
+        fails.append("query projection differs from brute force")
+    # head mapping: W_up row h*d+j feeds head h, dim j
+    wu = np.zeros((H * d, r)); wu[1 * d + 2, 0] = 1.0
+    got = O.query_projection(x, wd, g, wu, H, d, 0.0)
+    nz = np.argwhere(np.abs(got) > 0)
+    if not (len(nz) > 0 and np.all(nz[:, 1] == 1) and np.all(nz[:, 2] == 2)):
+        fails.append("head mapping of W_up rows is wrong")
+    return fails
+
+
+# ---------------------------------------------------------------- e4m3
+def check_e4m3(O):
+    import torch
+    fails = []
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    if not same.all():
+        fails.append(f"decode differs from torch at codes {np.flatnonzero(~same)[:8]}")
+    anchors = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+               0x38: 1.0, 0x40: 2.0, 0xB8: -1.0, 0x00: 0.0, 0x07: 7 * 2.0 ** -9}
+    for c, val in anchors.items():
+        if O.e4m3_decode(np.array([c], dtype=np.uint8))[0] != val:
+            fails.append(f"anchor code {c:#x} != {val}")
+    if not (np.isnan(O.e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))).all()):
+        fails.append("NaN codes")
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    rt = O.e4m3_encode(O.e4m3_decode(finite))
+    if not np.array_equal(rt, finite):
+        fails.append("round trip of finite values fails")
+    pos = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = O.e4m3_encode(mids)
+    if not np.all(enc % 2 == 0):
+        fails.append("midpoints do not round to the even code")
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 0.05, 1, 30, 200)]
+                          + [mids, -mids]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(vals.astype(np.float64))
+    # torch drops the sign of an exact zero result only for +0 inputs; compare magnitudes
+    # of codes that decode to zero, and exact codes elsewhere
+    dz = O.e4m3_decode(got) == 0
+    if not (np.array_equal(got[~dz], ref[~dz]) and np.all((ref[dz] & 0x7F) == 0)):
+        bad = np.flatnonzero((got != ref) & ~dz)[:5]
+        fails.append(f"encode differs from torch RNE at {vals[bad]}")
+    return fails
+
+
+def check_quantize(O):
+    fails = []
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((50, 256)) * rng.uniform(1e-3, 50, size=(50, 1))).astype(np.float32)
+    x[7] = 0.0
+    x[9, :] = -np.abs(x[9, :])
+    codes, s = O.quantize_tokens(x.astype(np.float64))
+    deq = O.dequantize_tokens(codes, s)
+    for i in range(50):
+        if i == 7:
+            if not (s[i] == 1.0 and np.all(codes[i] == 0)):
+                fails.append("zero row not (scale 1, code 0)")
+            continue
+        j = int(np.argmax(np.abs(x[i])))
+        if (codes[i, j] & 0x7F) != 0x7E:
+            fails.append(f"amax element of row {i} not coded as 448")
+            break
+    # error bound: half a step of the e4m3 grid at that magnitude, times s
+    y = np.abs(deq / s[:, None].astype(np.float64))
+    step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+    err = np.abs(deq - x) / s[:, None]
+    if not np.all(err <= step / 2 * (1 + 1e-6) + 1e-30):
+        fails.append("quantisation error beyond half a step")
+    if not np.all((codes[9] & 0x80) == 0x80):
+        fails.append("sign lost for negative row")
+    return fails
+
+
+def check_cost(O):
+    fails = []
+    with open(os.path.join(GOLDEN, "page_figures.json")) as f:
+        figs = {e["id"]: e["value"] for e in json.load(f)["figures"]}
+    if O.arithmetic_intensity(64, 256, 1) != figs["mfa_ai_8bit"]:
+        fails.append("intensity at 8-bit KV != page figure")
+    if O.effective_rank(64, 256) != figs["mfa_effective_rank"]:
+        fails.append("effective rank != page figure")
+    if O.kv_bytes_per_token(256, 2) != 1024:
+        fails.append("bf16 KV bytes per token")
+    return fails
+
+
+ALL_CHECKS = (check_attention, check_gather, check_combine, check_qproj, check_e4m3,
+              check_quantize, check_cost)
+
+
+def run_all(O):
+    fails = []
+    for chk in ALL_CHECKS:
+        fails.extend(f"{chk.__name__}: {m}" for m in chk(O))
+    return fails

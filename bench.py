@@ -1,0 +1,215 @@
+"""Benchmark of one MFA decode step on one MI355X.
+
+A step is the whole hot path over one batch: query path (down-projection,
+RMSNorm, up-projection), KV append of the new token, split-KV decode
+attention, split combine -- each one libmfa C-ABI call on one stream.
+Default workload: the Step-3-shaped bf16 decode (batch 32, hidden 7168,
+query rank 2048, 64 heads x 256 sharing one KV head, 4096-token contiguous
+cache). Inputs are seeded and synthetic and resident in HBM before timing;
+``--rotate`` independent copies of cache and weights are cycled so that the
+256 MB last-level cache cannot hold a step's working set.
+
+Prints one JSON line (see the project's measurement contract): throughput in
+decode tokens/s, the attention kernel's roofline (algorithmic KV bytes per
+launch / its average duration from HIP events recorded around every launch
+inside the timed region), and the fp64 oracle timed on a bounded sample on
+the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload index 1..5")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
+    ap.add_argument("--splits", type=int, default=0, help="override split count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample")
+    return ap.parse_args()
+
+
+def kv_bytes_per_token(w) -> int:
+    """K row + V row (+ one fp32 scale each for FP8): 2*d*b (+8)."""
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    return 2 * w.head_dim * elem + (8 if w.kv_dtype == "fp8" else 0)
+
+
+def counters_for(workload_name: str, kernel_sig: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary,
+    only if it was taken on the current attention kernel source."""
+    path = os.path.join(PROFILE_DIR, f"attn_counters_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256") != kernel_sig:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def kernel_source_sig() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("attn_mfma.hip", "device_common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "decode_attention_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(inp, n_seq: int):
+    """fp64 oracle on the first n_seq sequences of the same inputs (query
+    path for those rows, cache fill, attention). Returns the record."""
+    import copy
+
+    import numpy as np
+    from oracle import run as orun
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w = inp["workload"]
+    sub = copy.copy(inp)
+    seqs = list(range(n_seq))
+    t0 = time.perf_counter()
+    orun.decode_step(sub, seqs=seqs)
+    dt = time.perf_counter() - t0
+    toks = sum(int(inp["seq_lens"][b]) for b in seqs)
+    return {"value": n_seq / dt, "unit": "decode tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.batch} sequences of workload {w.name} "
+                      f"({toks} cached tokens, full query path for all rows), {dt:.1f} s fp64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_attention_02_amd as mfa
+    import workloads
+    from decode_attention_02_amd.step import DecodeStep, prefill
+
+    mfa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.config]
+    inp = workloads.make_inputs(args.config)
+    T = workloads.to_torch(inp, dev)
+    act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
+    B = w.batch
+    maxlen = int(inp["seq_lens"].max())
+    kvb = kv_bytes_per_token(w)
+    kv_bytes = int(inp["seq_lens"].sum()) * kvb
+    w_bytes = 0
+    if w.has_qproj:
+        w_bytes = (T["w_qdown"].numel() + T["w_qup"].numel()) * T["w_qup"].element_size()
+    rotate = args.rotate or max(2, min(8, -(-2 * 256 * 2 ** 20 // max(kv_bytes + w_bytes, 1))))
+
+    sets = []
+    for r in range(rotate):
+        cache = mfa.KVCache(inp["num_blocks"], w.head_dim, w.kv_dtype, inp["max_blocks_per_seq"],
+                            block_table=T["block_table"], device=dev, zero=False)
+        prefill(cache, T["k_ctx"], T["v_ctx"], inp["ctx_offsets"], inp["prefill_lens"])
+        ns = args.splits or w.num_splits
+        step = DecodeStep(cache, B, w.heads, maxlen, hidden=w.hidden, q_rank=w.q_rank,
+                          act_dtype=act, num_splits=ns, device=dev)
+        wts = None
+        if w.has_qproj:
+            wts = (T["w_qdown"].clone(), T["g"].clone(), T["w_qup"].clone())
+        sets.append((step, wts))
+    torch.cuda.synchronize()
+
+    def one(i, ev=None):
+        step, wts = sets[i % rotate]
+        if w.has_qproj:
+            q = step.query(T["x"], *wts)
+        else:
+            q = T["q"]
+        step.append(T["k_new"], T["v_new"], T["prefill_lens"])
+        if ev is not None:
+            ev[0].record()
+        if step.num_splits > 1:
+            mfa.decode_attn(q, step.cache, T["seq_lens"], step.max_seq_len, step.sm_scale,
+                            step.num_splits, step.chunk_tokens, workspace=step.split_ws,
+                            combine=False)
+            if ev is not None:
+                ev[1].record()
+            mfa.combine_splits(step.split_ws, B, w.heads, w.head_dim, step.num_splits, out=step.out)
+        else:
+            step.attend(q, T["seq_lens"])
+            if ev is not None:
+                ev[1].record()
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        one(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = float(np.mean(attn_ms))
+    achieved = kv_bytes / (attn_avg * 1e-3) / 1e9
+    step0 = sets[0][0]
+    traffic = counters_for(w.name, kernel_source_sig())
+    rec = {
+        "metric": "MFA decode-attention tokens/s and achieved KV HBM GB/s (% of peak), 1xMI355X",
+        "value": B / (ms * 1e-3),
+        "unit": "decode tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else ("fp8-kv/bf16" if w.kv_dtype == "fp8" else "f32"),
+        "data": "synthetic (seeded N(0,1) K/V, N(0,1/fan_in) weights, random-init)",
+        "config": {"workload": w.name, "batch": B, "context": maxlen, "heads": w.heads,
+                   "head_dim": w.head_dim, "kv_dtype": w.kv_dtype, "hidden": w.hidden,
+                   "q_rank": w.q_rank, "paged": w.paged, "num_splits": step0.num_splits,
+                   "chunk_tokens": step0.chunk_tokens, "rotate": rotate,
+                   "step": "qproj+kv_append+decode_attn+combine" if w.has_qproj
+                   else "kv_append+decode_attn+combine"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (traffic / (attn_avg * 1e-3) / 1e9) if traffic else None,
+                     "kernel": "mfa_decode_mfma_kernel", "kernel_avg_us": attn_avg * 1e3,
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "step_kv_plus_weights_GBps": (kv_bytes + w_bytes) / (ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample or (1 if w.batch <= 4 else min(4, w.batch))
+        rec["cpu_baseline"] = cpu_baseline(inp, n)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

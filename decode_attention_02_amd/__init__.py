@@ -1,0 +1,8 @@
+"""MFA decode attention for one AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libmfa.so`` (hand-written HIP kernels behind the C ABI
+of ``include/mfa.h``); this package is its thin torch-facing binding.
+"""
+from ._lib import BLOCK_TOKENS, MfaError, load  # noqa: F401
+from .api import (KVCache, combine_splits, decode_attn, decode_plan, kv_append,  # noqa: F401
+                  qproj, qproj_workspace_bytes, split_workspace_bytes)

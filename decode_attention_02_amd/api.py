@@ -1,0 +1,192 @@
+"""Thin torch-facing wrappers over libmfa's C ABI.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libmfa. torch supplies device memory and the current stream.
+Function names follow the C entry points (mfa_qproj -> ``qproj`` ...).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import BLOCK_TOKENS, MFA_BF16, MFA_F32, MFA_FP8_E4M3, check
+
+_DTYPES = {torch.float32: MFA_F32, torch.bfloat16: MFA_BF16}
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class KVCache:
+    """One layer's KV cache in libmfa's block layout (see include/mfa.h).
+
+    k [num_blocks][64][d], v [num_blocks][d][64] of the cache dtype; FP8
+    caches add fp32 k_scale / v_scale [num_blocks][64]. ``block_table``
+    [B][max_blocks_per_seq] int32 (None: contiguous, sequence b owns blocks
+    b*max_blocks_per_seq ..).
+    """
+
+    def __init__(self, num_blocks: int, head_dim: int, dtype: str, max_blocks_per_seq: int,
+                 block_table: Optional[torch.Tensor] = None, device="cuda", zero: bool = True):
+        self.num_blocks = int(num_blocks)
+        self.head_dim = int(head_dim)
+        self.dtype = dtype
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+        alloc = torch.zeros if zero else torch.empty
+        self.k = alloc((self.num_blocks, BLOCK_TOKENS, self.head_dim), dtype=tdt, device=device)
+        self.v = alloc((self.num_blocks, self.head_dim, BLOCK_TOKENS), dtype=tdt, device=device)
+        if dtype == "fp8":
+            self.k_scale = alloc((self.num_blocks, BLOCK_TOKENS), dtype=torch.float32, device=device)
+            self.v_scale = alloc((self.num_blocks, BLOCK_TOKENS), dtype=torch.float32, device=device)
+        else:
+            self.k_scale = self.v_scale = None
+        if block_table is not None:
+            _dev(block_table, "block_table")
+            if block_table.dtype != torch.int32:
+                raise ValueError("block_table must be int32")
+        self.block_table = block_table
+        self._desc = None
+
+    @property
+    def mfa_dtype(self) -> int:
+        return {"f32": MFA_F32, "bf16": MFA_BF16, "fp8": MFA_FP8_E4M3}[self.dtype]
+
+    def desc(self) -> _lib.KVCacheDesc:
+        d = _lib.KVCacheDesc()
+        d.k = self.k.data_ptr()
+        d.v = self.v.data_ptr()
+        d.k_scale = self.k_scale.data_ptr() if self.k_scale is not None else None
+        d.v_scale = self.v_scale.data_ptr() if self.v_scale is not None else None
+        d.block_table = self.block_table.data_ptr() if self.block_table is not None else None
+        d.num_blocks = self.num_blocks
+        d.max_blocks_per_seq = self.max_blocks_per_seq
+        d.head_dim = self.head_dim
+        d.dtype = self.mfa_dtype
+        return d
+
+
+def qproj_workspace_bytes(batch: int, hidden: int, q_rank: int, heads: int, head_dim: int,
+                          dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.mfa_qproj_workspace_bytes(batch, hidden, q_rank, heads, head_dim,
+                                             _DTYPES[dtype]))
+
+
+def qproj(x: torch.Tensor, w_qdown: torch.Tensor, q_norm_w: torch.Tensor, w_qup: torch.Tensor,
+          heads: int, head_dim: int, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [B][H][d] = RMSNorm(x W_qdown^T; g, eps) W_qup^T (mfa_qproj)."""
+    lib = _lib.load()
+    B, hidden = x.shape
+    q_rank = w_qdown.shape[0]
+    dt = _DTYPES[x.dtype]
+    for t, n in ((x, "x"), (w_qdown, "w_qdown"), (q_norm_w, "q_norm_w"), (w_qup, "w_qup")):
+        _dev(t, n)
+    if out is None:
+        out = torch.empty((B, heads, head_dim), dtype=x.dtype, device=x.device)
+    need = int(lib.mfa_qproj_workspace_bytes(B, hidden, q_rank, heads, head_dim, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    check("mfa_qproj", lib.mfa_qproj(_ptr(x), _ptr(w_qdown), _ptr(q_norm_w), _ptr(w_qup),
+                                     _ptr(out), _ptr(workspace), workspace.numel(), B, hidden,
+                                     q_rank, heads, head_dim, eps, dt, _stream(x.device)))
+    return out
+
+
+def kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+              pos: torch.Tensor) -> None:
+    """Write k_new/v_new [B][n_new][d] (or [B][d]) at positions pos[b].. (mfa_kv_append)."""
+    lib = _lib.load()
+    if k_new.dim() == 2:
+        k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
+    B, n_new, _ = k_new.shape
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (pos, "pos")):
+        _dev(t, n)
+    if pos.dtype != torch.int32:
+        raise ValueError("pos must be int32")
+    desc = cache.desc()
+    check("mfa_kv_append", lib.mfa_kv_append(_ptr(k_new), _ptr(v_new), _DTYPES[k_new.dtype],
+                                             _ptr(pos), n_new, B, ctypes.byref(desc),
+                                             _stream(k_new.device)))
+
+
+def decode_plan(batch: int, heads: int, head_dim: int, max_seq_len: int, kv_dtype: str):
+    """(num_splits, chunk_tokens) the library picks (mfa_decode_plan)."""
+    lib = _lib.load()
+    ns, ch = ctypes.c_int(), ctypes.c_int()
+    check("mfa_decode_plan", lib.mfa_decode_plan(
+        batch, heads, head_dim, max_seq_len,
+        {"f32": MFA_F32, "bf16": MFA_BF16, "fp8": MFA_FP8_E4M3}[kv_dtype],
+        ctypes.byref(ns), ctypes.byref(ch)))
+    return ns.value, ch.value
+
+
+def split_workspace_bytes(batch: int, heads: int, head_dim: int, num_splits: int) -> int:
+    return int(_lib.load().mfa_split_workspace_bytes(batch, heads, head_dim, num_splits))
+
+
+def decode_attn(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq_len: int,
+                sm_scale: Optional[float] = None, num_splits: int = 1,
+                chunk_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                combine: bool = True) -> Optional[torch.Tensor]:
+    """Attention of q [B][H][d] over the cache (mfa_decode_attn).
+
+    With num_splits > 1 and ``combine`` False, only the partials are written
+    to ``workspace`` (run ``combine_splits`` afterwards) and None is returned.
+    """
+    lib = _lib.load()
+    B, H, d = q.shape
+    _dev(q, "q")
+    _dev(seq_lens, "seq_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if chunk_tokens is None:
+        per = -(-max(max_seq_len, 1) // num_splits)
+        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+    if out_dtype is None:
+        out_dtype = q.dtype
+    if out is None and (num_splits == 1 or combine):
+        out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    if num_splits > 1 and workspace is None:
+        workspace = torch.empty(split_workspace_bytes(B, H, d, num_splits), dtype=torch.uint8,
+                                device=q.device)
+    desc = cache.desc()
+    check("mfa_decode_attn", lib.mfa_decode_attn(
+        _ptr(q), _DTYPES[q.dtype], B, H, ctypes.byref(desc), _ptr(seq_lens), int(max_seq_len),
+        float(sm_scale), int(num_splits), int(chunk_tokens), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0,
+        _ptr(out) if (num_splits == 1 or combine) else None, _DTYPES[out_dtype],
+        _stream(q.device)))
+    return out if (num_splits == 1 or combine) else None
+
+
+def combine_splits(workspace: torch.Tensor, batch: int, heads: int, head_dim: int, num_splits: int,
+                   out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Merge split partials into out [B][H][d] (mfa_combine)."""
+    lib = _lib.load()
+    _dev(workspace, "workspace")
+    if out is None:
+        out = torch.empty((batch, heads, head_dim), dtype=out_dtype, device=workspace.device)
+    check("mfa_combine", lib.mfa_combine(_ptr(workspace), workspace.numel(), batch, heads,
+                                         head_dim, num_splits, _ptr(out), _DTYPES[out.dtype],
+                                         _stream(workspace.device)))
+    return out

@@ -1,0 +1,149 @@
+// MFA decode attention on the vector ALUs, for head shapes the matrix-core
+// kernel does not cover (any H <= 64 with H*d <= 8192, d in {64,128,256})
+// and for fp32 caches. All arithmetic is fp32. Same semantics as the
+// matrix-core kernel: all H heads attend to the one shared K/V head
+// ("Step-3 is Large yet Affordable" summary page, §2 and §5), online softmax
+// over 8-token tiles, natural exp.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mfa {
+
+namespace {
+constexpr int kT = 8;            // tokens per tile
+constexpr int kMaxHD = 8192;     // H*d limit (q staged in LDS)
+constexpr int kMaxPerThread = kMaxHD / 256;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
+  __shared__ float q_s[kMaxHD];
+  __shared__ float k_s[kT][D];
+  __shared__ float v_s[kT][D];
+  __shared__ float p_s[64][kT];
+  __shared__ float alpha_s[64], m_s[64], l_s[64];
+
+  const int H = a.heads;
+  const int HD = H * D;
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x % a.num_splits;
+  const int b = blockIdx.x / a.num_splits;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int t0 = split * a.chunk_tokens;
+  const int t1 = min(t0 + a.chunk_tokens, L);
+
+  for (int i = tid; i < HD; i += 256) {
+    const size_t qi = static_cast<size_t>(b) * HD + i;
+    q_s[i] = a.q_f32 ? reinterpret_cast<const float*>(a.q)[qi] : bf16_to_f32(a.q[qi]);
+  }
+  if (tid < H) { m_s[tid] = -INFINITY; l_s[tid] = 0.f; }
+  float o[kMaxPerThread];
+#pragma unroll
+  for (int r = 0; r < kMaxPerThread; ++r) o[r] = 0.f;
+  const int* bt_row = a.block_table ? a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
+                                    : nullptr;
+  __syncthreads();
+
+  for (int tt = t0; tt < t1; tt += kT) {
+    const int n = min(kT, t1 - tt);
+    for (int i = tid; i < kT * D; i += 256) {
+      const int t = i / D, j = i % D;
+      float kv = 0.f, vv = 0.f;
+      if (t < n) {
+        const int tok = tt + t;
+        int id = bt_row ? bt_row[tok >> 6] : b * a.max_blocks_per_seq + (tok >> 6);
+        id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+        const size_t kidx = (static_cast<size_t>(id) * kBlockTokens + (tok & 63)) * D + j;
+        const size_t vidx = (static_cast<size_t>(id) * D + j) * kBlockTokens + (tok & 63);
+        if (a.kv_f32) {
+          kv = reinterpret_cast<const float*>(a.k)[kidx];
+          vv = reinterpret_cast<const float*>(a.v)[vidx];
+        } else {
+          kv = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[kidx]);
+          vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.v)[vidx]);
+        }
+      }
+      k_s[t][j] = kv;
+      v_s[t][j] = vv;
+    }
+    __syncthreads();
+    for (int i = tid; i < H * kT; i += 256) {
+      const int h = i / kT, t = i % kT;
+      float s = -INFINITY;
+      if (t < n) {
+        float acc = 0.f;
+        for (int j = 0; j < D; ++j) acc = fmaf(q_s[h * D + j], k_s[t][j], acc);
+        s = acc * a.sm_scale;
+      }
+      p_s[h][t] = s;
+    }
+    __syncthreads();
+    if (tid < H) {
+      const int h = tid;
+      float mx = m_s[h];
+      for (int t = 0; t < n; ++t) mx = fmaxf(mx, p_s[h][t]);
+      const float al = expf(m_s[h] - mx);
+      float sum = 0.f;
+      for (int t = 0; t < kT; ++t) {
+        const float p = t < n ? expf(p_s[h][t] - mx) : 0.f;
+        p_s[h][t] = p;
+        sum += p;
+      }
+      l_s[h] = l_s[h] * al + sum;
+      m_s[h] = mx;
+      alpha_s[h] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kMaxPerThread; ++r) {
+      const int e = tid + 256 * r;
+      if (e < HD) {
+        const int h = e / D, j = e % D;
+        float acc = o[r] * alpha_s[h];
+        for (int t = 0; t < n; ++t) acc = fmaf(p_s[h][t], v_s[t][j], acc);
+        o[r] = acc;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (a.num_splits == 1) {
+#pragma unroll
+    for (int r = 0; r < kMaxPerThread; ++r) {
+      const int e = tid + 256 * r;
+      if (e < HD) {
+        const int h = e / D;
+        const float l = l_s[h];
+        const float val = l > 0.f ? o[r] / l : 0.f;
+        const size_t oi = static_cast<size_t>(b) * HD + e;
+        if (a.out_f32) reinterpret_cast<float*>(a.out)[oi] = val;
+        else reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(val);
+      }
+    }
+  } else {
+    const size_t row = static_cast<size_t>(b) * a.num_splits + split;
+#pragma unroll
+    for (int r = 0; r < kMaxPerThread; ++r) {
+      const int e = tid + 256 * r;
+      if (e < HD) a.part_o[row * HD + e] = o[r];
+    }
+    if (tid < H) {
+      a.part_ml[(row * H + tid) * 2 + 0] = m_s[tid];
+      a.part_ml[(row * H + tid) * 2 + 1] = l_s[tid];
+    }
+  }
+}
+
+hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(B * a.num_splits)), block(256);
+  switch (a.head_dim) {
+    case 64: hipLaunchKernelGGL(mfa_decode_valu_kernel<64>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(mfa_decode_valu_kernel<128>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(mfa_decode_valu_kernel<256>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mfa

@@ -1,0 +1,101 @@
+// Device helpers shared by the MFA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlockTokens = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p;
+  p[0] = static_cast<__bf16>(lo);
+  p[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// 16x16x32 bf16 matrix-core product: acc[m][n] += sum_k A[m][k] B[k][n].
+// Operand layout (lane l, g = l/16, c = l%16): A lane holds A[c][8g..8g+7],
+// B lane holds B[8g..8g+7][c]; the accumulator lane holds C[4g+i][c], i<4.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                 const f32x4_t& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Two OCP e4m3 codes (the low or high 16 bits of `word`) -> two bf16. Every
+// e4m3 value is exact in bf16, and the scale 1.0 makes the conversion exact.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t word) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(word), 1.0f, HIGH);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight e4m3 codes (two dwords) -> eight bf16 as one matrix-core operand.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  uint4 u;
+  u.x = e4m3x2_to_bf16x2<false>(w0);
+  u.y = e4m3x2_to_bf16x2<true>(w0);
+  u.z = e4m3x2_to_bf16x2<false>(w1);
+  u.w = e4m3x2_to_bf16x2<true>(w1);
+  return as_bf16x8(u);
+}
+
+// Round-to-nearest-even encode of a float into an OCP e4m3 code, from the
+// format's definition: 3 mantissa bits, exponent bias 7, subnormal step
+// 2^-9, largest finite 448. Magnitudes above 448 saturate to 448 (callers
+// only pass |y| <= 448 * (1 + 2^-23)). The input's sign bit is kept.
+__device__ __forceinline__ uint32_t encode_e4m3_rne(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7fffffffu);
+  uint32_t code;
+  if (a < 0.015625f) {                      // below 2^-6: multiples of 2^-9
+    code = static_cast<uint32_t>(rintf(a * 512.0f));   // 0..8, ties to even
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    const int e = static_cast<int>(ua >> 23) - 127;    // >= -6
+    uint32_t keep = (ua >> 20) & 7u;
+    const uint32_t rem = ua & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep += 1;
+    uint32_t ef = static_cast<uint32_t>(e + 7);
+    if (keep == 8u) { keep = 0; ef += 1; }
+    code = (ef << 3) | keep;
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+}  // namespace mfa

@@ -1,0 +1,77 @@
+// Launch interfaces of the MFA kernels (internal to libmfa; the public ABI
+// is include/mfa.h). Every launcher enqueues on `stream` and returns the
+// launch status from hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+// Decode attention arguments (shared by the matrix-core and VALU kernels).
+struct AttnArgs {
+  const uint16_t* q;          // bf16 bits or (VALU kernel, f32 q) reinterpret
+  const uint8_t* k;           // cache blocks, bytes
+  const uint8_t* v;
+  const float* k_scale;       // FP8 only
+  const float* v_scale;
+  const int* block_table;     // nullable
+  const int* seq_lens;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int max_seq_len;
+  int chunk_tokens;           // multiple of 64
+  int num_splits;
+  int heads;                  // VALU kernel only (matrix-core kernel: 64)
+  int head_dim;               // VALU kernel only (matrix-core kernel: 256)
+  int q_f32;                  // VALU kernel: q dtype
+  int kv_f32;                 // VALU kernel: cache dtype (else bf16)
+  float sm_scale;             // VALU kernel (natural exp)
+  float scale_log2;           // matrix-core kernel: sm_scale * log2(e)
+  float* part_o;              // [B][S][H][d] when num_splits > 1
+  float* part_ml;             // [B][S][H][2]
+  void* out;                  // [B][H][d] when num_splits == 1
+  int out_f32;
+};
+
+hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
+hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
+
+hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
+                          int num_splits, void* out, int out_f32, hipStream_t stream);
+
+struct AppendArgs {
+  const void* k_new;          // [B][n_new][d]
+  const void* v_new;
+  int in_f32;                 // else bf16
+  const int* pos;             // [B]
+  int n_new;
+  int B;
+  uint8_t* k;                 // cache
+  uint8_t* v;
+  float* k_scale;
+  float* v_scale;
+  const int* block_table;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int d;
+  int cache_dtype;            // 0 f32, 1 bf16, 2 fp8
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
+// Query path.
+// bf16: C partials [ks][M][N] fp32 = A[M][K] . W[N][K]^T over K slice ks.
+hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* W, float* part, int M,
+                                   int N, int K, int ksplit, hipStream_t stream);
+// n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
+hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
+                                 float eps, void* out, int out_f32, hipStream_t stream);
+// out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
+hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
+                              int out_f32, hipStream_t stream);
+// f32: out[m][n] = A[m][K] . W[n][K]  (one wave per output).
+hipError_t launch_gemv_f32(const float* A, const float* W, float* out, int M, int N, int K,
+                           hipStream_t stream);
+
+}  // namespace mfa

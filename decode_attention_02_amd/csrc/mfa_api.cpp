@@ -1,0 +1,339 @@
+// libmfa C ABI (include/mfa.h): host-side validation, planning and dispatch.
+// Every check runs before any HIP call, so a rejected call touches neither
+// the device nor the runtime.
+#include "mfa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kBlock = MFA_BLOCK_TOKENS;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+mfa_status from_hip(hipError_t e) { return e == hipSuccess ? MFA_OK : MFA_ERR_HIP; }
+
+// ---- query path planning -------------------------------------------------
+constexpr int kRowsPerPass = 64;     // matrix-core GEMM handles <= 64 rows per pass
+constexpr int kKStage = 256;
+
+// K splits of a skinny bf16 product: the smallest divisor of K/256 (<= 16)
+// that gives >= 512 workgroups, else the largest such divisor.
+int pick_ksplit(int N, int K) {
+  const int stages = K / kKStage;
+  const int tiles = N / 64;
+  int best = 1;
+  for (int ks = 1; ks <= 16 && ks <= stages; ++ks) {
+    if (stages % ks) continue;
+    best = ks;
+    if (tiles * ks >= 512) break;
+  }
+  return best;
+}
+
+struct QprojPlan {
+  int rows;          // rows per pass
+  int ks_down, ks_up;
+  size_t off_part_down, off_n, off_part_up, total;
+};
+
+QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype) {
+  QprojPlan p{};
+  p.rows = B < kRowsPerPass ? B : kRowsPerPass;
+  if (dtype == MFA_BF16) {
+    p.ks_down = pick_ksplit(q_rank, hidden);
+    p.ks_up = pick_ksplit(HD, q_rank);
+    p.off_part_down = 0;
+    p.off_n = round_up(static_cast<size_t>(p.ks_down) * p.rows * q_rank * 4, 256);
+    p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 2, 256);
+    p.total = p.off_part_up + round_up(static_cast<size_t>(p.ks_up) * p.rows * HD * 4, 256);
+  } else {
+    p.ks_down = p.ks_up = 1;
+    p.off_part_down = 0;
+    p.off_n = round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
+    p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
+    p.total = p.off_part_up;
+  }
+  return p;
+}
+
+mfa_status check_qproj_shape(int B, int hidden, int q_rank, int H, int d, int dtype) {
+  if (dtype != MFA_BF16 && dtype != MFA_F32) return MFA_ERR_DTYPE;
+  if (B < 1 || B > 256 || hidden < 1 || q_rank < 1 || H < 1 || d < 1) return MFA_ERR_SHAPE;
+  if (q_rank > 8192) return MFA_ERR_SHAPE;
+  const long long hd = static_cast<long long>(H) * d;
+  if (hd > (1 << 24)) return MFA_ERR_SHAPE;
+  if (dtype == MFA_BF16) {
+    if (hidden % kKStage || q_rank % kKStage || hd % 64 || q_rank % 64) return MFA_ERR_SHAPE;
+  } else {
+    if (hidden % 4 || q_rank % 4 || hd % 4) return MFA_ERR_SHAPE;
+  }
+  return MFA_OK;
+}
+
+// ---- attention planning --------------------------------------------------
+bool mfma_shape(int H, int d, int kv_dtype) {
+  return H == 64 && d == 256 && (kv_dtype == MFA_BF16 || kv_dtype == MFA_FP8_E4M3);
+}
+
+bool valu_shape(int H, int d, int kv_dtype) {
+  return (kv_dtype == MFA_F32 || kv_dtype == MFA_BF16) && H >= 1 && H <= 64 &&
+         (d == 64 || d == 128 || d == 256) && H * d <= 8192;
+}
+
+mfa_status check_cache(const mfa_kv_cache* c) {
+  if (!c) return MFA_ERR_NULL;
+  if (!c->k || !c->v) return MFA_ERR_NULL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return MFA_ERR_ALIGN;
+  if (c->dtype != MFA_F32 && c->dtype != MFA_BF16 && c->dtype != MFA_FP8_E4M3) return MFA_ERR_DTYPE;
+  if (c->dtype == MFA_FP8_E4M3) {
+    if (!c->k_scale || !c->v_scale) return MFA_ERR_NULL;
+    if (!aligned16(c->k_scale) || !aligned16(c->v_scale)) return MFA_ERR_ALIGN;
+  }
+  if (c->num_blocks < 1 || c->max_blocks_per_seq < 1) return MFA_ERR_SHAPE;
+  if (c->head_dim < 1 || c->head_dim > 256 || c->head_dim % 64) return MFA_ERR_SHAPE;
+  if (c->block_table && !aligned4(c->block_table)) return MFA_ERR_ALIGN;
+  if (static_cast<long long>(c->max_blocks_per_seq) * kBlock > (1ll << 30)) return MFA_ERR_SHAPE;
+  return MFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mfa_abi_version(void) { return MFA_ABI_VERSION; }
+
+const char* mfa_status_str(int s) {
+  switch (s) {
+    case MFA_OK: return "ok";
+    case MFA_ERR_NULL: return "required pointer is NULL";
+    case MFA_ERR_SHAPE: return "size out of range or inconsistent";
+    case MFA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MFA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MFA_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
+    case MFA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MFA_ERR_HIP: return "HIP runtime reported a launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, int dtype) {
+  if (check_qproj_shape(B, hidden, q_rank, H, d, dtype) != MFA_OK) return 0;
+  return plan_qproj(B, hidden, q_rank, H * d, dtype).total;
+}
+
+mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, const void* w_qup,
+                     void* q_out, void* workspace, size_t workspace_bytes, int B, int hidden,
+                     int q_rank, int H, int d, float eps, int dtype, void* stream) {
+  if (!x || !w_qdown || !q_norm_w || !w_qup || !q_out) return MFA_ERR_NULL;
+  const mfa_status sh = check_qproj_shape(B, hidden, q_rank, H, d, dtype);
+  if (sh != MFA_OK) return sh;
+  if (!aligned16(x) || !aligned16(w_qdown) || !aligned16(q_norm_w) || !aligned16(w_qup) ||
+      !aligned16(q_out) || (workspace && !aligned16(workspace)))
+    return MFA_ERR_ALIGN;
+  if (!(eps >= 0.f)) return MFA_ERR_SHAPE;
+  const int HD = H * d;
+  const QprojPlan p = plan_qproj(B, hidden, q_rank, HD, dtype);
+  if (!workspace) return MFA_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return MFA_ERR_WORKSPACE;
+
+  hipStream_t st = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t esz = dtype == MFA_BF16 ? 2 : 4;
+  for (int r0 = 0; r0 < B; r0 += p.rows) {
+    const int M = (B - r0) < p.rows ? (B - r0) : p.rows;
+    const uint8_t* xa = static_cast<const uint8_t*>(x) + static_cast<size_t>(r0) * hidden * esz;
+    uint8_t* qo = static_cast<uint8_t*>(q_out) + static_cast<size_t>(r0) * HD * esz;
+    hipError_t e;
+    if (dtype == MFA_BF16) {
+      float* pd = reinterpret_cast<float*>(ws + p.off_part_down);
+      uint16_t* n = reinterpret_cast<uint16_t*>(ws + p.off_n);
+      e = mfa::launch_gemm_bf16_splitk(reinterpret_cast<const uint16_t*>(xa),
+                                       static_cast<const uint16_t*>(w_qdown), pd, M, q_rank, hidden,
+                                       p.ks_down, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+      e = mfa::launch_rmsnorm_reduce(pd, p.ks_down, q_norm_w, M, q_rank, eps, n, 0, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+      float* pu = reinterpret_cast<float*>(ws + p.off_part_up);
+      e = mfa::launch_gemm_bf16_splitk(n, static_cast<const uint16_t*>(w_qup), pu, M, HD, q_rank,
+                                       p.ks_up, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+      e = mfa::launch_reduce_cast(pu, p.ks_up, M, HD, qo, 0, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+    } else {
+      float* c = reinterpret_cast<float*>(ws + p.off_part_down);
+      float* n = reinterpret_cast<float*>(ws + p.off_n);
+      e = mfa::launch_gemv_f32(reinterpret_cast<const float*>(xa),
+                               static_cast<const float*>(w_qdown), c, M, q_rank, hidden, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+      e = mfa::launch_rmsnorm_reduce(c, 1, q_norm_w, M, q_rank, eps, n, 1, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+      e = mfa::launch_gemv_f32(n, static_cast<const float*>(w_qup), reinterpret_cast<float*>(qo),
+                               M, HD, q_rank, st);
+      if (e != hipSuccess) return MFA_ERR_HIP;
+    }
+  }
+  return MFA_OK;
+}
+
+mfa_status mfa_kv_append(const void* k_new, const void* v_new, int in_dtype, const int32_t* pos,
+                         int n_new, int B, const mfa_kv_cache* cache, void* stream) {
+  if (!k_new || !v_new || !pos) return MFA_ERR_NULL;
+  const mfa_status cs = check_cache(cache);
+  if (cs != MFA_OK) return cs;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(pos)) return MFA_ERR_ALIGN;
+  if (B < 1 || n_new < 1) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(n_new) > static_cast<long long>(cache->max_blocks_per_seq) * kBlock)
+    return MFA_ERR_SHAPE;
+  if (in_dtype != MFA_F32 && in_dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  if (cache->dtype != MFA_FP8_E4M3 && cache->dtype != in_dtype) return MFA_ERR_DTYPE;
+  if (!cache->block_table &&
+      static_cast<long long>(B) * cache->max_blocks_per_seq > cache->num_blocks)
+    return MFA_ERR_SHAPE;
+  mfa::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_f32 = in_dtype == MFA_F32;
+  a.pos = pos;
+  a.n_new = n_new;
+  a.B = B;
+  a.k = static_cast<uint8_t*>(cache->k);
+  a.v = static_cast<uint8_t*>(cache->v);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = cache->block_table;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = cache->max_blocks_per_seq;
+  a.d = cache->head_dim;
+  a.cache_dtype = cache->dtype == MFA_F32 ? 0 : (cache->dtype == MFA_BF16 ? 1 : 2);
+  return from_hip(mfa::launch_kv_append(a, as_stream(stream)));
+}
+
+mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, int* num_splits,
+                           int* chunk_tokens) {
+  if (!num_splits || !chunk_tokens) return MFA_ERR_NULL;
+  if (B < 1 || H < 1 || d < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
+  (void)kv_dtype;
+  const int blocks = (max_seq_len + kBlock - 1) / kBlock;
+  // Aim for >= 1024 workgroups (four per compute unit) without making a
+  // split shorter than 4 blocks; long contexts keep at least 16 blocks/split.
+  int splits = 1;
+  if (blocks > 0) {
+    const int want = (1024 + B - 1) / B;
+    int per = (blocks + want - 1) / want;
+    if (per < 4) per = 4;
+    splits = (blocks + per - 1) / per;
+    if (splits < 1) splits = 1;
+  }
+  int per_blocks = blocks > 0 ? (blocks + splits - 1) / splits : 1;
+  splits = blocks > 0 ? (blocks + per_blocks - 1) / per_blocks : 1;
+  *num_splits = splits;
+  *chunk_tokens = per_blocks * kBlock;
+  return MFA_OK;
+}
+
+size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || d < 1 || num_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * num_splits * H;
+  return round_up(rows * d * 4, 256) + rows * 2 * 4;
+}
+
+mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
+                           const int32_t* seq_lens, int max_seq_len, float sm_scale,
+                           int num_splits, int chunk_tokens, void* workspace,
+                           size_t workspace_bytes, void* out, int out_dtype, void* stream) {
+  if (!q || !seq_lens) return MFA_ERR_NULL;
+  const mfa_status cs = check_cache(cache);
+  if (cs != MFA_OK) return cs;
+  if (!aligned16(q) || !aligned4(seq_lens) || (out && !aligned16(out)) ||
+      (workspace && !aligned16(workspace)))
+    return MFA_ERR_ALIGN;
+  const int d = cache->head_dim;
+  if (B < 1 || H < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(max_seq_len) > static_cast<long long>(cache->max_blocks_per_seq) * kBlock)
+    return MFA_ERR_SHAPE;
+  if (!cache->block_table &&
+      static_cast<long long>(B) * cache->max_blocks_per_seq > cache->num_blocks)
+    return MFA_ERR_SHAPE;
+  if (num_splits < 1 || chunk_tokens < kBlock || chunk_tokens % kBlock) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(num_splits) * chunk_tokens < max_seq_len) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(B) * num_splits > 0x7fffffffll) return MFA_ERR_SHAPE;
+  if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
+  if (!(sm_scale == sm_scale)) return MFA_ERR_SHAPE;
+  const bool mfma = mfma_shape(H, d, cache->dtype);
+  if (mfma) {
+    if (q_dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  } else if (valu_shape(H, d, cache->dtype)) {
+    if (q_dtype != MFA_BF16 && q_dtype != MFA_F32) return MFA_ERR_DTYPE;
+  } else {
+    return MFA_ERR_UNSUPPORTED;
+  }
+  if (num_splits == 1) {
+    if (!out) return MFA_ERR_NULL;
+  } else {
+    if (!workspace) return MFA_ERR_WORKSPACE;
+    if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
+  }
+
+  mfa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint8_t*>(cache->k);
+  a.v = static_cast<const uint8_t*>(cache->v);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.block_table = cache->block_table;
+  a.seq_lens = seq_lens;
+  a.max_blocks_per_seq = cache->max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  a.max_seq_len = max_seq_len;
+  a.chunk_tokens = chunk_tokens;
+  a.num_splits = num_splits;
+  a.heads = H;
+  a.head_dim = d;
+  a.q_f32 = q_dtype == MFA_F32;
+  a.kv_f32 = cache->dtype == MFA_F32;
+  a.sm_scale = sm_scale;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const size_t rows = static_cast<size_t>(B) * num_splits * H;
+  if (num_splits > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + round_up(rows * d * 4, 256));
+  }
+  a.out = out;
+  a.out_f32 = out_dtype == MFA_F32;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = mfma ? mfa::launch_decode_mfma(a, cache->dtype == MFA_FP8_E4M3, B, st)
+                      : mfa::launch_decode_valu(a, B, st);
+  if (e != hipSuccess) return MFA_ERR_HIP;
+  if (num_splits > 1 && out) {
+    e = mfa::launch_combine(a.part_o, a.part_ml, B, H, d, num_splits, out, a.out_f32, st);
+    if (e != hipSuccess) return MFA_ERR_HIP;
+  }
+  return MFA_OK;
+}
+
+mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int H, int d,
+                       int num_splits, void* out, int out_dtype, void* stream) {
+  if (!workspace || !out) return MFA_ERR_NULL;
+  if (!aligned16(workspace) || !aligned16(out)) return MFA_ERR_ALIGN;
+  if (B < 1 || H < 1 || d < 1 || d > 4096 || num_splits < 2) return MFA_ERR_SHAPE;
+  if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
+  if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B) * num_splits * H;
+  const float* po = static_cast<const float*>(workspace);
+  const float* pml =
+      reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + round_up(rows * d * 4, 256));
+  return from_hip(mfa::launch_combine(po, pml, B, H, d, num_splits, out,
+                                      out_dtype == MFA_F32, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""One MFA decode step through libmfa: query path, KV append, attention,
+split combine, on the current stream. Marshalling only; each stage is one
+C-ABI call (mfa_qproj, mfa_kv_append, mfa_decode_attn, mfa_combine).
+
+Also fills a cache from prompt tokens (mfa_kv_append with n_new > 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib, api
+from ._lib import check
+
+
+class DecodeStep:
+    """Pre-planned decode step for B sequences of at most ``max_seq_len`` tokens.
+
+    Workspaces (query-path partials, split partials) and outputs are
+    allocated once here, so calling the step allocates nothing.
+    """
+
+    def __init__(self, cache: api.KVCache, batch: int, heads: int, max_seq_len: int,
+                 hidden: Optional[int] = None, q_rank: Optional[int] = None,
+                 act_dtype: torch.dtype = torch.bfloat16, num_splits: Optional[int] = None,
+                 chunk_tokens: Optional[int] = None, eps: float = 1e-6,
+                 out_dtype: Optional[torch.dtype] = None, sm_scale: Optional[float] = None,
+                 device="cuda"):
+        self.cache = cache
+        self.B, self.H, self.d = batch, heads, cache.head_dim
+        self.max_seq_len = int(max_seq_len)
+        self.hidden, self.q_rank = hidden, q_rank
+        self.act_dtype = act_dtype
+        self.eps = eps
+        self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(self.d)
+        if num_splits is None:
+            num_splits, chunk_tokens = api.decode_plan(batch, heads, self.d, self.max_seq_len,
+                                                       cache.dtype)
+        elif chunk_tokens is None:
+            per = -(-max(self.max_seq_len, 1) // num_splits)
+            chunk_tokens = -(-per // _lib.BLOCK_TOKENS) * _lib.BLOCK_TOKENS
+        self.num_splits, self.chunk_tokens = int(num_splits), int(chunk_tokens)
+        self.out_dtype = out_dtype or act_dtype
+        self.out = torch.empty((batch, heads, self.d), dtype=self.out_dtype, device=device)
+        self.q = torch.empty((batch, heads, self.d), dtype=act_dtype, device=device)
+        nbytes = api.split_workspace_bytes(batch, heads, self.d, self.num_splits)
+        self.split_ws = (torch.empty(nbytes, dtype=torch.uint8, device=device)
+                         if nbytes else None)
+        self.qproj_ws = None
+        if hidden is not None:
+            nb = api.qproj_workspace_bytes(batch, hidden, q_rank, heads, self.d, act_dtype)
+            self.qproj_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+        self._desc = cache.desc()
+        self._lib = _lib.load()
+
+    # -- stages ---------------------------------------------------------
+    def query(self, x, w_qdown, g, w_qup):
+        return api.qproj(x, w_qdown, g, w_qup, self.H, self.d, self.eps, out=self.q,
+                         workspace=self.qproj_ws)
+
+    def append(self, k_new, v_new, pos):
+        api.kv_append(self.cache, k_new, v_new, pos)
+
+    def attend(self, q, seq_lens, combine_separately: bool = True):
+        """Attention (+ combine). ``combine_separately`` runs mfa_combine as its
+        own call; otherwise mfa_decode_attn merges into ``out`` itself."""
+        if self.num_splits == 1:
+            return api.decode_attn(q, self.cache, seq_lens, self.max_seq_len, self.sm_scale, 1,
+                                   self.chunk_tokens, out=self.out)
+        if combine_separately:
+            api.decode_attn(q, self.cache, seq_lens, self.max_seq_len, self.sm_scale,
+                            self.num_splits, self.chunk_tokens, workspace=self.split_ws,
+                            combine=False)
+            return api.combine_splits(self.split_ws, self.B, self.H, self.d, self.num_splits,
+                                      out=self.out)
+        return api.decode_attn(q, self.cache, seq_lens, self.max_seq_len, self.sm_scale,
+                               self.num_splits, self.chunk_tokens, out=self.out,
+                               workspace=self.split_ws)
+
+    def __call__(self, k_new, v_new, pos, seq_lens, x=None, weights=None, q=None):
+        """q from x and weights=(w_qdown, g, w_qup) (or given), append, attend."""
+        if q is None:
+            q = self.query(x, *weights)
+        self.append(k_new, v_new, pos)
+        return self.attend(q, seq_lens)
+
+
+def prefill(cache: api.KVCache, k_rows: torch.Tensor, v_rows: torch.Tensor, offsets,
+            lengths) -> None:
+    """Write tokens 0..lengths[b]-1 of every sequence b from the packed rows
+    k_rows/v_rows [sum(lengths)][d] (sequence-major, ``offsets`` host [B+1])."""
+    lib = _lib.load()
+    B = len(lengths)
+    dev = k_rows.device
+    dt = api._DTYPES[k_rows.dtype]
+    if max(int(l) for l in lengths) == 0:
+        return
+    if all(int(l) == int(lengths[0]) for l in lengths) and int(lengths[0]) > 0:
+        L = int(lengths[0])
+        pos = torch.zeros(B, dtype=torch.int32, device=dev)
+        api.kv_append(cache, k_rows.view(B, L, -1), v_rows.view(B, L, -1), pos)
+        return
+    if cache.block_table is None:
+        # contiguous cache: every sequence owns its region, so pad to the
+        # longest prompt; rows past a sequence's length land in its own
+        # region beyond seq_len and are never attended
+        L = max(int(l) for l in lengths)
+        kp = torch.zeros((B, L, k_rows.shape[1]), dtype=k_rows.dtype, device=dev)
+        vp = torch.zeros_like(kp)
+        for b in range(B):
+            n, o = int(lengths[b]), int(offsets[b])
+            kp[b, :n] = k_rows[o:o + n]
+            vp[b, :n] = v_rows[o:o + n]
+        api.kv_append(cache, kp, vp, torch.zeros(B, dtype=torch.int32, device=dev))
+        return
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    stride = cache.max_blocks_per_seq * 4
+    for b in range(B):
+        n = int(lengths[b])
+        if n == 0:
+            continue
+        desc = cache.desc()
+        desc.block_table = cache.block_table.data_ptr() + b * stride
+        o = int(offsets[b])
+        kb = k_rows[o:o + n].unsqueeze(0)
+        vb = v_rows[o:o + n].unsqueeze(0)
+        check("mfa_kv_append", lib.mfa_kv_append(
+            ctypes.c_void_p(kb.data_ptr()), ctypes.c_void_p(vb.data_ptr()), dt,
+            ctypes.c_void_p(zero.data_ptr()), n, 1, ctypes.byref(desc),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))

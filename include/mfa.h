@@ -1,0 +1,212 @@
+/*
+ * mfa.h -- C ABI of libmfa: the decode step of Multi-Matrix Factorization
+ * Attention (MFA) on one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "Step-3 is Large yet Affordable: Model-system
+ * Co-design for Cost-effective Decoding" (paperlayer.ai summary of arXiv
+ * 2507.19427v1). §2 Step-3 Model Card: MFA applies a low-rank factorisation
+ * in the QK circuit so that many attention heads share a small KV cache.
+ * §5 Model-System Co-design: one KV head of an 8-bit cache shared by all
+ * query heads gives arithmetic intensity 128 and effective rank 16,384
+ * (64 heads x 256); KV quantisation raises the intensity. §6 Non-Flagship
+ * Hardware Support: the attention stays memory-bandwidth bound. §7
+ * Implementation and Results: attention instances own the KV caches.
+ *
+ * The pages print no equations. The readings this library implements:
+ *   q    = RMSNorm(x W_qdown^T; g, eps) W_qup^T, split into H heads of width d
+ *          (head h = output columns h*d .. h*d+d-1);
+ *   o[h] = softmax_t(q[h] . k_t * sm_scale) . V over every cached token t of
+ *          the sequence, all H heads against the same single K/V head.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers are DEVICE pointers unless marked "host". The caller allocates
+ *   and owns all memory, including scratch ("workspace") buffers; the
+ *   library keeps no state between calls and never allocates, frees or
+ *   synchronises.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *   void*; NULL means the null stream).
+ * - Arguments are checked on the host before anything is launched; a check
+ *   that fails returns a nonzero mfa_status and enqueues nothing. A launch
+ *   failure reported by the HIP runtime returns MFA_ERR_HIP.
+ * - Device-side data (sequence lengths, positions, block ids) is clamped to
+ *   its documented range by the kernels, so malformed values give
+ *   meaningless results but no out-of-bounds access.
+ * - Every call is reentrant. Calls that write the same memory race unless
+ *   the caller orders them on one stream.
+ * - Tensors are dense and row-major in the order written, with the last
+ *   index fastest. Device pointers must be 16-byte aligned, except the int32
+ *   arrays (block table, positions, lengths), which need 4.
+ *
+ * KV cache layout (owned by the caller, written only by mfa_kv_append)
+ * ---------------------------------------------------------------------
+ * The cache of one layer holds one K head and one V head of width d. It is
+ * stored in blocks of MFA_BLOCK_TOKENS consecutive logical tokens of one
+ * sequence:
+ *   k       [num_blocks][64][d]   token-major blocks
+ *   v       [num_blocks][d][64]   dim-major (transposed) blocks
+ *   k_scale [num_blocks][64]      fp32, FP8 caches only (else NULL)
+ *   v_scale [num_blocks][64]      fp32, FP8 caches only (else NULL)
+ * Logical token t of sequence b is in logical block t/64 at offset t%64. The
+ * block table [B][max_blocks_per_seq] (int32, device) maps logical block j of
+ * sequence b to a physical block id. Without a block table (NULL) the cache
+ * is contiguous: logical block j of sequence b is physical block
+ * b*max_blocks_per_seq + j. The V blocks are transposed so that, for a fixed
+ * feature, 64 consecutive tokens are contiguous: that is the contraction
+ * order of p.V on the matrix cores.
+ *
+ * FP8 caches hold OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, max 448, no infinities) with one fp32 scale per token for K
+ * and one for V: scale = amax/448 over the token's d values (one correctly
+ * rounded fp32 division; 1 when amax = 0), code = round-to-nearest-even of
+ * the correctly rounded fp32 quotient x/scale. The stored value is
+ * code * scale.
+ */
+#ifndef MFA_H
+#define MFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MFA_ABI_VERSION 1
+#define MFA_BLOCK_TOKENS 64
+
+typedef enum {
+  MFA_OK = 0,
+  MFA_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  MFA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent        */
+  MFA_ERR_DTYPE = 3,        /* unsupported dtype or dtype combination        */
+  MFA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned       */
+  MFA_ERR_UNSUPPORTED = 5,  /* valid request this build has no kernel for    */
+  MFA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required    */
+  MFA_ERR_HIP = 7           /* the HIP runtime reported a launch failure     */
+} mfa_status;
+
+typedef enum {
+  MFA_F32 = 0,              /* IEEE binary32                                 */
+  MFA_BF16 = 1,             /* bfloat16                                      */
+  MFA_FP8_E4M3 = 2          /* OCP e4m3 ("e4m3fn"), KV caches only           */
+} mfa_dtype;
+
+/* Description of one layer's KV cache (host struct, read during the call). */
+typedef struct {
+  void *k;                      /* device: [num_blocks][64][d] of dtype      */
+  void *v;                      /* device: [num_blocks][d][64] of dtype      */
+  float *k_scale;               /* device: [num_blocks][64], FP8 only        */
+  float *v_scale;               /* device: [num_blocks][64], FP8 only        */
+  const int32_t *block_table;   /* device: [B][max_blocks_per_seq] or NULL   */
+  int32_t num_blocks;           /* physical blocks in k / v                  */
+  int32_t max_blocks_per_seq;   /* table row length; capacity = 64x this     */
+  int32_t head_dim;             /* d                                         */
+  int32_t dtype;                /* mfa_dtype of k and v                      */
+} mfa_kv_cache;
+
+/* Version of this ABI (MFA_ABI_VERSION of the built library). */
+int mfa_abi_version(void);
+
+/* Static, host-owned text for a status code. Never NULL. */
+const char *mfa_status_str(int status);
+
+/*
+ * Query path (§2 Step-3 Model Card: low-rank factorisation in the QK
+ * circuit; reading: down-projection, RMSNorm with gain, up-projection):
+ *   c = x W_qdown^T            (fp32 accumulation)
+ *   n = c / sqrt(mean(c^2) + eps) * g
+ *   q = n W_qup^T -> q_out[B][H][d]
+ * x        [B][hidden]          dtype
+ * w_qdown  [q_rank][hidden]     dtype (torch Linear [out][in])
+ * q_norm_w [q_rank]             fp32 gain g
+ * w_qup    [H*d][q_rank]        dtype
+ * q_out    [B][H][d]            dtype
+ * workspace: >= mfa_qproj_workspace_bytes(B, hidden, q_rank, H, d, dtype) bytes
+ *          (fp32 split-K partials and the normalised latent n).
+ * dtype: MFA_BF16 (c kept in fp32; n and q rounded to bf16) or MFA_F32 (all
+ * fp32). Limits: 1 <= B <= 256, q_rank <= 8192; bf16: hidden and q_rank
+ * multiples of 256, H*d a multiple of 64; fp32: multiples of 4.
+ */
+size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, int dtype);
+mfa_status mfa_qproj(const void *x, const void *w_qdown, const float *q_norm_w,
+                     const void *w_qup, void *q_out, void *workspace,
+                     size_t workspace_bytes, int B, int hidden, int q_rank,
+                     int H, int d, float eps, int dtype, void *stream);
+
+/*
+ * KV append (§7 Implementation and Results: attention instances own the KV
+ * caches): writes n_new consecutive tokens of every sequence b, logical
+ * positions pos[b] .. pos[b]+n_new-1, into the cache. The decode step uses
+ * n_new = 1; a larger n_new fills a cache from a prompt.
+ * k_new, v_new [B][n_new][d] of in_dtype (MFA_F32 or MFA_BF16).
+ * pos [B] int32 device. Positions must lie below 64*max_blocks_per_seq and
+ * their blocks must be mapped by the block table.
+ * Caches of dtype F32 or BF16 take inputs of the same dtype and store them
+ * bit for bit. FP8 caches quantise each token as documented above and
+ * store codes and scales.
+ * Sequence lengths are the caller's: after appending, the caller sets
+ * seq_lens[b] = pos[b] + n_new.
+ */
+mfa_status mfa_kv_append(const void *k_new, const void *v_new, int in_dtype,
+                         const int32_t *pos, int n_new, int B,
+                         const mfa_kv_cache *cache, void *stream);
+
+/*
+ * Split plan for mfa_decode_attn: the number of KV splits and tokens per
+ * split (a multiple of 64) this library would use for B sequences of at
+ * most max_seq_len tokens with H heads of width d. Host-only, no launch.
+ * Returns MFA_OK and writes *num_splits, *chunk_tokens (host pointers).
+ */
+mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
+                           int *num_splits, int *chunk_tokens);
+
+/* Bytes of split workspace for mfa_decode_attn / mfa_combine:
+ * part_o fp32 [B][num_splits][H][d] followed by part_ml fp32
+ * [B][num_splits][H][2] (running max m in natural-log units of the scaled
+ * logits, then l = sum_t exp(s_t - m)). 0 when num_splits == 1. */
+size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * Decode attention (§2/§5: all H query heads against one shared K/V head).
+ * q          [B][H][d] of q_dtype (MFA_BF16 with BF16/FP8 caches, MFA_F32 with
+ *            F32 caches)
+ * seq_lens   [B] int32 device: tokens of sequence b to attend (0..max_seq_len;
+ *            0 gives zeros)
+ * max_seq_len host upper bound of seq_lens (sizes the launch)
+ * sm_scale   logit scale (1/sqrt(d) for scaled dot products)
+ * num_splits >= 1 KV splits per sequence; split j covers tokens
+ *            [j*chunk_tokens, min((j+1)*chunk_tokens, seq_len)). Requires
+ *            chunk_tokens % 64 == 0 and num_splits*chunk_tokens >= max_seq_len.
+ * workspace  mfa_split_workspace_bytes(...) bytes when num_splits > 1
+ *            (receives the per-split partials), else may be NULL.
+ * out        [B][H][d] of out_dtype (MFA_BF16 or MFA_F32). With
+ *            num_splits > 1, out may be NULL: only the partials are
+ *            written and the caller runs mfa_combine; otherwise the library
+ *            merges the partials into out on the same stream.
+ * Supported: H in 1..64 and d in {64,128,256} with F32 caches (VALU kernel);
+ * H == 64 and d == 256 with BF16 or FP8 caches (matrix-core kernel).
+ */
+mfa_status mfa_decode_attn(const void *q, int q_dtype, int B, int H,
+                           const mfa_kv_cache *cache, const int32_t *seq_lens,
+                           int max_seq_len, float sm_scale, int num_splits,
+                           int chunk_tokens, void *workspace,
+                           size_t workspace_bytes, void *out, int out_dtype,
+                           void *stream);
+
+/*
+ * Split combine: merges the num_splits partials (layout as in
+ * mfa_split_workspace_bytes) of every (sequence, head) by log-sum-exp:
+ *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.
+ * Splits with l_j == 0 (empty) get weight 0; a head whose splits are all
+ * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32).
+ */
+mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
+                       int H, int d, int num_splits, void *out, int out_dtype,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_H */

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/mfa.h declares, and rejects malformed calls on the host before
+anything is launched. Fake device pointers are only ever passed to calls
+that fail validation, so no kernel runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfa.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+F32, BF16, FP8 = 0, 1, 2
+P = 0x10000          # fake, 16-byte aligned, never dereferenced
+PM = 0x10008         # fake, misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mfa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmfa.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert decl, "no declarations parsed"
+    assert sorted(_lib.SIGNATURES) == decl, "binding signatures differ from the header"
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mfa_abi_version() == 1
+    for s in range(8):
+        assert lib.mfa_status_str(s)
+    assert lib.mfa_status_str(99) == b"unknown status"
+
+
+def _cache(**kw):
+    d = _lib.KVCacheDesc()
+    d.k, d.v = P, P + 4096
+    d.k_scale = d.v_scale = None
+    d.block_table = None
+    d.num_blocks, d.max_blocks_per_seq, d.head_dim, d.dtype = 64, 16, 256, BF16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _attn(lib, cache, q=P, qdt=BF16, B=4, H=64, seq=P, maxlen=512, ns=1, chunk=512, ws=None,
+          wsb=0, out=P, odt=BF16):
+    return lib.mfa_decode_attn(q, qdt, B, H, ctypes.byref(cache), seq, maxlen, 0.0625, ns, chunk,
+                               ws, wsb, out, odt, None)
+
+
+def test_decode_attn_validation(lib):
+    c = _cache()
+    assert _attn(lib, c, q=None) == NULL
+    assert _attn(lib, c, seq=None) == NULL
+    assert _attn(lib, c, q=PM) == ALIGN
+    assert _attn(lib, _cache(k=PM)) == ALIGN
+    assert _attn(lib, _cache(dtype=7)) == DTYPE
+    assert _attn(lib, c, maxlen=16 * 64 + 1) == SHAPE            # beyond capacity
+    assert _attn(lib, c, ns=0) == SHAPE
+    assert _attn(lib, c, chunk=100) == SHAPE                     # not a multiple of 64
+    assert _attn(lib, c, ns=2, chunk=64, maxlen=512) == SHAPE    # splits do not cover
+    assert _attn(lib, c, ns=8, chunk=64, ws=None) == WS
+    assert _attn(lib, c, ns=8, chunk=64, ws=P, wsb=16) == WS
+    assert _attn(lib, c, qdt=F32) == DTYPE                       # bf16 cache, f32 q on MFMA path
+    assert _attn(lib, c, out=None) == NULL
+    assert _attn(lib, c, odt=FP8) == DTYPE
+    assert _attn(lib, c, B=5) == SHAPE                           # contiguous cache too small
+    assert _attn(lib, _cache(dtype=FP8)) == NULL                 # fp8 without scales
+    assert _attn(lib, _cache(dtype=FP8, k_scale=P, v_scale=P), H=32) == UNSUP
+    assert _attn(lib, _cache(head_dim=96)) == SHAPE
+
+
+def test_kv_append_validation(lib):
+    c = _cache()
+    ap = lambda **kw: lib.mfa_kv_append(kw.get("k", P), kw.get("v", P), kw.get("dt", BF16),
+                                        kw.get("pos", P), kw.get("n", 1), kw.get("B", 4),
+                                        ctypes.byref(kw.get("cache", c)), None)
+    assert ap(k=None) == NULL
+    assert ap(pos=None) == NULL
+    assert ap(v=PM) == ALIGN
+    assert ap(n=0) == SHAPE
+    assert ap(n=16 * 64 + 1) == SHAPE
+    assert ap(dt=F32) == DTYPE                                   # bf16 cache, f32 input
+    assert ap(dt=FP8) == DTYPE
+    assert ap(B=5) == SHAPE
+    assert lib.mfa_kv_append(P, P, BF16, P, 1, 4, None, None) == NULL
+
+
+def test_qproj_validation_and_workspace(lib):
+    q = lambda **kw: lib.mfa_qproj(kw.get("x", P), P, P, P, P, kw.get("ws", P),
+                                   kw.get("wsb", 1 << 30), kw.get("B", 32), kw.get("hid", 7168),
+                                   kw.get("r", 2048), 64, 256, 1e-6, kw.get("dt", BF16), None)
+    assert q(x=None) == NULL
+    assert q(x=PM) == ALIGN
+    assert q(B=0) == SHAPE
+    assert q(B=257) == SHAPE
+    assert q(hid=7000) == SHAPE
+    assert q(dt=FP8) == DTYPE
+    assert q(ws=None) == WS
+    need = lib.mfa_qproj_workspace_bytes(32, 7168, 2048, 64, 256, BF16)
+    assert need > 0
+    assert q(wsb=need - 1) == WS
+    assert lib.mfa_qproj_workspace_bytes(32, 7000, 2048, 64, 256, BF16) == 0
+    assert lib.mfa_qproj_workspace_bytes(2, 256, 128, 4, 64, F32) > 0
+
+
+def test_plan_and_split_workspace(lib):
+    ns, ch = ctypes.c_int(), ctypes.c_int()
+    for B, L in ((32, 4096), (128, 8193), (16, 32768), (4, 65536), (1, 1), (2, 0)):
+        assert lib.mfa_decode_plan(B, 64, 256, L, BF16, ctypes.byref(ns), ctypes.byref(ch)) == OK
+        assert ns.value >= 1 and ch.value % 64 == 0 and ns.value * ch.value >= L
+    assert lib.mfa_decode_plan(0, 64, 256, 10, BF16, ctypes.byref(ns), ctypes.byref(ch)) == SHAPE
+    assert lib.mfa_split_workspace_bytes(4, 64, 256, 1) == 0
+    rows = 4 * 32 * 64
+    assert lib.mfa_split_workspace_bytes(4, 64, 256, 32) == rows * 256 * 4 + rows * 2 * 4
+    assert lib.mfa_combine(None, 0, 4, 64, 256, 32, P, BF16, None) == NULL
+    assert lib.mfa_combine(P, 16, 4, 64, 256, 32, P, BF16, None) == WS
+    assert lib.mfa_combine(P, 1 << 30, 4, 64, 256, 1, P, BF16, None) == SHAPE

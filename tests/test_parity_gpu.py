@@ -1,0 +1,277 @@
+"""GPU parity: libmfa (through its C ABI) against the fp64 oracle on the same
+seeded inputs. Tolerances: bf16 and FP8-KV outputs rel-L2 <= 5e-3 and max
+abs <= 2e-2; fp32 rel-L2 <= 1e-5; KV append bit-exact."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import (MAX_ABS_BF16, REL_L2_BF16, REL_L2_F32, max_abs, rel_l2, run, say, setup,
+                      to_np)
+from oracle import mfa as omfa
+from oracle import run as orun
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def small(base, **kw):
+    return dataclasses.replace(W[base], **kw)
+
+
+def check_bf16(got, want, what):
+    r, m = rel_l2(got, want), max_abs(got, want)
+    say(f"{what}: rel_l2={r:.3e} max_abs={m:.3e}")
+    assert r <= REL_L2_BF16 and m <= MAX_ABS_BF16, (what, r, m)
+
+
+# ---------------------------------------------------------------- small cases
+# bf16 / fp8, paged and contiguous, ragged lengths spanning several blocks,
+# 1, 2, 3, 7 splits (chunk chosen to leave empty and partial splits).
+SMALL = [
+    ("bf16-contig", 3, dict(paged=False), [0, 63, 200]),
+    ("bf16-contig-tail", 3, dict(paged=False), [64, 129, 1]),
+    ("bf16-paged", 3, dict(), [1, 62, 63, 64, 65, 127, 300, 777]),
+    ("fp8-paged", 4, dict(), [0, 63, 64, 190, 513]),
+    ("fp8-contig", 4, dict(paged=False), [255, 70, 3]),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+@pytest.mark.parametrize("name,base,over,lens", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(gpu_lib, name, base, over, lens, splits):
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=101 + base)
+    say(f"small {name} splits={splits} lens={lens}")
+    maxlen = int(inp["seq_lens"].max())
+    chunk = -(-maxlen // splits)
+    chunk = -(-chunk // 64) * 64
+    T, cache, step = setup(inp, num_splits=splits, chunk_tokens=chunk)
+    _, out = run(T, step)
+    want = orun.decode_step(inp)
+    check_bf16(to_np(out), want["o"], f"{name}/S={splits}")
+
+
+def test_small_f32_generic(gpu_lib):
+    """fp32 cache and q on the vector-ALU kernel, ragged lengths, 1 and 3 splits."""
+    w = small(1, hidden=None, q_rank=None)
+    for splits in (1, 3):
+        inp = workloads.make_inputs(1, workload=w, prefill_lens=[0, 5, 130], seed=7)
+        say(f"f32 generic splits={splits}")
+        T, cache, step = setup(inp, num_splits=splits)
+        _, out = run(T, step)
+        want = orun.decode_step(inp)
+        r = rel_l2(to_np(out), want["o"])
+        say(f"f32 generic S={splits}: rel_l2={r:.3e}")
+        assert r <= REL_L2_F32
+
+
+def test_single_token_returns_v_exactly(gpu_lib):
+    """Context of one token: the output is V bit for bit (bf16 cache, bf16 out)."""
+    w = small(3, paged=False)
+    inp = workloads.make_inputs(3, workload=w, prefill_lens=[0, 0, 0], seed=3)
+    say("single token")
+    T, cache, step = setup(inp, num_splits=1)
+    _, out = run(T, step)
+    v = T["v_new"].view(3, 1, 256).expand(3, 64, 256)
+    assert torch.equal(out.cpu(), v.cpu())
+
+
+def test_physical_block_permutation_bit_identical(gpu_lib):
+    """Same logical tokens under two different block tables: identical bits."""
+    w = small(3)
+    lens = [100, 400, 250]
+    outs = []
+    for seed in (11, 12):          # seeds differ only in the block permutation
+        inp = workloads.make_inputs(3, workload=w, prefill_lens=lens, seed=10)
+        rng = np.random.default_rng(seed)
+        nblk = (inp["seq_lens"] + 63) // 64
+        perm = rng.permutation(inp["num_blocks"]).astype(np.int32)
+        bt = np.full_like(inp["block_table"], -1)
+        p = 0
+        for b in range(3):
+            bt[b, :nblk[b]] = perm[p:p + nblk[b]]
+            p += nblk[b]
+        inp["block_table"] = bt
+        say(f"block permutation seed={seed}")
+        T, cache, step = setup(inp, num_splits=2)
+        _, out = run(T, step)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_split_counts_agree(gpu_lib):
+    w = small(3)
+    inp = workloads.make_inputs(3, workload=w, prefill_lens=[2047, 1000], seed=5)
+    want = orun.decode_step(inp)["o"]
+    res = {}
+    for s in (1, 2, 7, 32):
+        say(f"split count {s}")
+        T, cache, step = setup(inp, num_splits=s)
+        _, out = run(T, step)
+        res[s] = to_np(out)
+        check_bf16(res[s], want, f"splits={s}")
+    for s in (2, 7, 32):
+        assert rel_l2(res[s], res[1]) <= 2 * REL_L2_BF16
+
+
+def test_combine_standalone(gpu_lib):
+    """mfa_combine on drawn partials (some splits empty) against the oracle's
+    log-sum-exp merge; fp32 output."""
+    import decode_attention_02_amd as mfa
+    rng = np.random.default_rng(77)
+    B, S, H, d = 3, 5, 64, 256
+    o = rng.standard_normal((B, S, H, d)).astype(np.float32)
+    m = (rng.standard_normal((B, S, H)) * 3).astype(np.float32)
+    l = rng.uniform(0.5, 40, size=(B, S, H)).astype(np.float32)
+    empty = rng.random((B, S, H)) < 0.3
+    empty[0, :, 0] = True                      # a head with every split empty
+    m[empty], l[empty], o[empty] = -np.inf, 0.0, 0.0
+    nbytes = mfa.split_workspace_bytes(B, H, d, S)
+    ws = np.zeros(nbytes, dtype=np.uint8)
+    rows = B * S * H
+    off = -(-rows * d * 4 // 256) * 256
+    ws[:rows * d * 4] = o.reshape(-1).view(np.uint8)
+    ws[off:off + rows * 8] = np.stack([m, l], axis=-1).reshape(-1).view(np.uint8)
+    say("combine standalone")
+    out = mfa.combine_splits(torch.from_numpy(ws).cuda(), B, H, d, S, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    for b in range(B):
+        want = omfa.combine([(o[b, s], m[b, s], l[b, s]) for s in range(S)])
+        assert rel_l2(got[b], want) <= 1e-6
+    assert np.all(got[0, 0] == 0)
+
+
+# ---------------------------------------------------------------- KV append
+@pytest.mark.parametrize("base,over,lens", [
+    (3, dict(), [10, 64, 130]),
+    (3, dict(paged=False), [5, 64, 70]),
+    (4, dict(), [10, 64, 200]),
+    (1, dict(hidden=None, q_rank=None), [3, 66]),
+])
+def test_append_bit_exact(gpu_lib, base, over, lens):
+    """Prefill + one appended token, then read back every token's stored
+    bytes (and FP8 scales) and compare with the oracle's codec and layout."""
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=41)
+    say(f"append bit-exact base={base} {over} {lens}")
+    T, cache, step = setup(inp, num_splits=1)
+    run(T, step)
+    exp, _ = orun.expected_cache_bytes(inp, range(len(lens)))
+    raw = {"f32": lambda t: t.cpu().numpy(), "bf16": lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16),
+           "fp8": lambda t: t.cpu().numpy()}[w.kv_dtype]
+    kg, vg = raw(cache.k), raw(cache.v)
+    for b, L in enumerate(inp["seq_lens"]):
+        rows = omfa.physical_rows(b, int(L), inp["block_table"], inp["max_blocks_per_seq"])
+        blk, off = rows // 64, rows % 64
+        assert np.array_equal(kg[blk, off].view(np.uint8), exp["k"][blk, off].view(np.uint8)), b
+        assert np.array_equal(vg[blk, :, off].view(np.uint8), exp["v"][blk, :, off].view(np.uint8)), b
+        if w.kv_dtype == "fp8":
+            ks, vs = cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()
+            assert np.array_equal(ks[blk, off].view(np.uint32), exp["k_scale"][blk, off].view(np.uint32))
+            assert np.array_equal(vs[blk, off].view(np.uint32), exp["v_scale"][blk, off].view(np.uint32))
+
+
+def test_fp8_codec_bit_exact_random_scales(gpu_lib):
+    """Quantise many random bf16 tokens at several magnitudes (incl. tiny and
+    zero rows) through mfa_kv_append; codes and scales equal the oracle's."""
+    import decode_attention_02_amd as mfa
+    rng = np.random.default_rng(9)
+    n, d = 512, 256
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-6, 3, size=(n, 1))).astype(np.float32)
+    x[5] = 0.0
+    x[6, :] = -np.abs(x[6])
+    bits = workloads.f32_to_bf16_bits(x)
+    xb = omfa.bf16_bits_to_f64(bits)
+    kc, ks = omfa.quantize_tokens(xb)
+    cache = mfa.KVCache(8, d, "fp8", 8)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda().view(1, n, d)
+    say("fp8 codec random")
+    mfa.kv_append(cache, t, t, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    got = cache.k.cpu().numpy().reshape(n, d)
+    assert np.array_equal(got, kc)
+    assert np.array_equal(cache.k_scale.cpu().numpy().reshape(n).view(np.uint32), ks.view(np.uint32))
+    gv = cache.v.cpu().numpy().transpose(0, 2, 1).reshape(n, d)
+    assert np.array_equal(gv, kc)
+
+
+# ---------------------------------------------------------------- query path
+def test_qproj_small_bf16(gpu_lib):
+    import decode_attention_02_amd as mfa
+    w = dataclasses.replace(W[2], batch=5, hidden=512, q_rank=256, heads=64, head_dim=256,
+                            context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=21)
+    T = workloads.to_torch(inp)
+    say("qproj small bf16")
+    q = mfa.qproj(T["x"], T["w_qdown"], T["g"], T["w_qup"], 64, 256)
+    torch.cuda.synchronize()
+    check_bf16(to_np(q), orun.query(inp), "qproj small")
+
+
+# ---------------------------------------------------------------- full sizes
+def test_full_tiny_f32(gpu_lib):
+    inp = workloads.make_inputs(1)
+    say("full tiny f32")
+    T, cache, step = setup(inp)
+    q, out = run(T, step)
+    want = orun.decode_step(inp)
+    rq, ro = rel_l2(to_np(q), want["q"]), rel_l2(to_np(out), want["o"])
+    say(f"tiny f32: q rel_l2={rq:.3e} o rel_l2={ro:.3e}")
+    assert rq <= REL_L2_F32 and ro <= REL_L2_F32
+
+
+def test_full_step3_bf16(gpu_lib):
+    inp = workloads.make_inputs(2)
+    say("full step3 bf16 4k")
+    T, cache, step = setup(inp)
+    say(f"plan: splits={step.num_splits} chunk={step.chunk_tokens}")
+    q, out = run(T, step)
+    want = orun.decode_step(inp)
+    check_bf16(to_np(q), want["q"], "step3 q")
+    check_bf16(to_np(out), want["o"], "step3 o")
+
+
+def test_full_paged_mixed(gpu_lib):
+    inp = workloads.make_inputs(3)
+    say("full paged mixed")
+    T, cache, step = setup(inp)
+    say(f"plan: splits={step.num_splits} chunk={step.chunk_tokens}")
+    _, out = run(T, step)
+    want = orun.decode_step(inp)
+    check_bf16(to_np(out), want["o"], "paged mixed")
+
+
+def test_full_fp8_32k_sampled(gpu_lib):
+    inp = workloads.make_inputs(4)
+    say("full fp8 32k")
+    T, cache, step = setup(inp)
+    say(f"plan: splits={step.num_splits} chunk={step.chunk_tokens}")
+    _, out = run(T, step)
+    seqs = [0, 7, 15]
+    want = orun.decode_step(inp, seqs=seqs)
+    check_bf16(to_np(out)[seqs], want["o"], "fp8 32k sampled")
+    # stored codes of the appended token of each sampled sequence
+    exp, _ = orun.expected_cache_bytes(inp, seqs)
+    kg = cache.k.cpu().numpy()
+    for b in seqs:
+        r = omfa.physical_rows(b, int(inp["seq_lens"][b]), inp["block_table"],
+                               inp["max_blocks_per_seq"])
+        blk, off = r // 64, r % 64
+        assert np.array_equal(kg[blk, off], exp["k"][blk, off])
+
+
+def test_full_split32_64k(gpu_lib):
+    inp = workloads.make_inputs(5)
+    say("full split32 64k")
+    T, cache, step = setup(inp)
+    assert step.num_splits == 32
+    q, out = run(T, step)
+    want = orun.decode_step(inp)
+    check_bf16(to_np(q), want["q"], "split32 q")
+    check_bf16(to_np(out), want["o"], "split32 o")

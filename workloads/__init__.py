@@ -101,11 +101,13 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = None,
-                context: Optional[int] = None, workload: Optional[Workload] = None):
+                context: Optional[int] = None, workload: Optional[Workload] = None,
+                prefill_lens=None):
     """Draw the inputs of one decode step of workload ``index``.
 
     ``batch`` / ``context`` shrink the workload (for tests that need a small
-    instance of the same structure); ``workload`` replaces it entirely.
+    instance of the same structure); ``workload`` replaces it entirely;
+    ``prefill_lens`` fixes the pre-append lengths (no length draw).
 
     Returns a dict of numpy arrays in storage form (see module docstring):
     ``x, w_qdown, g, w_qup`` or ``q``; ``k_ctx, v_ctx`` ([sum prefill][d],
@@ -126,7 +128,11 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
     kvin = "f32" if w.kv_dtype == "f32" else "bf16"
 
     # 1. lengths
-    if w.context_range is not None:
+    if prefill_lens is not None:
+        prefill = np.asarray(prefill_lens, dtype=np.int64)
+        w = dataclasses.replace(w, batch=len(prefill))
+        B = w.batch
+    elif w.context_range is not None:
         lo, hi = w.context_range
         if context is not None:           # shrunk instance keeps the spread, scaled
             lo, hi = max(1, context // 8), context
@@ -179,4 +185,40 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
         out["block_table"] = None
         out["num_blocks"] = B * max_blocks
     out["max_blocks_per_seq"] = max_blocks
+    return out
+
+
+def to_torch(inp, device="cuda"):
+    """Copy the drawn arrays to ``device`` as torch tensors (bf16 bits are
+    reinterpreted as torch.bfloat16, fp32 stays float32, int32 stays int32).
+    Pure data movement."""
+    import torch
+
+    w = inp["workload"]
+
+    def t(a, dt):
+        if dt == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(
+            torch.bfloat16).to(device)
+
+    kvin = "f32" if w.kv_dtype == "f32" else "bf16"
+    out = {"workload": w}
+    if w.has_qproj:
+        for k in ("x", "w_qdown", "w_qup"):
+            out[k] = t(inp[k], w.act_dtype)
+        out["g"] = torch.from_numpy(inp["g"]).to(device)
+    else:
+        out["q"] = t(inp["q"], w.act_dtype)
+    for k in ("k_ctx", "v_ctx", "k_new", "v_new"):
+        out[k] = t(inp[k], kvin)
+    out["ctx_offsets"] = inp["ctx_offsets"]
+    out["prefill_lens"] = torch.from_numpy(inp["prefill_lens"]).to(device)
+    out["seq_lens"] = torch.from_numpy(inp["seq_lens"]).to(device)
+    out["block_table"] = (torch.from_numpy(inp["block_table"]).to(device)
+                          if inp["block_table"] is not None else None)
+    for k in ("num_blocks", "max_blocks_per_seq"):
+        out[k] = inp[k]
+    out["prefill_host"] = inp["prefill_lens"]
+    out["seq_lens_host"] = inp["seq_lens"]
     return out

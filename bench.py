@@ -9,11 +9,12 @@ cache). Inputs are seeded and synthetic and resident in HBM before timing;
 ``--rotate`` independent copies of cache and weights are cycled so that the
 256 MB last-level cache cannot hold a step's working set.
 
-Prints one JSON line (see the project's measurement contract): throughput in
-decode tokens/s, the attention kernel's roofline (algorithmic KV bytes per
-launch / its average duration from HIP events recorded around every launch
-inside the timed region), and the fp64 oracle timed on a bounded sample on
-the host cores.
+The steps are captured once into HIP graphs (no allocation happens inside a
+step) and replayed, so the GPU runs them back to back. Prints one JSON line:
+throughput in decode tokens/s over K timed steps; the attention kernel's
+roofline (algorithmic KV bytes per launch / its average duration, from HIP
+events around K back-to-back attention launches on the same buffers); and
+the fp64 oracle timed on the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
     return ap.parse_args()
 
 
@@ -72,12 +73,11 @@ def kernel_source_sig() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(inp, n_seq: int):
-    """fp64 oracle on the first n_seq sequences of the same inputs (query
-    path for those rows, cache fill, attention). Returns the record."""
-    import copy
-
-    import numpy as np
+def cpu_baseline(inp, min_seconds: float = 10.0):
+    """fp64 oracle on the same inputs: the whole batch (query path, cache
+    fill, attention of every sequence), repeated until ``min_seconds`` of
+    host time have passed. Returns the record."""
+    import numpy as np  # noqa: F401
     from oracle import run as orun
     try:
         from threadpoolctl import threadpool_info
@@ -85,16 +85,18 @@ def cpu_baseline(inp, n_seq: int):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     w = inp["workload"]
-    sub = copy.copy(inp)
-    seqs = list(range(n_seq))
-    t0 = time.perf_counter()
-    orun.decode_step(sub, seqs=seqs)
-    dt = time.perf_counter() - t0
-    toks = sum(int(inp["seq_lens"][b]) for b in seqs)
-    return {"value": n_seq / dt, "unit": "decode tokens/s", "cores": int(threads),
+    runs, total = 0, 0.0
+    while total < min_seconds and runs < 50:
+        t0 = time.perf_counter()
+        orun.decode_step(inp)
+        total += time.perf_counter() - t0
+        runs += 1
+    dt = total / runs
+    toks = int(inp["seq_lens"].sum())
+    return {"value": w.batch / dt, "unit": "decode tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_seq} of {w.batch} sequences of workload {w.name} "
-                      f"({toks} cached tokens, full query path for all rows), {dt:.1f} s fp64 numpy"}
+            "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
+                      f"tokens), fp64 numpy, mean of {runs} runs ({dt:.2f} s each)"}
 
 
 def main():
@@ -140,42 +142,75 @@ def main():
         sets.append((step, wts))
     torch.cuda.synchronize()
 
-    def one(i, ev=None):
-        step, wts = sets[i % rotate]
-        if w.has_qproj:
-            q = step.query(T["x"], *wts)
-        else:
-            q = T["q"]
-        step.append(T["k_new"], T["v_new"], T["prefill_lens"])
-        if ev is not None:
-            ev[0].record()
+    def attention(i, q):
+        step = sets[i % rotate][0]
         if step.num_splits > 1:
             mfa.decode_attn(q, step.cache, T["seq_lens"], step.max_seq_len, step.sm_scale,
                             step.num_splits, step.chunk_tokens, workspace=step.split_ws,
                             combine=False)
-            if ev is not None:
-                ev[1].record()
-            mfa.combine_splits(step.split_ws, B, w.heads, w.head_dim, step.num_splits, out=step.out)
         else:
             step.attend(q, T["seq_lens"])
-            if ev is not None:
-                ev[1].record()
 
-    for i in range(args.warmup):
-        one(i)
+    def one(i):
+        """One decode step on buffer set i % rotate: qproj, append, attention, combine."""
+        step, wts = sets[i % rotate]
+        q = step.query(T["x"], *wts) if w.has_qproj else T["q"]
+        step.append(T["k_new"], T["v_new"], T["prefill_lens"])
+        attention(i, q)
+        if step.num_splits > 1:
+            mfa.combine_splits(step.split_ws, B, w.heads, w.head_dim, step.num_splits, out=step.out)
+
+    q_fixed = [sets[r][0].q if w.has_qproj else T["q"] for r in range(rotate)]
+
+    def capture(fn):
+        """HIP graph of fn's launches (one graph launch replays them back to back)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    use_graph = not args.eager
+    if use_graph:
+        g_warm = capture(lambda: [one(i) for i in range(args.warmup)])
+        g_steps = capture(lambda: [one(i) for i in range(args.steps)])
+        g_attn = capture(lambda: [attention(i, q_fixed[i % rotate]) for i in range(args.steps)])
+    # warmup
+    if use_graph:
+        g_warm.replay()
+    else:
+        for i in range(args.warmup):
+            one(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region 1: K whole steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
-        one(i, evs[i])
+    if use_graph:
+        g_steps.replay()
+    else:
+        for i in range(args.steps):
+            one(i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg = float(np.mean(attn_ms))
+    # timed region 2: K attention launches back to back (same buffers, same
+    # rotation), bracketed by HIP events on the launching stream
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    if use_graph:
+        g_attn.replay()
+    else:
+        for i in range(args.steps):
+            attention(i, q_fixed[i % rotate])
+    a1.record()
+    torch.cuda.synchronize()
+    attn_avg = a0.elapsed_time(a1) / args.steps
     achieved = kv_bytes / (attn_avg * 1e-3) / 1e9
     step0 = sets[0][0]
     traffic = counters_for(w.name, kernel_source_sig())
@@ -206,8 +241,7 @@ def main():
         "step_kv_plus_weights_GBps": (kv_bytes + w_bytes) / (ms * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample or (1 if w.batch <= 4 else min(4, w.batch))
-        rec["cpu_baseline"] = cpu_baseline(inp, n)
+        rec["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(rec), flush=True)
 
 

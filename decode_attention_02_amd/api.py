@@ -36,10 +36,11 @@ def _dev(t: torch.Tensor, name: str):
 class KVCache:
     """One layer's KV cache in libmfa's block layout (see include/mfa.h).
 
-    k [num_blocks][64][d], v [num_blocks][d][64] of the cache dtype; FP8
-    caches add fp32 k_scale / v_scale [num_blocks][64]. ``block_table``
-    [B][max_blocks_per_seq] int32 (None: contiguous, sequence b owns blocks
-    b*max_blocks_per_seq ..).
+    k and v hold num_blocks blocks of 64*d elements of the cache dtype (the
+    element order inside a block is the library's, written only by
+    ``kv_append``); FP8 caches add fp32 k_scale / v_scale [num_blocks][64].
+    ``block_table`` [B][max_blocks_per_seq] int32 (None: contiguous,
+    sequence b owns blocks b*max_blocks_per_seq ..).
     """
 
     def __init__(self, num_blocks: int, head_dim: int, dtype: str, max_blocks_per_seq: int,
@@ -50,8 +51,8 @@ class KVCache:
         self.max_blocks_per_seq = int(max_blocks_per_seq)
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
         alloc = torch.zeros if zero else torch.empty
-        self.k = alloc((self.num_blocks, BLOCK_TOKENS, self.head_dim), dtype=tdt, device=device)
-        self.v = alloc((self.num_blocks, self.head_dim, BLOCK_TOKENS), dtype=tdt, device=device)
+        self.k = alloc((self.num_blocks, BLOCK_TOKENS * self.head_dim), dtype=tdt, device=device)
+        self.v = alloc((self.num_blocks, BLOCK_TOKENS * self.head_dim), dtype=tdt, device=device)
         if dtype == "fp8":
             self.k_scale = alloc((self.num_blocks, BLOCK_TOKENS), dtype=torch.float32, device=device)
             self.v_scale = alloc((self.num_blocks, BLOCK_TOKENS), dtype=torch.float32, device=device)

@@ -6,6 +6,7 @@
 // over 8-token tiles, natural exp.
 #include "device_common.h"
 #include "kernels.h"
+#include "kv_layout.h"
 
 namespace mfa {
 
@@ -54,14 +55,17 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
         const int tok = tt + t;
         int id = bt_row ? bt_row[tok >> 6] : b * a.max_blocks_per_seq + (tok >> 6);
         id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-        const size_t kidx = (static_cast<size_t>(id) * kBlockTokens + (tok & 63)) * D + j;
-        const size_t vidx = (static_cast<size_t>(id) * D + j) * kBlockTokens + (tok & 63);
+        const int off = tok & 63;
         if (a.kv_f32) {
-          kv = reinterpret_cast<const float*>(a.k)[kidx];
-          vv = reinterpret_cast<const float*>(a.v)[vidx];
+          const uint8_t* kb = a.k + static_cast<size_t>(id) * kBlockTokens * D * 4;
+          const uint8_t* vb = a.v + static_cast<size_t>(id) * kBlockTokens * D * 4;
+          kv = *reinterpret_cast<const float*>(kb + k_off_f32(off, j, D));
+          vv = *reinterpret_cast<const float*>(vb + v_off_f32(off, j));
         } else {
-          kv = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[kidx]);
-          vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.v)[vidx]);
+          const uint8_t* kb = a.k + static_cast<size_t>(id) * kBlockTokens * D * 2;
+          const uint8_t* vb = a.v + static_cast<size_t>(id) * kBlockTokens * D * 2;
+          kv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(kb + k_off_bf16(off, j, D)));
+          vv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(vb + v_off_bf16(off, j)));
         }
       }
       k_s[t][j] = kv;

@@ -11,39 +11,58 @@
 
 namespace mfa {
 
+// One workgroup of 256 threads covers 1024/d heads of one sequence; a thread
+// owns 4 consecutive features of one head and reads one float4 per split.
 __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int S, int H, int d, void* out,
                                                           int out_f32) {
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H;
+  const int tpb = d >> 2;                        // threads per head
+  const int hpb = 256 / tpb;                     // heads per workgroup
+  const int groups = (H + hpb - 1) / hpb;
+  const int b = blockIdx.x / groups;
+  const int h = (blockIdx.x % groups) * hpb + threadIdx.x / tpb;
+  const int f = (threadIdx.x % tpb) * 4;
+  if (h >= H) return;
   const size_t row0 = static_cast<size_t>(b) * S;
   float mstar = -INFINITY;
   for (int s = 0; s < S; ++s) {
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row0 + s) * H + h) * 2);
     if (ml.y > 0.f) mstar = fmaxf(mstar, ml.x);
   }
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row0 + s) * H + h) * 2);
-      if (ml.y > 0.f) {
-        const float wgt = expf(ml.x - mstar);
-        den = fmaf(wgt, ml.y, den);
-        num = fmaf(wgt, part_o[((row0 + s) * H + h) * d + j], num);
-      }
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row0 + s) * H + h) * 2);
+    if (ml.y > 0.f) {
+      const float wgt = expf(ml.x - mstar);
+      den = fmaf(wgt, ml.y, den);
+      const float4 o = *reinterpret_cast<const float4*>(part_o + ((row0 + s) * H + h) * d + f);
+      num.x = fmaf(wgt, o.x, num.x);
+      num.y = fmaf(wgt, o.y, num.y);
+      num.z = fmaf(wgt, o.z, num.z);
+      num.w = fmaf(wgt, o.w, num.w);
     }
-    const float val = den > 0.f ? num / den : 0.f;
-    const size_t oi = (static_cast<size_t>(b) * H + h) * d + j;
-    if (out_f32) reinterpret_cast<float*>(out)[oi] = val;
-    else reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(val);
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const size_t oi = (static_cast<size_t>(b) * H + h) * d + f;
+  if (out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(num.x * inv, num.y * inv);
+    pk.y = pack_bf16x2(num.z * inv, num.w * inv);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = pk;
   }
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
                           int num_splits, void* out, int out_f32, hipStream_t stream) {
-  const int threads = d >= 256 ? 256 : ((d + 63) / 64) * 64;
-  hipLaunchKernelGGL(mfa_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(threads), 0,
+  if (d % 4 || d > 1024) return hipErrorInvalidValue;
+  const int hpb = 256 / (d / 4);
+  const int groups = (H + hpb - 1) / hpb;
+  hipLaunchKernelGGL(mfa_combine_kernel, dim3(static_cast<unsigned>(B * groups)), dim3(256), 0,
                      stream, part_o, part_ml, num_splits, H, d, out, out_f32);
   return hipGetLastError();
 }

@@ -61,9 +61,12 @@ struct AppendArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 
 // Query path.
-// bf16: C partials [ks][M][N] fp32 = A[M][K] . W[N][K]^T over K slice ks.
-hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* W, float* part, int M,
-                                   int N, int K, int ksplit, hipStream_t stream);
+// bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 64. With ksplit > 1 writes fp32
+// partials part[ks][M][N] (K slice ks); with ksplit == 1 and out_bf16 set,
+// writes bf16 C directly. ntiles (2 or 4) = 16-column tiles per workgroup.
+// Requires N % (16*ntiles) == 0 and (K/ksplit) % 32 == 0.
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
+                            int M, int N, int K, int ksplit, int ntiles, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
                                  float eps, void* out, int out_f32, hipStream_t stream);

@@ -5,12 +5,13 @@
 // raising arithmetic intensity.
 //
 // One workgroup covers the new tokens of one sequence that fall into one
-// 64-token block. F32/BF16 caches copy bits; K rows are token-major, V blocks
-// feature-major (transposed). FP8 caches quantise each token: amax over the
-// token's d values, scale = amax/448 (correctly rounded fp32 division, 1
-// when amax = 0), code = RNE e4m3 of the correctly rounded quotient x/scale.
+// 64-token block. F32/BF16 caches copy bits; FP8 caches quantise each token:
+// amax over the token's d values, scale = amax/448 (correctly rounded fp32
+// division, 1 when amax = 0), code = RNE e4m3 of the correctly rounded
+// quotient x/scale. Element positions inside a block follow kv_layout.h.
 #include "device_common.h"
 #include "kernels.h"
+#include "kv_layout.h"
 
 namespace mfa {
 
@@ -45,6 +46,18 @@ __device__ __forceinline__ Span block_span(const AppendArgs& a, int b, int jj) {
 }  // namespace
 
 template <typename T>
+__device__ __forceinline__ uint32_t k_off(int t, int d, int D) {
+  if constexpr (sizeof(T) == 4) return k_off_f32(t, d, D);
+  else return k_off_bf16(t, d, D);
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t v_off(int t, int f) {
+  if constexpr (sizeof(T) == 4) return v_off_f32(t, f);
+  else return v_off_bf16(t, f);
+}
+
+template <typename T>
 __global__ __launch_bounds__(256) void kv_append_copy_kernel(AppendArgs a) {
   const int b = blockIdx.x;
   const Span sp = block_span(a, b, blockIdx.y);
@@ -52,12 +65,13 @@ __global__ __launch_bounds__(256) void kv_append_copy_kernel(AppendArgs a) {
   const int n = sp.hi - sp.lo, off0 = sp.lo & 63, i0 = sp.lo - sp.p0, d = a.d;
   const T* kin = reinterpret_cast<const T*>(a.k_new) + (static_cast<size_t>(b) * a.n_new + i0) * d;
   const T* vin = reinterpret_cast<const T*>(a.v_new) + (static_cast<size_t>(b) * a.n_new + i0) * d;
-  T* kc = reinterpret_cast<T*>(a.k) + (static_cast<size_t>(sp.blk) * kBlockTokens + off0) * d;
-  T* vc = reinterpret_cast<T*>(a.v) + static_cast<size_t>(sp.blk) * d * kBlockTokens + off0;
-  for (int idx = threadIdx.x; idx < n * d; idx += 256) kc[idx] = kin[idx];   // rows contiguous
-  for (int idx = threadIdx.x; idx < n * d; idx += 256) {                     // token fastest
-    const int jd = idx / n, t = idx % n;
-    vc[jd * kBlockTokens + t] = vin[static_cast<size_t>(t) * d + jd];
+  const size_t block_bytes = static_cast<size_t>(kBlockTokens) * d * sizeof(T);
+  uint8_t* kc = a.k + static_cast<size_t>(sp.blk) * block_bytes;
+  uint8_t* vc = a.v + static_cast<size_t>(sp.blk) * block_bytes;
+  for (int idx = threadIdx.x; idx < n * d; idx += 256) {
+    const int t = idx / d, jd = idx % d;
+    *reinterpret_cast<T*>(kc + k_off<T>(off0 + t, jd, d)) = kin[idx];
+    *reinterpret_cast<T*>(vc + v_off<T>(off0 + t, jd)) = vin[idx];
   }
 }
 
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
   if (sp.lo >= sp.hi || sp.blk < 0) return;
   const int n = sp.hi - sp.lo, off0 = sp.lo & 63, i0 = sp.lo - sp.p0, d = a.d;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint8_t* kc = a.k + (static_cast<size_t>(sp.blk) * kBlockTokens + off0) * d;
+  uint8_t* kc = a.k + static_cast<size_t>(sp.blk) * kBlockTokens * d;
   for (int t = w; t < n; t += 4) {
     const size_t row = (static_cast<size_t>(b) * a.n_new + i0 + t) * d;
     float xk[EPT], xv[EPT];
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int jd = lane * EPT + e;
-      kc[static_cast<size_t>(t) * d + jd] = static_cast<uint8_t>(encode_e4m3_rne(xk[e] / sk));
+      kc[k_off_fp8(off0 + t, jd, d)] = static_cast<uint8_t>(encode_e4m3_rne(xk[e] / sk));
       vt[jd][t] = static_cast<uint8_t>(encode_e4m3_rne(xv[e] / sv));
     }
     if (lane == 0) {
@@ -97,16 +111,86 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
     }
   }
   __syncthreads();
-  uint8_t* vc = a.v + static_cast<size_t>(sp.blk) * d * kBlockTokens + off0;
+  uint8_t* vc = a.v + static_cast<size_t>(sp.blk) * d * kBlockTokens;
   for (int idx = threadIdx.x; idx < n * d; idx += 256) {
     const int jd = idx / n, t = idx % n;
-    vc[jd * kBlockTokens + t] = vt[jd][t];
+    vc[v_off_fp8(off0 + t, jd)] = vt[jd][t];
   }
+}
+
+// Decode-step append (one new token per sequence): one wave per sequence,
+// lane l owns features l*EPT .. l*EPT+EPT-1.
+template <int CACHE, int EPT>   // CACHE: 0 f32, 1 bf16, 2 fp8
+__global__ __launch_bounds__(64) void kv_append_one_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const Span sp = block_span(a, b, 0);
+  if (sp.lo >= sp.hi || sp.blk < 0) return;
+  const int d = a.d;
+  const int off = sp.lo & 63;
+  const size_t row = static_cast<size_t>(b) * d;   // n_new == 1
+  float xk[EPT], xv[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    xk[e] = load_in(a.k_new, row + lane * EPT + e, a.in_f32);
+    xv[e] = load_in(a.v_new, row + lane * EPT + e, a.in_f32);
+  }
+  const size_t esz = CACHE == 0 ? 4 : (CACHE == 1 ? 2 : 1);
+  uint8_t* kb = a.k + static_cast<size_t>(sp.blk) * kBlockTokens * d * esz;
+  uint8_t* vb = a.v + static_cast<size_t>(sp.blk) * kBlockTokens * d * esz;
+  if constexpr (CACHE == 2) {
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) { ak = fmaxf(ak, fabsf(xk[e])); av = fmaxf(av, fabsf(xv[e])); }
+    ak = wave_max(ak);
+    av = wave_max(av);
+    const float sk = ak > 0.f ? ak / 448.0f : 1.0f;
+    const float sv = av > 0.f ? av / 448.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      kb[k_off_fp8(off, f, d)] = static_cast<uint8_t>(encode_e4m3_rne(xk[e] / sk));
+      vb[v_off_fp8(off, f)] = static_cast<uint8_t>(encode_e4m3_rne(xv[e] / sv));
+    }
+    if (lane == 0) {
+      a.k_scale[static_cast<size_t>(sp.blk) * kBlockTokens + off] = sk;
+      a.v_scale[static_cast<size_t>(sp.blk) * kBlockTokens + off] = sv;
+    }
+  } else if constexpr (CACHE == 1) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      *reinterpret_cast<uint16_t*>(kb + k_off_bf16(off, f, d)) = f32_to_bf16(xk[e]);  // exact
+      *reinterpret_cast<uint16_t*>(vb + v_off_bf16(off, f)) = f32_to_bf16(xv[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      *reinterpret_cast<float*>(kb + k_off_f32(off, f, d)) = xk[e];
+      *reinterpret_cast<float*>(vb + v_off_f32(off, f)) = xv[e];
+    }
+  }
+}
+
+template <int CACHE>
+static void launch_one(const AppendArgs& a, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(a.B)), block(64);
+  if (a.d == 64) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 1>), grid, block, 0, stream, a);
+  else if (a.d == 128) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 2>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 4>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(a.B), static_cast<unsigned>((a.n_new + kBlockTokens - 1) / kBlockTokens + 1));
   dim3 block(256);
+  if (a.d != 64 && a.d != 128 && a.d != 256) return hipErrorInvalidValue;
+  if (a.n_new == 1) {
+    if (a.cache_dtype == 0) launch_one<0>(a, stream);
+    else if (a.cache_dtype == 1) launch_one<1>(a, stream);
+    else launch_one<2>(a, stream);
+    return hipGetLastError();
+  }
   switch (a.cache_dtype) {
     case 0: hipLaunchKernelGGL(kv_append_copy_kernel<float>, grid, block, 0, stream, a); break;
     case 1: hipLaunchKernelGGL(kv_append_copy_kernel<uint16_t>, grid, block, 0, stream, a); break;

@@ -24,25 +24,28 @@ mfa_status from_hip(hipError_t e) { return e == hipSuccess ? MFA_OK : MFA_ERR_HI
 
 // ---- query path planning -------------------------------------------------
 constexpr int kRowsPerPass = 64;     // matrix-core GEMM handles <= 64 rows per pass
-constexpr int kKStage = 256;
 
-// K splits of a skinny bf16 product: the smallest divisor of K/256 (<= 16)
-// that gives >= 512 workgroups, else the largest such divisor.
-int pick_ksplit(int N, int K) {
-  const int stages = K / kKStage;
-  const int tiles = N / 64;
-  int best = 1;
-  for (int ks = 1; ks <= 16 && ks <= stages; ++ks) {
-    if (stages % ks) continue;
-    best = ks;
-    if (tiles * ks >= 512) break;
-  }
-  return best;
+struct GemmPlan {
+  int ntiles;        // 16-column tiles per workgroup (2 or 4)
+  int ks;            // K slices
+};
+
+// Column tiles of 32 (64 when N is not a multiple of 32... it always is for
+// the admitted shapes); K is halved until the grid reaches 512 workgroups or
+// a slice would drop below 8 k-steps of 32.
+GemmPlan plan_gemm(int N, int K) {
+  GemmPlan p{N % 32 == 0 ? 2 : 4, 1};
+  const int tiles = N / (16 * p.ntiles);
+  const int steps = K / 32;
+  while (static_cast<long long>(tiles) * p.ks < 512 && steps % (p.ks * 2) == 0 &&
+         steps / (p.ks * 2) >= 8)
+    p.ks *= 2;
+  return p;
 }
 
 struct QprojPlan {
   int rows;          // rows per pass
-  int ks_down, ks_up;
+  GemmPlan down, up;
   size_t off_part_down, off_n, off_part_up, total;
 };
 
@@ -50,14 +53,15 @@ QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype) {
   QprojPlan p{};
   p.rows = B < kRowsPerPass ? B : kRowsPerPass;
   if (dtype == MFA_BF16) {
-    p.ks_down = pick_ksplit(q_rank, hidden);
-    p.ks_up = pick_ksplit(HD, q_rank);
+    p.down = plan_gemm(q_rank, hidden);
+    p.up = plan_gemm(HD, q_rank);
     p.off_part_down = 0;
-    p.off_n = round_up(static_cast<size_t>(p.ks_down) * p.rows * q_rank * 4, 256);
+    p.off_n = round_up(static_cast<size_t>(p.down.ks) * p.rows * q_rank * 4, 256);
     p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 2, 256);
-    p.total = p.off_part_up + round_up(static_cast<size_t>(p.ks_up) * p.rows * HD * 4, 256);
+    p.total = p.off_part_up +
+              (p.up.ks > 1 ? round_up(static_cast<size_t>(p.up.ks) * p.rows * HD * 4, 256) : 0);
   } else {
-    p.ks_down = p.ks_up = 1;
+    p.down = p.up = GemmPlan{0, 1};
     p.off_part_down = 0;
     p.off_n = round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
     p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
@@ -73,9 +77,9 @@ mfa_status check_qproj_shape(int B, int hidden, int q_rank, int H, int d, int dt
   const long long hd = static_cast<long long>(H) * d;
   if (hd > (1 << 24)) return MFA_ERR_SHAPE;
   if (dtype == MFA_BF16) {
-    if (hidden % kKStage || q_rank % kKStage || hd % 64 || q_rank % 64) return MFA_ERR_SHAPE;
+    if (hidden % 256 || q_rank % 256 || hd % 64) return MFA_ERR_SHAPE;
   } else {
-    if (hidden % 4 || q_rank % 4 || hd % 4) return MFA_ERR_SHAPE;
+    if (hidden % 4 || q_rank % 8 || hd % 4) return MFA_ERR_SHAPE;
   }
   return MFA_OK;
 }
@@ -100,7 +104,7 @@ mfa_status check_cache(const mfa_kv_cache* c) {
     if (!aligned16(c->k_scale) || !aligned16(c->v_scale)) return MFA_ERR_ALIGN;
   }
   if (c->num_blocks < 1 || c->max_blocks_per_seq < 1) return MFA_ERR_SHAPE;
-  if (c->head_dim < 1 || c->head_dim > 256 || c->head_dim % 64) return MFA_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return MFA_ERR_SHAPE;
   if (c->block_table && !aligned4(c->block_table)) return MFA_ERR_ALIGN;
   if (static_cast<long long>(c->max_blocks_per_seq) * kBlock > (1ll << 30)) return MFA_ERR_SHAPE;
   return MFA_OK;
@@ -157,17 +161,22 @@ mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, 
     if (dtype == MFA_BF16) {
       float* pd = reinterpret_cast<float*>(ws + p.off_part_down);
       uint16_t* n = reinterpret_cast<uint16_t*>(ws + p.off_n);
-      e = mfa::launch_gemm_bf16_splitk(reinterpret_cast<const uint16_t*>(xa),
-                                       static_cast<const uint16_t*>(w_qdown), pd, M, q_rank, hidden,
-                                       p.ks_down, st);
+      e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
+                                static_cast<const uint16_t*>(w_qdown), pd, nullptr, M, q_rank,
+                                hidden, p.down.ks, p.down.ntiles, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(pd, p.ks_down, q_norm_w, M, q_rank, eps, n, 0, st);
+      e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, q_norm_w, M, q_rank, eps, n, 0, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      float* pu = reinterpret_cast<float*>(ws + p.off_part_up);
-      e = mfa::launch_gemm_bf16_splitk(n, static_cast<const uint16_t*>(w_qup), pu, M, HD, q_rank,
-                                       p.ks_up, st);
-      if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_reduce_cast(pu, p.ks_up, M, HD, qo, 0, st);
+      if (p.up.ks == 1) {
+        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), nullptr,
+                                  reinterpret_cast<uint16_t*>(qo), M, HD, q_rank, 1, p.up.ntiles, st);
+      } else {
+        float* pu = reinterpret_cast<float*>(ws + p.off_part_up);
+        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), pu, nullptr, M, HD,
+                                  q_rank, p.up.ks, p.up.ntiles, st);
+        if (e != hipSuccess) return MFA_ERR_HIP;
+        e = mfa::launch_reduce_cast(pu, p.up.ks, M, HD, qo, 0, st);
+      }
       if (e != hipSuccess) return MFA_ERR_HIP;
     } else {
       float* c = reinterpret_cast<float*>(ws + p.off_part_down);
@@ -223,21 +232,21 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, i
   if (!num_splits || !chunk_tokens) return MFA_ERR_NULL;
   if (B < 1 || H < 1 || d < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
   (void)kv_dtype;
+  (void)H;
+  (void)d;
   const int blocks = (max_seq_len + kBlock - 1) / kBlock;
-  // Aim for >= 1024 workgroups (four per compute unit) without making a
-  // split shorter than 4 blocks; long contexts keep at least 16 blocks/split.
-  int splits = 1;
-  if (blocks > 0) {
-    const int want = (1024 + B - 1) / B;
-    int per = (blocks + want - 1) / want;
-    if (per < 4) per = 4;
-    splits = (blocks + per - 1) / per;
-    if (splits < 1) splits = 1;
-  }
-  int per_blocks = blocks > 0 ? (blocks + splits - 1) / splits : 1;
-  splits = blocks > 0 ? (blocks + per_blocks - 1) / per_blocks : 1;
+  // One 8-wave attention workgroup per compute unit of an MI355X (256 CUs):
+  // split each sequence so that the grid covers the chip once, with splits
+  // of whole 128-token tiles (two cache blocks).
+  constexpr int kTargetWorkgroups = 256;
+  int splits = kTargetWorkgroups / B;
+  if (splits < 1) splits = 1;
+  if (splits > blocks / 2) splits = blocks / 2 > 0 ? blocks / 2 : 1;
+  int per = blocks > 0 ? (blocks + splits - 1) / splits : 2;
+  per = (per + 1) / 2 * 2;
+  splits = blocks > 0 ? (blocks + per - 1) / per : 1;
   *num_splits = splits;
-  *chunk_tokens = per_blocks * kBlock;
+  *chunk_tokens = per * kBlock;
   return MFA_OK;
 }
 
@@ -325,7 +334,8 @@ mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int
                        int num_splits, void* out, int out_dtype, void* stream) {
   if (!workspace || !out) return MFA_ERR_NULL;
   if (!aligned16(workspace) || !aligned16(out)) return MFA_ERR_ALIGN;
-  if (B < 1 || H < 1 || d < 1 || d > 4096 || num_splits < 2) return MFA_ERR_SHAPE;
+  if (B < 1 || H < 1 || num_splits < 2) return MFA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B) * num_splits * H;

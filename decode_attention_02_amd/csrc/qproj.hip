@@ -8,102 +8,145 @@
 //
 // At decode batch sizes (M <= 64 rows) both products are skinny: every
 // weight byte is used by at most 64 rows, so they are bound by the weight
-// stream from HBM. The bf16 kernel streams each weight row slice straight
-// into registers in matrix-core operand layout (16 contiguous bytes per
-// lane), stages the small activation panel through LDS, splits K across
-// workgroups so that the grid covers the chip, and leaves fp32 partials;
-// the RMSNorm (for the down product) or the bf16 cast (for the up product)
-// sums them in a second pass.
+// stream from HBM. The bf16 kernel streams weight row slices straight into
+// registers in matrix-core operand layout (16 contiguous bytes per lane),
+// splits K across workgroups when the output alone cannot fill the chip,
+// and leaves fp32 partials that the RMSNorm pass sums (down product) or
+// writes bf16 directly (up product, one K slice).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace mfa {
 
-namespace {
-constexpr int kKC = 256;                 // K per LDS stage (8 k-steps of 32)
-constexpr int kRow = kKC * 2 + 16;       // padded LDS row: conflict-free 16-lane reads
-}
-
-template <int MT>   // M tiles of 16 rows
-__global__ __launch_bounds__(256) void gemm_bf16_splitk_kernel(const uint16_t* __restrict__ A,
-                                                               const uint16_t* __restrict__ W,
-                                                               float* __restrict__ part, int M,
-                                                               int N, int K, int kchunk) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[MT * 16 * kRow];
+// Skinny bf16 product on the matrix cores: part[ks][m][n] = sum over the K
+// slice ks of A[m][k] * W[n][k] for m < M <= 64.
+//
+// A workgroup owns NT*16 output columns and one K slice; its four waves take
+// interleaved 32-wide k-steps of that slice, so every wave streams distinct
+// weight bytes. Per k-step a wave loads NT weight fragments (lane: 16
+// contiguous bytes of one weight row) and MT activation fragments (lane: 16
+// bytes of one activation row; the activations are small and stay in L2),
+// keeping PD k-steps of loads in flight. The four waves' accumulators are
+// summed through LDS at the end; the sum is written as fp32 partials, or as
+// bf16 directly when the product has a single K slice.
+template <int MT, int NT, int PD>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ W,
+                                                          float* __restrict__ part,
+                                                          uint16_t* __restrict__ out_bf16, int M,
+                                                          int N, int K, int kchunk) {
+  constexpr int TM = MT * 16, TN = NT * 16;
+  constexpr int kPad = TN + 4;                       // padded LDS row (floats)
+  __shared__ __attribute__((aligned(16))) float red[4][TM * kPad];
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int n0 = blockIdx.x * 64 + w * 16;
+  const int n0 = blockIdx.x * TN;
   const int ks = blockIdx.y;
-  const int kbeg = ks * kchunk, kend = kbeg + kchunk;
+  const int kbeg = ks * kchunk;
+  const int nsteps = kchunk / 32;                    // k-steps in the slice
+  const int mine = (nsteps - w + 3) / 4;             // k-steps of this wave: w, w+4, ...
 
-  f32x4_t acc[MT];
+  const uint16_t* wp[NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // B operand: lane holds W[n0 + c][k + 8g .. +8]
-  const uint16_t* wrow = W + static_cast<size_t>(n0 + c) * K + g * 8;
-  uint4 wcur[8], wnxt[8];
+  for (int nt = 0; nt < NT; ++nt) wp[nt] = W + static_cast<size_t>(n0 + nt * 16 + c) * K + kbeg + g * 8;
+  const uint16_t* ap[MT];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) wcur[s] = *reinterpret_cast<const uint4*>(wrow + kbeg + s * 32);
-
-  for (int k0 = kbeg; k0 < kend; k0 += kKC) {
-    if (k0 + kKC < kend) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        wnxt[s] = *reinterpret_cast<const uint4*>(wrow + k0 + kKC + s * 32);
-    }
-    // A panel rows [0, MT*16) x [k0, k0+256): 32 pieces of 16 B per row
-#pragma unroll
-    for (int r = 0; r < MT * 2; ++r) {
-      const int idx = tid + 256 * r;
-      const int m = idx >> 5, piece = idx & 31;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M) v = *reinterpret_cast<const uint4*>(A + static_cast<size_t>(m) * K + k0 + piece * 8);
-      *reinterpret_cast<uint4*>(a_lds + m * kRow + piece * 16) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8_t bop = as_bf16x8(wcur[s]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint4 av = *reinterpret_cast<const uint4*>(a_lds + (mt * 16 + c) * kRow + (s * 32 + g * 8) * 2);
-        acc[mt] = mfma_16x16x32(as_bf16x8(av), bop, acc[mt]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) wcur[s] = wnxt[s];
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + c, M - 1);           // rows >= M feed only rows >= M of C
+    ap[mt] = A + static_cast<size_t>(m) * K + kbeg + g * 8;
   }
-  // accumulator lane holds C[mt*16 + 4g + i][n0 + c]
+
+  f32x4_t acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * g + i;
-      if (m < M) part[(static_cast<size_t>(ks) * M + m) * N + n0 + c] = acc[mt][i];
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wb[PD][NT], ab[PD][MT];
+  auto issue = [&](int slot, int j) {                // j-th k-step of this wave
+    const int koff = (w + 4 * j) * 32;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wb[slot][nt] = *reinterpret_cast<const uint4*>(wp[nt] + koff);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + koff);
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < mine) issue(p, p);
+  for (int j0 = 0; j0 < mine; j0 += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int j = j0 + p;
+      if (j < mine) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt][nt] = mfma_16x16x32(as_bf16x8(ab[p][mt]), as_bf16x8(wb[p][nt]), acc[mt][nt]);
+        if (j + PD < mine) issue(p, j + PD);
+      }
     }
+  }
+
+  // accumulator lane holds C[mt*16 + 4g + i][nt*16 + c]; sum the four waves
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w][(mt * 16 + 4 * g + i) * kPad + nt * 16 + c] = acc[mt][nt][i];
+  __syncthreads();
+  constexpr int kPer = TM * TN / 256;                // outputs per thread (contiguous in n)
+  const int e0 = tid * kPer;
+  const int m = e0 / TN, nl = e0 % TN;
+  if (m < M) {
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = m * kPad + nl + j;
+      v[j] = (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
+    }
+    if (out_bf16) {
+      uint16_t* dst = out_bf16 + static_cast<size_t>(m) * N + n0 + nl;
+#pragma unroll
+      for (int j = 0; j < kPer; j += 2) *reinterpret_cast<uint32_t*>(dst + j) = pack_bf16x2(v[j], v[j + 1]);
+    } else {
+      float* dst = part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl;
+#pragma unroll
+      for (int j = 0; j < kPer; j += 4)
+        *reinterpret_cast<float4*>(dst + j) = make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+    }
+  }
 }
 
+// c[m][:] = sum of the K-slice partials; n = c / sqrt(mean(c^2) + eps) * g.
+// One workgroup per row; each thread owns 8 consecutive columns per 2048.
 __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __restrict__ part,
                                                              int ksplit, const float* __restrict__ g,
                                                              int M, int R, float eps, void* out,
                                                              int out_f32) {
-  constexpr int kMaxPer = 32;          // R <= 8192
+  constexpr int kMaxChunks = 4;        // R <= 8192 = 4 chunks of 2048
   __shared__ float wsum[4];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
-  float cv[kMaxPer];
+  float cv[kMaxChunks][8];
   float ss = 0.f;
 #pragma unroll
-  for (int r = 0; r < kMaxPer; ++r) {
-    const int j = tid + 256 * r;
-    float cj = 0.f;
-    if (j < R) {
-      for (int ks = 0; ks < ksplit; ++ks) cj += part[(static_cast<size_t>(ks) * M + m) * R + j];
+  for (int ch = 0; ch < kMaxChunks; ++ch) {
+    const int j0 = ch * 2048 + tid * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cv[ch][j] = 0.f;
+    if (j0 < R) {
+      for (int ks = 0; ks < ksplit; ++ks) {
+        const float* p = part + (static_cast<size_t>(ks) * M + m) * R + j0;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        cv[ch][0] += a.x; cv[ch][1] += a.y; cv[ch][2] += a.z; cv[ch][3] += a.w;
+        cv[ch][4] += b.x; cv[ch][5] += b.y; cv[ch][6] += b.z; cv[ch][7] += b.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(cv[ch][j], cv[ch][j], ss);
     }
-    cv[r] = cj;
-    ss = fmaf(cj, cj, ss);
   }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
@@ -111,13 +154,25 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
   const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(R) + eps);
 #pragma unroll
-  for (int r = 0; r < kMaxPer; ++r) {
-    const int j = tid + 256 * r;
-    if (j < R) {
-      const float v = cv[r] * inv * g[j];
-      const size_t o = static_cast<size_t>(m) * R + j;
-      if (out_f32) reinterpret_cast<float*>(out)[o] = v;
-      else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(v);
+  for (int ch = 0; ch < kMaxChunks; ++ch) {
+    const int j0 = ch * 2048 + tid * 8;
+    if (j0 < R) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = cv[ch][j] * inv * g[j0 + j];
+      const size_t o = static_cast<size_t>(m) * R + j0;
+      if (out_f32) {
+        float* d = reinterpret_cast<float*>(out) + o;
+        *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        uint4 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        pk.z = pack_bf16x2(v[4], v[5]);
+        pk.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + o) = pk;
+      }
     }
   }
 }
@@ -150,16 +205,27 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
   if (lane == 0) out[static_cast<size_t>(m) * N + n] = acc;
 }
 
-hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* W, float* part, int M,
-                                   int N, int K, int ksplit, hipStream_t stream) {
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
+                            int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
   const int kchunk = K / ksplit;
-  dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit)), block(256);
-  if (M <= 16)
-    hipLaunchKernelGGL(gemm_bf16_splitk_kernel<1>, grid, block, 0, stream, A, W, part, M, N, K, kchunk);
-  else if (M <= 32)
-    hipLaunchKernelGGL(gemm_bf16_splitk_kernel<2>, grid, block, 0, stream, A, W, part, M, N, K, kchunk);
-  else
-    hipLaunchKernelGGL(gemm_bf16_splitk_kernel<4>, grid, block, 0, stream, A, W, part, M, N, K, kchunk);
+  dim3 block(256);
+  if (ntiles == 4) {
+    dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+    else if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 2>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+  } else {
+    dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, 8>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+    else if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 6>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, 2, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+  }
   return hipGetLastError();
 }
 

@@ -41,19 +41,33 @@
  * KV cache layout (owned by the caller, written only by mfa_kv_append)
  * ---------------------------------------------------------------------
  * The cache of one layer holds one K head and one V head of width d. It is
- * stored in blocks of MFA_BLOCK_TOKENS consecutive logical tokens of one
- * sequence:
- *   k       [num_blocks][64][d]   token-major blocks
- *   v       [num_blocks][d][64]   dim-major (transposed) blocks
+ * stored in blocks of MFA_BLOCK_TOKENS = 64 consecutive logical tokens of
+ * one sequence; every block of k and of v is 64*d elements:
+ *   k       [num_blocks][64*d]    elements of dtype, order below
+ *   v       [num_blocks][64*d]    elements of dtype, order below
  *   k_scale [num_blocks][64]      fp32, FP8 caches only (else NULL)
  *   v_scale [num_blocks][64]      fp32, FP8 caches only (else NULL)
  * Logical token t of sequence b is in logical block t/64 at offset t%64. The
  * block table [B][max_blocks_per_seq] (int32, device) maps logical block j of
  * sequence b to a physical block id. Without a block table (NULL) the cache
  * is contiguous: logical block j of sequence b is physical block
- * b*max_blocks_per_seq + j. The V blocks are transposed so that, for a fixed
- * feature, 64 consecutive tokens are contiguous: that is the contraction
- * order of p.V on the matrix cores.
+ * b*max_blocks_per_seq + j.
+ *
+ * Element order inside a block (t = token in block, f = feature < d). BF16
+ * and FP8 blocks are stored in the order the matrix-core operands consume
+ * them, as units of 64 lanes x 16 bytes (1 KB), so that every wave-wide
+ * 16-byte load of the attention kernel reads contiguous memory:
+ *   BF16 K: unit u = (t/16)*(d/32) + f/32; lane = 16*((f%32)/8) + t%16;
+ *           element (t, f) at ((u*64 + lane)*8 + f%8)
+ *   BF16 V: unit u = (f/16)*2 + t/32; lane = 16*((t%32)/8) + f%16;
+ *           element (t, f) at ((u*64 + lane)*8 + t%8)
+ *   FP8 K:  unit u = (t/16)*(d/64) + f/64; lane = 16*((f%64)/16) + t%16;
+ *           element (t, f) at ((u*64 + lane)*16 + f%16)
+ *   FP8 V:  unit u = f/16; lane = 16*(t/16) + f%16;
+ *           element (t, f) at ((u*64 + lane)*16 + t%16)
+ *   F32 K:  element (t, f) at (t*d + f)      (token-major rows)
+ *   F32 V:  element (t, f) at (f*64 + t)     (feature-major rows)
+ * (positions in elements from the start of the block).
  *
  * FP8 caches hold OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3
  * mantissa bits, max 448, no infinities) with one fp32 scale per token for K
@@ -101,7 +115,7 @@ typedef struct {
   const int32_t *block_table;   /* device: [B][max_blocks_per_seq] or NULL   */
   int32_t num_blocks;           /* physical blocks in k / v                  */
   int32_t max_blocks_per_seq;   /* table row length; capacity = 64x this     */
-  int32_t head_dim;             /* d                                         */
+  int32_t head_dim;             /* d: 64, 128 or 256                         */
   int32_t dtype;                /* mfa_dtype of k and v                      */
 } mfa_kv_cache;
 
@@ -126,7 +140,8 @@ const char *mfa_status_str(int status);
  *          (fp32 split-K partials and the normalised latent n).
  * dtype: MFA_BF16 (c kept in fp32; n and q rounded to bf16) or MFA_F32 (all
  * fp32). Limits: 1 <= B <= 256, q_rank <= 8192; bf16: hidden and q_rank
- * multiples of 256, H*d a multiple of 64; fp32: multiples of 4.
+ * multiples of 256, H*d a multiple of 64; fp32: hidden and H*d multiples of 4,
+ * q_rank a multiple of 8.
  */
 size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, int dtype);
 mfa_status mfa_qproj(const void *x, const void *w_qdown, const float *q_norm_w,
@@ -200,6 +215,7 @@ mfa_status mfa_decode_attn(const void *q, int q_dtype, int B, int H,
  *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.
  * Splits with l_j == 0 (empty) get weight 0; a head whose splits are all
  * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32).
+ * num_splits >= 2; d in {64, 128, 256}.
  */
 mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
                        int H, int d, int num_splits, void *out, int out_dtype,

@@ -1,16 +1,25 @@
-"""The physical KV-cache layout that the MFA library documents, written out.
+"""The physical KV-cache block layout that the MFA library documents, written
+out with numpy reshapes.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``). Used to check the
 library's KV append bit for bit. The layout is the library's contract (its C
 header states it); this module restates it from that statement:
 
-* a cache block holds 64 consecutive logical tokens of one sequence;
-* K blocks are token-major: element (block, token-in-block, dim);
-* V blocks are dim-major (transposed): element (block, dim, token-in-block);
-* FP8 caches keep one fp32 scale per token for K and for V:
-  (block, token-in-block);
-* without a block table, logical block j of sequence b is physical block
-  b * max_blocks_per_seq + j.
+* a cache block holds 64 consecutive logical tokens of one sequence; without
+  a block table, logical block j of sequence b is physical block
+  b * max_blocks_per_seq + j; FP8 caches keep one fp32 scale per token for K
+  and for V, indexed (block, token-in-block);
+* fp32 blocks: K is token-major [64][d], V is feature-major [d][64];
+* bf16 blocks are cut into 1 KB units of 64 lanes x 16 bytes:
+  K: units ordered (token group t//16, dim group d//32); in a unit, lane
+     (16*((d%32)//8) + t%16) holds the 8 values K[t][8*(d//8) .. +8];
+  V: units ordered (feature group f//16, token half t//32); in a unit, lane
+     (16*((t%32)//8) + f%16) holds the 8 values V[8*(t//8) .. +8][f];
+* FP8 blocks, same idea with 16 one-byte codes per lane:
+  K: units ordered (token group t//16, dim group d//64); lane
+     (16*((d%64)//16) + t%16) holds K[t][16*(d//16) .. +16];
+  V: units ordered (feature group f//16); lane (16*(t//16) + f%16) holds
+     V[16*(t//16) .. +16][f].
 """
 from __future__ import annotations
 
@@ -19,17 +28,64 @@ import numpy as np
 BLOCK_TOKENS = 64
 
 
-def k_blocks(token_rows: np.ndarray) -> np.ndarray:
-    """Token-major rows [num_blocks*64][d] -> K block array [num_blocks][64][d]."""
-    nb = token_rows.shape[0] // BLOCK_TOKENS
-    return token_rows.reshape(nb, BLOCK_TOKENS, token_rows.shape[1])
+def _split(rows: np.ndarray) -> np.ndarray:
+    nb = rows.shape[0] // BLOCK_TOKENS
+    return rows.reshape(nb, BLOCK_TOKENS, rows.shape[1])
 
 
-def v_blocks(token_rows: np.ndarray) -> np.ndarray:
-    """Token-major rows [num_blocks*64][d] -> V block array [num_blocks][d][64]."""
-    nb = token_rows.shape[0] // BLOCK_TOKENS
-    return np.ascontiguousarray(
-        token_rows.reshape(nb, BLOCK_TOKENS, token_rows.shape[1]).transpose(0, 2, 1))
+def k_blocks(token_rows: np.ndarray, dtype: str) -> np.ndarray:
+    """Token-major rows [num_blocks*64][d] of stored values -> K blocks,
+    flattened per block in storage order: [num_blocks][64*d]."""
+    x = _split(token_rows)
+    nb, _, d = x.shape
+    if dtype == "f32":
+        return x.reshape(nb, -1)
+    if dtype == "bf16":
+        # t = (tg, c); d = (s, g, j)  ->  order (tg, s, g, c, j)
+        y = x.reshape(nb, 4, 16, d // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5)
+        return np.ascontiguousarray(y).reshape(nb, -1)
+    if dtype == "fp8":
+        # t = (tg, c); d = (u, g, j)  ->  order (tg, u, g, c, j)
+        y = x.reshape(nb, 4, 16, d // 64, 4, 16).transpose(0, 1, 3, 4, 2, 5)
+        return np.ascontiguousarray(y).reshape(nb, -1)
+    raise ValueError(dtype)
+
+
+def v_blocks(token_rows: np.ndarray, dtype: str) -> np.ndarray:
+    """Token-major rows [num_blocks*64][d] -> V blocks [num_blocks][64*d]."""
+    x = _split(token_rows)
+    nb, _, d = x.shape
+    if dtype == "f32":
+        return np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(nb, -1)
+    if dtype == "bf16":
+        # t = (s2, g, j); f = (fg, c)  ->  order (fg, s2, g, c, j)
+        y = x.reshape(nb, 2, 4, 8, d // 16, 16).transpose(0, 4, 1, 2, 5, 3)
+        return np.ascontiguousarray(y).reshape(nb, -1)
+    if dtype == "fp8":
+        # t = (g, j); f = (fg, c)  ->  order (fg, g, c, j)
+        y = x.reshape(nb, 4, 16, d // 16, 16).transpose(0, 3, 1, 4, 2)
+        return np.ascontiguousarray(y).reshape(nb, -1)
+    raise ValueError(dtype)
+
+
+def _inverse(fwd, blocks: np.ndarray, d: int, dtype: str) -> np.ndarray:
+    """Undo a forward layout by pushing token/dim indices through it."""
+    nb = blocks.shape[0]
+    idx = np.arange(BLOCK_TOKENS * d, dtype=np.int64).reshape(BLOCK_TOKENS, d)
+    pos = fwd(idx, dtype)[0]                     # pos[k] = flat (t*d + dd) stored at k
+    rows = np.empty((nb, BLOCK_TOKENS * d), dtype=blocks.dtype)
+    rows[:, pos] = blocks.reshape(nb, -1)
+    return rows.reshape(nb * BLOCK_TOKENS, d)
+
+
+def k_rows_from_blocks(blocks: np.ndarray, d: int, dtype: str) -> np.ndarray:
+    """Storage-order K blocks [num_blocks][64*d] -> token-major rows."""
+    return _inverse(k_blocks, blocks, d, dtype)
+
+
+def v_rows_from_blocks(blocks: np.ndarray, d: int, dtype: str) -> np.ndarray:
+    """Storage-order V blocks [num_blocks][64*d] -> token-major rows."""
+    return _inverse(v_blocks, blocks, d, dtype)
 
 
 def scale_blocks(token_scales: np.ndarray) -> np.ndarray:

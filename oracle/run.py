@@ -14,7 +14,7 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-from . import layout, mfa
+from . import mfa
 
 DEFAULT_EPS = 1e-6
 
@@ -83,10 +83,12 @@ def decode_step(inp: Dict, seqs: Optional[Sequence[int]] = None,
     return {"q": q, "o": o, "seqs": list(seqs)}
 
 
-def expected_cache_bytes(inp: Dict, seqs: Sequence[int]):
-    """Stored K/V (and FP8 scales) of the given sequences after the append, in
-    the library's documented block layout. Returns a dict of arrays indexed by
-    physical block, and the list of blocks the sequences own."""
+def expected_cache_rows(inp: Dict, seqs: Sequence[int]):
+    """Stored K/V values (bf16 bits, e4m3 codes or fp32) and FP8 scales of the
+    given sequences after the append, as token-major physical rows
+    [num_blocks*64][d] (rows of other sequences are zero), plus the physical
+    rows each sequence owns. ``oracle.layout`` turns rows into the library's
+    block storage order and back."""
     w = inp["workload"]
     nrows = inp["num_blocks"] * mfa.BLOCK_TOKENS
     d = w.head_dim
@@ -95,11 +97,11 @@ def expected_cache_bytes(inp: Dict, seqs: Sequence[int]):
     vrows = np.zeros((nrows, d), dtype=store)
     ks = np.zeros(nrows, dtype=np.float32)
     vs = np.zeros(nrows, dtype=np.float32)
-    owned = []
+    owned = {}
     for b in seqs:
         L = int(inp["seq_lens"][b])
         rows = mfa.physical_rows(b, L, inp["block_table"], inp["max_blocks_per_seq"])
-        owned.extend(sorted(set((rows // mfa.BLOCK_TOKENS).tolist())))
+        owned[b] = rows
         k, v = sequence_tokens(inp, b)
         if w.kv_dtype == "fp8":
             _, _, (kcodes, kscale, vcodes, vscale) = sequence_kv_f64(inp, b)
@@ -107,8 +109,8 @@ def expected_cache_bytes(inp: Dict, seqs: Sequence[int]):
             ks[rows], vs[rows] = kscale, vscale
         else:
             krows[rows], vrows[rows] = k, v
-    res = {"k": layout.k_blocks(krows), "v": layout.v_blocks(vrows)}
+    res = {"k": krows, "v": vrows}
     if w.kv_dtype == "fp8":
-        res["k_scale"] = layout.scale_blocks(ks)
-        res["v_scale"] = layout.scale_blocks(vs)
+        res["k_scale"] = ks
+        res["v_scale"] = vs
     return res, owned

@@ -65,3 +65,21 @@ def run(T, step):
         out = step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=q)
     torch.cuda.synchronize()
     return q, out
+
+
+def cache_rows(cache):
+    """Stored K and V of a GPU cache as token-major rows [num_blocks*64][d]
+    (bf16 as uint16 bits, FP8 as uint8 codes, fp32 as float32), undoing the
+    library's block storage order with the oracle's restatement of it."""
+    from oracle import layout
+    dt = cache.dtype
+    d = cache.head_dim
+
+    def raw(t):
+        t = t.detach().cpu()
+        if dt == "bf16":
+            return t.view(torch.int16).numpy().view(np.uint16).reshape(t.shape[0], -1)
+        return t.numpy().reshape(t.shape[0], -1)
+    k = layout.k_rows_from_blocks(raw(cache.k), d, dt)
+    v = layout.v_rows_from_blocks(raw(cache.v), d, dt)
+    return k, v

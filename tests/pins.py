@@ -24,6 +24,8 @@ What pins what:
 * quantisation -- the amax element encodes to +-448; error within half an
   e4m3 step times the scale; zero rows; sign kept.
 * cost -- the page's intensity 128 at 8-bit KV and effective rank 16,384.
+* block layout -- hand-worked element positions of the documented storage
+  order, a bijection, and the inverse undoing the forward map.
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def real_oracle():
-    from oracle import brute, cost, e4m3, mfa
+    from oracle import brute, cost, e4m3, layout, mfa
     return types.SimpleNamespace(
         softmax_attention=mfa.softmax_attention,
         physical_rows=mfa.physical_rows,
@@ -55,6 +57,10 @@ def real_oracle():
         arithmetic_intensity=cost.arithmetic_intensity,
         effective_rank=cost.effective_rank,
         kv_bytes_per_token=cost.kv_bytes_per_token,
+        k_blocks=layout.k_blocks,
+        v_blocks=layout.v_blocks,
+        k_rows_from_blocks=layout.k_rows_from_blocks,
+        v_rows_from_blocks=layout.v_rows_from_blocks,
         brute=brute,
     )
 
@@ -322,8 +328,48 @@ def check_cost(O):
     return fails
 
 
+# Element positions inside one 64-token block with d = 256, worked by hand
+# from the documented order: (kind, dtype, token, dim) -> flat element index.
+LAYOUT_EXAMPLES = [
+    # bf16 K: unit (17//16)*8 + 42//32 = 9, lane 16*((42%32)//8) + 17%16 = 17, j 2
+    ("k", "bf16", 17, 42, (9 * 64 + 17) * 8 + 2),
+    # bf16 V: unit (200//16)*2 + 37//32 = 25, lane 16*((37%32)//8) + 200%16 = 8, j 5
+    ("v", "bf16", 37, 200, (25 * 64 + 8) * 8 + 5),
+    # fp8 K: unit (17//16)*4 + 42//64 = 4, lane 16*((42%64)//16) + 1 = 33, j 10
+    ("k", "fp8", 17, 42, (4 * 64 + 33) * 16 + 10),
+    # fp8 V: unit 200//16 = 12, lane 16*(37//16) + 8 = 40, j 5
+    ("v", "fp8", 37, 200, (12 * 64 + 40) * 16 + 5),
+    ("k", "f32", 17, 42, 17 * 256 + 42),
+    ("v", "f32", 37, 200, 200 * 64 + 37),
+    ("k", "bf16", 63, 255, (31 * 64 + 63) * 8 + 7),
+    ("v", "bf16", 0, 0, 0),
+]
+
+
+def check_layout(O):
+    fails = []
+    d = 256
+    ids = (np.arange(64)[:, None] * d + np.arange(d)[None, :]).astype(np.int64)
+    rows2 = np.concatenate([ids, ids + 64 * d])          # two blocks
+    for kind, dt, t, dim, pos in LAYOUT_EXAMPLES:
+        fwd = O.k_blocks if kind == "k" else O.v_blocks
+        blk = fwd(ids, dt)[0]
+        if blk[pos] != t * d + dim:
+            fails.append(f"{kind}/{dt}: element ({t},{dim}) not at {pos}")
+    for dt in ("f32", "bf16", "fp8"):
+        for kind in ("k", "v"):
+            fwd = O.k_blocks if kind == "k" else O.v_blocks
+            inv = O.k_rows_from_blocks if kind == "k" else O.v_rows_from_blocks
+            blk = fwd(rows2, dt)
+            if sorted(blk[0].tolist()) != list(range(64 * d)):
+                fails.append(f"{kind}/{dt}: not a permutation")
+            if not np.array_equal(inv(blk, d, dt), rows2):
+                fails.append(f"{kind}/{dt}: inverse does not undo the layout")
+    return fails
+
+
 ALL_CHECKS = (check_attention, check_gather, check_combine, check_qproj, check_e4m3,
-              check_quantize, check_cost)
+              check_quantize, check_cost, check_layout)
 
 
 def run_all(O):

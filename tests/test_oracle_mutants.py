@@ -113,6 +113,14 @@ def _ai_qk_only(H, d, b, sb=0):
     return 2 * H * d / (2 * d * b + 2 * sb)
 
 
+def _k_blocks_gc_swapped(rows, dt):
+    from oracle import layout
+    if dt != "bf16":
+        return layout.k_blocks(rows, dt)
+    x = rows.reshape(-1, 4, 16, rows.shape[1] // 32, 4, 8).transpose(0, 1, 3, 2, 4, 5)
+    return np.ascontiguousarray(x).reshape(x.shape[0], -1)
+
+
 MUTANTS = {
     "attention_missing_scale": dict(softmax_attention=_attn_no_scale),
     "attention_softmax_over_heads": dict(softmax_attention=_attn_heads_axis),
@@ -130,6 +138,7 @@ MUTANTS = {
     "e4m3_truncates": dict(e4m3_encode=_encode_truncate),
     "quant_wrong_max": dict(quantize_tokens=_quant_wrong_max),
     "cost_counts_qk_only": dict(arithmetic_intensity=_ai_qk_only),
+    "layout_lane_order_swapped": dict(k_blocks=_k_blocks_gc_swapped),
 }
 
 

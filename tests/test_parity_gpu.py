@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import (MAX_ABS_BF16, REL_L2_BF16, REL_L2_F32, max_abs, rel_l2, run, say, setup,
-                      to_np)
+from gpu_util import (MAX_ABS_BF16, REL_L2_BF16, REL_L2_F32, cache_rows, max_abs, rel_l2, run,
+                      say, setup, to_np)
 from oracle import mfa as omfa
 from oracle import run as orun
 
@@ -161,19 +161,16 @@ def test_append_bit_exact(gpu_lib, base, over, lens):
     say(f"append bit-exact base={base} {over} {lens}")
     T, cache, step = setup(inp, num_splits=1)
     run(T, step)
-    exp, _ = orun.expected_cache_bytes(inp, range(len(lens)))
-    raw = {"f32": lambda t: t.cpu().numpy(), "bf16": lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16),
-           "fp8": lambda t: t.cpu().numpy()}[w.kv_dtype]
-    kg, vg = raw(cache.k), raw(cache.v)
-    for b, L in enumerate(inp["seq_lens"]):
-        rows = omfa.physical_rows(b, int(L), inp["block_table"], inp["max_blocks_per_seq"])
-        blk, off = rows // 64, rows % 64
-        assert np.array_equal(kg[blk, off].view(np.uint8), exp["k"][blk, off].view(np.uint8)), b
-        assert np.array_equal(vg[blk, :, off].view(np.uint8), exp["v"][blk, :, off].view(np.uint8)), b
+    exp, owned = orun.expected_cache_rows(inp, range(len(lens)))
+    kg, vg = cache_rows(cache)
+    for b, rows in owned.items():
+        assert np.array_equal(kg[rows].view(np.uint8), exp["k"][rows].view(np.uint8)), b
+        assert np.array_equal(vg[rows].view(np.uint8), exp["v"][rows].view(np.uint8)), b
         if w.kv_dtype == "fp8":
-            ks, vs = cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()
-            assert np.array_equal(ks[blk, off].view(np.uint32), exp["k_scale"][blk, off].view(np.uint32))
-            assert np.array_equal(vs[blk, off].view(np.uint32), exp["v_scale"][blk, off].view(np.uint32))
+            ks = cache.k_scale.cpu().numpy().reshape(-1)
+            vs = cache.v_scale.cpu().numpy().reshape(-1)
+            assert np.array_equal(ks[rows].view(np.uint32), exp["k_scale"][rows].view(np.uint32))
+            assert np.array_equal(vs[rows].view(np.uint32), exp["v_scale"][rows].view(np.uint32))
 
 
 def test_fp8_codec_bit_exact_random_scales(gpu_lib):
@@ -194,10 +191,9 @@ def test_fp8_codec_bit_exact_random_scales(gpu_lib):
     say("fp8 codec random")
     mfa.kv_append(cache, t, t, torch.zeros(1, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
-    got = cache.k.cpu().numpy().reshape(n, d)
+    got, gv = cache_rows(cache)
     assert np.array_equal(got, kc)
     assert np.array_equal(cache.k_scale.cpu().numpy().reshape(n).view(np.uint32), ks.view(np.uint32))
-    gv = cache.v.cpu().numpy().transpose(0, 2, 1).reshape(n, d)
     assert np.array_equal(gv, kc)
 
 
@@ -256,14 +252,14 @@ def test_full_fp8_32k_sampled(gpu_lib):
     seqs = [0, 7, 15]
     want = orun.decode_step(inp, seqs=seqs)
     check_bf16(to_np(out)[seqs], want["o"], "fp8 32k sampled")
-    # stored codes of the appended token of each sampled sequence
-    exp, _ = orun.expected_cache_bytes(inp, seqs)
-    kg = cache.k.cpu().numpy()
-    for b in seqs:
-        r = omfa.physical_rows(b, int(inp["seq_lens"][b]), inp["block_table"],
-                               inp["max_blocks_per_seq"])
-        blk, off = r // 64, r % 64
-        assert np.array_equal(kg[blk, off], exp["k"][blk, off])
+    # stored codes and scales of every token of the sampled sequences
+    exp, owned = orun.expected_cache_rows(inp, seqs)
+    kg, vg = cache_rows(cache)
+    ks = cache.k_scale.cpu().numpy().reshape(-1)
+    for b, rows in owned.items():
+        assert np.array_equal(kg[rows], exp["k"][rows])
+        assert np.array_equal(vg[rows], exp["v"][rows])
+        assert np.array_equal(ks[rows].view(np.uint32), exp["k_scale"][rows].view(np.uint32))
 
 
 def test_full_split32_64k(gpu_lib):

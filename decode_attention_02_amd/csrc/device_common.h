@@ -86,6 +86,27 @@ __device__ __forceinline__ uint32_t encode_e4m3_rne(float y) {
   return code | sign;
 }
 
+// Max / sum over the four 16-lane rows of a wave: lane c of every row gets
+// the result for column c (rows are swapped pairwise by the gfx950 permlane
+// swaps, so no LDS round trip is involved).
+__device__ __forceinline__ float rows4_max(float v) {
+  const int iv = __float_as_int(v);
+  auto p = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+  v = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  const int iw = __float_as_int(v);
+  auto q = __builtin_amdgcn_permlane32_swap(iw, iw, false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float v) {
+  const int iv = __float_as_int(v);
+  auto p = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+  v = __int_as_float(p[0]) + __int_as_float(p[1]);
+  const int iw = __float_as_int(v);
+  auto q = __builtin_amdgcn_permlane32_swap(iw, iw, false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));

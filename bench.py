@@ -134,11 +134,16 @@ def main():
                             block_table=T["block_table"], device=dev, zero=False)
         prefill(cache, T["k_ctx"], T["v_ctx"], inp["ctx_offsets"], inp["prefill_lens"])
         ns = args.splits or w.num_splits
+        packed = w.has_qproj and w.act_dtype == "bf16"
         step = DecodeStep(cache, B, w.heads, maxlen, hidden=w.hidden, q_rank=w.q_rank,
-                          act_dtype=act, num_splits=ns, device=dev)
+                          act_dtype=act, num_splits=ns, packed_weights=packed, device=dev)
         wts = None
         if w.has_qproj:
-            wts = (T["w_qdown"].clone(), T["g"].clone(), T["w_qup"].clone())
+            # weights are static: packed once into operand order, like a load step
+            if packed:
+                wts = (mfa.pack_weight(T["w_qdown"]), T["g"].clone(), mfa.pack_weight(T["w_qup"]))
+            else:
+                wts = (T["w_qdown"].clone(), T["g"].clone(), T["w_qup"].clone())
         sets.append((step, wts))
     torch.cuda.synchronize()
 

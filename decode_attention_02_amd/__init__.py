@@ -5,4 +5,4 @@ of ``include/mfa.h``); this package is its thin torch-facing binding.
 """
 from ._lib import BLOCK_TOKENS, MfaError, load  # noqa: F401
 from .api import (KVCache, combine_splits, decode_attn, decode_plan, kv_append,  # noqa: F401
-                  qproj, qproj_workspace_bytes, split_workspace_bytes)
+                  pack_weight, qproj, qproj_workspace_bytes, split_workspace_bytes)

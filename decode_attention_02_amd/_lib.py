@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmfa.so")
 
 MFA_OK = 0
 MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
+MFA_WEIGHTS_ROWMAJOR, MFA_WEIGHTS_PACKED = 0, 1
 BLOCK_TOKENS = 64
 STATUS_NAMES = {0: "MFA_OK", 1: "MFA_ERR_NULL", 2: "MFA_ERR_SHAPE", 3: "MFA_ERR_DTYPE",
                 4: "MFA_ERR_ALIGN", 5: "MFA_ERR_UNSUPPORTED", 6: "MFA_ERR_WORKSPACE",
@@ -43,7 +44,8 @@ SIGNATURES = {
     "mfa_abi_version": (_i, []),
     "mfa_status_str": (ctypes.c_char_p, [_i]),
     "mfa_qproj_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "mfa_qproj": (_i, [_p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "mfa_qproj": (_i, [_p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
+    "mfa_pack_weight": (_i, [_p, _p, _i, _i, _i, _p]),
     "mfa_kv_append": (_i, [_p, _p, _i, _p, _i, _i, _pdesc, _p]),
     "mfa_decode_plan": (_i, [_i, _i, _i, _i, _i, _pi, _pi]),
     "mfa_split_workspace_bytes": (_sz, [_i, _i, _i, _i]),

@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import BLOCK_TOKENS, MFA_BF16, MFA_F32, MFA_FP8_E4M3, check
+from ._lib import (BLOCK_TOKENS, MFA_BF16, MFA_F32, MFA_FP8_E4M3, MFA_WEIGHTS_PACKED,
+                   MFA_WEIGHTS_ROWMAJOR, check)
 
 _DTYPES = {torch.float32: MFA_F32, torch.bfloat16: MFA_BF16}
 
@@ -90,10 +91,25 @@ def qproj_workspace_bytes(batch: int, hidden: int, q_rank: int, heads: int, head
                                              _DTYPES[dtype]))
 
 
+def pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Operand-order packed copy of a bf16 weight [N][K] (mfa_pack_weight).
+    The result keeps the logical shape [N][K]; its element order is the
+    library's."""
+    lib = _lib.load()
+    _dev(w, "w")
+    N, K = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    check("mfa_pack_weight", lib.mfa_pack_weight(_ptr(w), _ptr(out), N, K, _DTYPES[w.dtype],
+                                                 _stream(w.device)))
+    return out
+
+
 def qproj(x: torch.Tensor, w_qdown: torch.Tensor, q_norm_w: torch.Tensor, w_qup: torch.Tensor,
           heads: int, head_dim: int, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """q [B][H][d] = RMSNorm(x W_qdown^T; g, eps) W_qup^T (mfa_qproj)."""
+          workspace: Optional[torch.Tensor] = None, packed: bool = False) -> torch.Tensor:
+    """q [B][H][d] = RMSNorm(x W_qdown^T; g, eps) W_qup^T (mfa_qproj). With
+    ``packed`` both weights come from ``pack_weight``."""
     lib = _lib.load()
     B, hidden = x.shape
     q_rank = w_qdown.shape[0]
@@ -105,9 +121,11 @@ def qproj(x: torch.Tensor, w_qdown: torch.Tensor, q_norm_w: torch.Tensor, w_qup:
     need = int(lib.mfa_qproj_workspace_bytes(B, hidden, q_rank, heads, head_dim, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    layout = MFA_WEIGHTS_PACKED if packed else MFA_WEIGHTS_ROWMAJOR
     check("mfa_qproj", lib.mfa_qproj(_ptr(x), _ptr(w_qdown), _ptr(q_norm_w), _ptr(w_qup),
                                      _ptr(out), _ptr(workspace), workspace.numel(), B, hidden,
-                                     q_rank, heads, head_dim, eps, dt, _stream(x.device)))
+                                     q_rank, heads, head_dim, eps, dt, layout,
+                                     _stream(x.device)))
     return out
 
 

@@ -25,23 +25,43 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
   const int f = (threadIdx.x % tpb) * 4;
   if (h >= H) return;
   const size_t row0 = static_cast<size_t>(b) * S;
+  // Loads are issued in batches of 8 splits before any is used, so their
+  // latencies overlap (every split's partials are valid memory, empty ones too).
+  constexpr int kBatch = 8;
   float mstar = -INFINITY;
-  for (int s = 0; s < S; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row0 + s) * H + h) * 2);
-    if (ml.y > 0.f) mstar = fmaxf(mstar, ml.x);
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float2 ml[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      ml[j] = s0 + j < S ? *reinterpret_cast<const float2*>(part_ml + ((row0 + s0 + j) * H + h) * 2)
+                         : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (ml[j].y > 0.f) mstar = fmaxf(mstar, ml[j].x);
   }
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((row0 + s) * H + h) * 2);
-    if (ml.y > 0.f) {
-      const float wgt = expf(ml.x - mstar);
-      den = fmaf(wgt, ml.y, den);
-      const float4 o = *reinterpret_cast<const float4*>(part_o + ((row0 + s) * H + h) * d + f);
-      num.x = fmaf(wgt, o.x, num.x);
-      num.y = fmaf(wgt, o.y, num.y);
-      num.z = fmaf(wgt, o.z, num.z);
-      num.w = fmaf(wgt, o.w, num.w);
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float2 ml[kBatch];
+    float4 o[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = s0 + j < S;
+      ml[j] = in ? *reinterpret_cast<const float2*>(part_ml + ((row0 + s0 + j) * H + h) * 2)
+                 : make_float2(-INFINITY, 0.f);
+      o[j] = in ? *reinterpret_cast<const float4*>(part_o + ((row0 + s0 + j) * H + h) * d + f)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ml[j].y > 0.f) {              // empty splits contribute nothing, whatever they hold
+        const float wgt = expf(ml[j].x - mstar);
+        den = fmaf(wgt, ml[j].y, den);
+        num.x = fmaf(wgt, o[j].x, num.x);
+        num.y = fmaf(wgt, o[j].y, num.y);
+        num.z = fmaf(wgt, o[j].z, num.z);
+        num.w = fmaf(wgt, o[j].w, num.w);
+      }
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;

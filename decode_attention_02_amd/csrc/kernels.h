@@ -66,7 +66,10 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // writes bf16 C directly. ntiles (2 or 4) = 16-column tiles per workgroup.
 // Requires N % (16*ntiles) == 0 and (K/ksplit) % 32 == 0.
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
-                            int M, int N, int K, int ksplit, int ntiles, hipStream_t stream);
+                            int M, int N, int K, int ksplit, int ntiles, bool packed,
+                            hipStream_t stream);
+// Row-major bf16 W [N][K] -> operand-order packed weight (N % 16 == 0, K % 32 == 0).
+hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
                                  float eps, void* out, int out_f32, hipStream_t stream);

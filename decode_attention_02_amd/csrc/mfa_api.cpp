@@ -135,12 +135,26 @@ size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, in
   return plan_qproj(B, hidden, q_rank, H * d, dtype).total;
 }
 
+mfa_status mfa_pack_weight(const void* w, void* packed, int N, int K, int dtype, void* stream) {
+  if (!w || !packed) return MFA_ERR_NULL;
+  if (dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  if (N < 16 || K < 32 || N % 16 || K % 32) return MFA_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed)) return MFA_ERR_ALIGN;
+  return from_hip(mfa::launch_pack_weight(static_cast<const uint16_t*>(w),
+                                          static_cast<uint16_t*>(packed), N, K, as_stream(stream)));
+}
+
 mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, const void* w_qup,
                      void* q_out, void* workspace, size_t workspace_bytes, int B, int hidden,
-                     int q_rank, int H, int d, float eps, int dtype, void* stream) {
+                     int q_rank, int H, int d, float eps, int dtype, int weight_layout,
+                     void* stream) {
   if (!x || !w_qdown || !q_norm_w || !w_qup || !q_out) return MFA_ERR_NULL;
   const mfa_status sh = check_qproj_shape(B, hidden, q_rank, H, d, dtype);
   if (sh != MFA_OK) return sh;
+  if (weight_layout != MFA_WEIGHTS_ROWMAJOR && weight_layout != MFA_WEIGHTS_PACKED)
+    return MFA_ERR_SHAPE;
+  if (weight_layout == MFA_WEIGHTS_PACKED && dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  const bool packed = weight_layout == MFA_WEIGHTS_PACKED;
   if (!aligned16(x) || !aligned16(w_qdown) || !aligned16(q_norm_w) || !aligned16(w_qup) ||
       !aligned16(q_out) || (workspace && !aligned16(workspace)))
     return MFA_ERR_ALIGN;
@@ -163,17 +177,18 @@ mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, 
       uint16_t* n = reinterpret_cast<uint16_t*>(ws + p.off_n);
       e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
                                 static_cast<const uint16_t*>(w_qdown), pd, nullptr, M, q_rank,
-                                hidden, p.down.ks, p.down.ntiles, st);
+                                hidden, p.down.ks, p.down.ntiles, packed, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, q_norm_w, M, q_rank, eps, n, 0, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       if (p.up.ks == 1) {
         e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), nullptr,
-                                  reinterpret_cast<uint16_t*>(qo), M, HD, q_rank, 1, p.up.ntiles, st);
+                                  reinterpret_cast<uint16_t*>(qo), M, HD, q_rank, 1, p.up.ntiles,
+                                  packed, st);
       } else {
         float* pu = reinterpret_cast<float*>(ws + p.off_part_up);
         e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), pu, nullptr, M, HD,
-                                  q_rank, p.up.ks, p.up.ntiles, st);
+                                  q_rank, p.up.ks, p.up.ntiles, packed, st);
         if (e != hipSuccess) return MFA_ERR_HIP;
         e = mfa::launch_reduce_cast(pu, p.up.ks, M, HD, qo, 0, st);
       }

@@ -29,7 +29,11 @@ namespace mfa {
 // keeping PD k-steps of loads in flight. The four waves' accumulators are
 // summed through LDS at the end; the sum is written as fp32 partials, or as
 // bf16 directly when the product has a single K slice.
-template <int MT, int NT, int PD>
+// Weights: row-major [N][K] (PACKED = false) or packed in operand order
+// (PACKED = true): 1 KB unit (nt = n/16, kt = k/32) at unit index
+// nt*(K/32) + kt, lane 16*((k%32)/8) + n%16 holding W[n][8*(k/8) .. +8], so
+// that each wave-wide weight load reads 1 KB of contiguous memory.
+template <int MT, int NT, int PD, bool PACKED>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W,
                                                           float* __restrict__ part,
@@ -47,8 +51,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
   const int mine = (nsteps - w + 3) / 4;             // k-steps of this wave: w, w+4, ...
 
   const uint16_t* wp[NT];
+  const int ksteps = K / 32;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wp[nt] = W + static_cast<size_t>(n0 + nt * 16 + c) * K + kbeg + g * 8;
+  for (int nt = 0; nt < NT; ++nt) {
+    if constexpr (PACKED)
+      wp[nt] = W + (static_cast<size_t>((n0 / 16 + nt) * ksteps + kbeg / 32) * 64 + lane) * 8;
+    else
+      wp[nt] = W + static_cast<size_t>(n0 + nt * 16 + c) * K + kbeg + g * 8;
+  }
   const uint16_t* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -66,7 +76,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
   auto issue = [&](int slot, int j) {                // j-th k-step of this wave
     const int koff = (w + 4 * j) * 32;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wb[slot][nt] = *reinterpret_cast<const uint4*>(wp[nt] + koff);
+    for (int nt = 0; nt < NT; ++nt)
+      wb[slot][nt] = *reinterpret_cast<const uint4*>(wp[nt] + (PACKED ? koff * 16 : koff));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + koff);
   };
@@ -205,27 +216,58 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
   if (lane == 0) out[static_cast<size_t>(m) * N + n] = acc;
 }
 
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
-                            int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
+template <bool PACKED>
+static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
+                                int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
   const int kchunk = K / ksplit;
   dim3 block(256);
   if (ntiles == 4) {
     dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 2>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 2, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
   } else {
     dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, 8>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, 8, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 6>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 6, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, 2, 4>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, 2, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
   }
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
+                            int M, int N, int K, int ksplit, int ntiles, bool packed,
+                            hipStream_t stream) {
+  if (packed) launch_gemm_variant<true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+  else launch_gemm_variant<false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+  return hipGetLastError();
+}
+
+// Pack a row-major bf16 weight [N][K] into operand order (see above); one
+// thread per 16-byte lane slot.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ W,
+                                                          uint16_t* __restrict__ P, int N, int K) {
+  const int ksteps = K / 32;
+  const size_t slots = static_cast<size_t>(N / 16) * ksteps * 64;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < slots; i += static_cast<size_t>(gridDim.x) * 256) {
+    const int lane = static_cast<int>(i & 63);
+    const size_t unit = i >> 6;
+    const int nt = static_cast<int>(unit / ksteps), kt = static_cast<int>(unit % ksteps);
+    const int n = nt * 16 + (lane & 15), k = kt * 32 + (lane >> 4) * 8;
+    *reinterpret_cast<uint4*>(P + i * 8) = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(n) * K + k);
+  }
+}
+
+hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream) {
+  const size_t slots = static_cast<size_t>(N / 16) * (K / 32) * 64;
+  size_t blocks = (slots + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, W, P, N, K);
   return hipGetLastError();
 }
 

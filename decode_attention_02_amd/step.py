@@ -28,13 +28,14 @@ class DecodeStep:
                  act_dtype: torch.dtype = torch.bfloat16, num_splits: Optional[int] = None,
                  chunk_tokens: Optional[int] = None, eps: float = 1e-6,
                  out_dtype: Optional[torch.dtype] = None, sm_scale: Optional[float] = None,
-                 device="cuda"):
+                 packed_weights: bool = False, device="cuda"):
         self.cache = cache
         self.B, self.H, self.d = batch, heads, cache.head_dim
         self.max_seq_len = int(max_seq_len)
         self.hidden, self.q_rank = hidden, q_rank
         self.act_dtype = act_dtype
         self.eps = eps
+        self.packed_weights = packed_weights
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(self.d)
         if num_splits is None:
             num_splits, chunk_tokens = api.decode_plan(batch, heads, self.d, self.max_seq_len,
@@ -59,7 +60,7 @@ class DecodeStep:
     # -- stages ---------------------------------------------------------
     def query(self, x, w_qdown, g, w_qup):
         return api.qproj(x, w_qdown, g, w_qup, self.H, self.d, self.eps, out=self.q,
-                         workspace=self.qproj_ws)
+                         workspace=self.qproj_ws, packed=self.packed_weights)
 
     def append(self, k_new, v_new, pos):
         api.kv_append(self.cache, k_new, v_new, pos)

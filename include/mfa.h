@@ -101,6 +101,11 @@ typedef enum {
 } mfa_status;
 
 typedef enum {
+  MFA_WEIGHTS_ROWMAJOR = 0, /* [out][in] row-major (torch Linear)            */
+  MFA_WEIGHTS_PACKED = 1    /* operand order, made by mfa_pack_weight        */
+} mfa_weight_layout;
+
+typedef enum {
   MFA_F32 = 0,              /* IEEE binary32                                 */
   MFA_BF16 = 1,             /* bfloat16                                      */
   MFA_FP8_E4M3 = 2          /* OCP e4m3 ("e4m3fn"), KV caches only           */
@@ -132,9 +137,11 @@ const char *mfa_status_str(int status);
  *   n = c / sqrt(mean(c^2) + eps) * g
  *   q = n W_qup^T -> q_out[B][H][d]
  * x        [B][hidden]          dtype
- * w_qdown  [q_rank][hidden]     dtype (torch Linear [out][in])
+ * w_qdown  [q_rank][hidden]     dtype (torch Linear [out][in]), or packed
  * q_norm_w [q_rank]             fp32 gain g
- * w_qup    [H*d][q_rank]        dtype
+ * w_qup    [H*d][q_rank]        dtype, or packed
+ * weight_layout: MFA_WEIGHTS_ROWMAJOR, or MFA_WEIGHTS_PACKED (bf16 only: both
+ *          weights packed by mfa_pack_weight)
  * q_out    [B][H][d]            dtype
  * workspace: >= mfa_qproj_workspace_bytes(B, hidden, q_rank, H, d, dtype) bytes
  *          (fp32 split-K partials and the normalised latent n).
@@ -147,7 +154,21 @@ size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, in
 mfa_status mfa_qproj(const void *x, const void *w_qdown, const float *q_norm_w,
                      const void *w_qup, void *q_out, void *workspace,
                      size_t workspace_bytes, int B, int hidden, int q_rank,
-                     int H, int d, float eps, int dtype, void *stream);
+                     int H, int d, float eps, int dtype, int weight_layout,
+                     void *stream);
+
+/*
+ * Weight packing for mfa_qproj (bf16): rewrites a row-major weight w [N][K]
+ * (torch Linear [out][in]) into packed [N*K] in the order the matrix-core
+ * operands read it, so that the query path streams weights in 1 KB
+ * contiguous pieces. The packed weight is cut into 1 KB units of 64 lanes x
+ * 16 bytes; unit (nt = n/16, kt = k/32) is unit number nt*(K/32) + kt, and
+ * in it lane 16*((k%32)/8) + n%16 holds w[n][8*(k/8) .. 8*(k/8)+7].
+ * Pack once (weights are static) and pass MFA_WEIGHTS_PACKED to mfa_qproj.
+ * N % 16 == 0, K % 32 == 0, dtype MFA_BF16. packed must not alias w.
+ */
+mfa_status mfa_pack_weight(const void *w, void *packed, int N, int K, int dtype,
+                           void *stream);
 
 /*
  * KV append (§7 Implementation and Results: attention instances own the KV

@@ -2,7 +2,7 @@
 out with numpy reshapes.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``). Used to check the
-library's KV append bit for bit. The layout is the library's contract (its C
+library's KV append and weight packing bit for bit. The layout is the library's contract (its C
 header states it); this module restates it from that statement:
 
 * a cache block holds 64 consecutive logical tokens of one sequence; without
@@ -91,3 +91,16 @@ def v_rows_from_blocks(blocks: np.ndarray, d: int, dtype: str) -> np.ndarray:
 def scale_blocks(token_scales: np.ndarray) -> np.ndarray:
     """Per-token scales [num_blocks*64] -> [num_blocks][64]."""
     return token_scales.reshape(-1, BLOCK_TOKENS)
+
+
+def pack_weight(w: np.ndarray) -> np.ndarray:
+    """Row-major weight [N][K] -> the library's packed operand order, flat.
+
+    1 KB units (16 rows x 32 columns of bf16) ordered (row group n//16,
+    column group k//32); in a unit, lane 16*((k%32)//8) + n%16 holds the 8
+    values w[n][8*(k//8) .. +8].
+    """
+    N, K = w.shape
+    # n = (nt, c); k = (kt, g, j)  ->  order (nt, kt, g, c, j)
+    y = w.reshape(N // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(y).reshape(-1)

@@ -61,6 +61,7 @@ def real_oracle():
         v_blocks=layout.v_blocks,
         k_rows_from_blocks=layout.k_rows_from_blocks,
         v_rows_from_blocks=layout.v_rows_from_blocks,
+        pack_weight=layout.pack_weight,
         brute=brute,
     )
 
@@ -365,6 +366,15 @@ def check_layout(O):
                 fails.append(f"{kind}/{dt}: not a permutation")
             if not np.array_equal(inv(blk, d, dt), rows2):
                 fails.append(f"{kind}/{dt}: inverse does not undo the layout")
+    # packed weight [32][64]: w[17][42] -> unit 1*2 + 1 = 3, lane 16*1 + 1 = 17, j 2
+    wid = (np.arange(32)[:, None] * 64 + np.arange(64)[None, :]).astype(np.int64)
+    pk = O.pack_weight(wid)
+    if pk[(3 * 64 + 17) * 8 + 2] != 17 * 64 + 42:
+        fails.append("packed weight: element (17,42) misplaced")
+    if pk[(0 * 64 + 16 * 3 + 15) * 8 + 7] != 15 * 64 + 31:
+        fails.append("packed weight: element (15,31) misplaced")
+    if sorted(pk.tolist()) != list(range(32 * 64)):
+        fails.append("packed weight: not a permutation")
     return fails
 
 

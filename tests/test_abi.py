@@ -105,7 +105,8 @@ def test_kv_append_validation(lib):
 def test_qproj_validation_and_workspace(lib):
     q = lambda **kw: lib.mfa_qproj(kw.get("x", P), P, P, P, P, kw.get("ws", P),
                                    kw.get("wsb", 1 << 30), kw.get("B", 32), kw.get("hid", 7168),
-                                   kw.get("r", 2048), 64, 256, 1e-6, kw.get("dt", BF16), None)
+                                   kw.get("r", 2048), 64, 256, 1e-6, kw.get("dt", BF16),
+                                   kw.get("lay", 0), None)
     assert q(x=None) == NULL
     assert q(x=PM) == ALIGN
     assert q(B=0) == SHAPE
@@ -113,11 +114,21 @@ def test_qproj_validation_and_workspace(lib):
     assert q(hid=7000) == SHAPE
     assert q(dt=FP8) == DTYPE
     assert q(ws=None) == WS
+    assert q(lay=2) == SHAPE                                     # unknown weight layout
+    assert q(lay=1, dt=F32, hid=256, r=128) == DTYPE             # packed weights are bf16 only
     need = lib.mfa_qproj_workspace_bytes(32, 7168, 2048, 64, 256, BF16)
     assert need > 0
     assert q(wsb=need - 1) == WS
     assert lib.mfa_qproj_workspace_bytes(32, 7000, 2048, 64, 256, BF16) == 0
     assert lib.mfa_qproj_workspace_bytes(2, 256, 128, 4, 64, F32) > 0
+
+
+def test_pack_weight_validation(lib):
+    assert lib.mfa_pack_weight(None, P, 64, 64, BF16, None) == NULL
+    assert lib.mfa_pack_weight(P, P, 64, 64, F32, None) == DTYPE
+    assert lib.mfa_pack_weight(P, P, 60, 64, BF16, None) == SHAPE
+    assert lib.mfa_pack_weight(P, P, 64, 48, BF16, None) == SHAPE
+    assert lib.mfa_pack_weight(PM, P, 64, 64, BF16, None) == ALIGN
 
 
 def test_plan_and_split_workspace(lib):

@@ -210,6 +210,36 @@ def test_qproj_small_bf16(gpu_lib):
     check_bf16(to_np(q), orun.query(inp), "qproj small")
 
 
+def test_pack_weight_bit_exact(gpu_lib):
+    """mfa_pack_weight puts every bf16 weight where the documented packed
+    order says (checked against the oracle's restatement of that order)."""
+    import decode_attention_02_amd as mfa
+    from oracle import layout
+    rng = np.random.default_rng(12)
+    w = workloads.f32_to_bf16_bits(rng.standard_normal((96, 320)).astype(np.float32))
+    t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    say("pack weight")
+    pk = mfa.pack_weight(t)
+    torch.cuda.synchronize()
+    got = pk.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(got, layout.pack_weight(w))
+
+
+@pytest.mark.parametrize("B", [5, 32, 70])
+def test_qproj_packed_matches_oracle(gpu_lib, B):
+    import decode_attention_02_amd as mfa
+    w = dataclasses.replace(W[2], batch=B, hidden=1024, q_rank=512, context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=22)
+    T = workloads.to_torch(inp)
+    say(f"qproj packed B={B}")
+    wd, wu = mfa.pack_weight(T["w_qdown"]), mfa.pack_weight(T["w_qup"])
+    q = mfa.qproj(T["x"], wd, T["g"], wu, 64, 256, packed=True)
+    q_rm = mfa.qproj(T["x"], T["w_qdown"], T["g"], T["w_qup"], 64, 256)
+    torch.cuda.synchronize()
+    check_bf16(to_np(q), orun.query(inp), f"qproj packed B={B}")
+    check_bf16(to_np(q_rm), orun.query(inp), f"qproj row-major B={B}")
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

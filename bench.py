@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -99,15 +101,34 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
                       f"tokens), fp64 numpy, mean of {runs} runs ({dt:.2f} s each)"}
 
 
+def copy_calibration(mib: int) -> None:
+    """Five device-to-device copies of exactly ``mib`` MiB each: a kernel whose
+    HBM traffic is known (mib MiB read, mib MiB written per launch), so that
+    rocprofv3's FETCH_SIZE / WRITE_SIZE readings can be scaled to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    pad = torch.empty(1 << 27, dtype=torch.float32, device="cuda:0")
+    for _ in range(5):
+        pad.fill_(0.0)           # evict src/dst from the 256 MB last-level cache
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: n bytes in, n bytes out
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import decode_attention_02_amd as mfa
     import workloads
     from decode_attention_02_amd.step import DecodeStep, prefill

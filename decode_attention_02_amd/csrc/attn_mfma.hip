@@ -10,20 +10,26 @@
 // with several cache blocks in flight per compute unit at all times.
 //
 // One workgroup (8 waves, 2 per SIMD) owns one (sequence, split) pair and
-// walks it one 64-token cache block at a time. The waves split by role:
+// walks it one 64-token cache block at a time. The waves split by role, and
+// each role runs its own loop (the role index is a scalar, so the branch is
+// uniform and each wave passes only its own role's barriers; both loops pass
+// the same number):
 //   * QK waves 0..3: wave w holds K rows 16w..16w+15 of each block and
 //     computes S^T[token][head] = K . Q^T on the 16x16x32 matrix cores (the
 //     16 tokens are the row side, the 64 heads sharing the KV head four
 //     16-column tiles of Q, staged once in LDS in operand order); then the
 //     online softmax: per-head block max across the four QK waves through
-//     LDS, p = exp2(s - m), lane-partial row sums, P^T (bf16) into LDS;
+//     LDS, p = exp2(s * c - m) as one fma and one exp2, lane-partial row
+//     sums, P^T (bf16) into LDS;
 //   * PV waves 4..7: wave 4+j holds the V^T rows (features) 64j..64j+63 of
 //     each block and accumulates O^T[feature][head] += V^T . P^T.
-// Each wave only ever holds its own role's operands, so a ring of R blocks
-// of registers keeps R-1 blocks of loads in flight per wave (bf16: R = 4,
-// 192 KB per compute unit). The three stages are skewed across iterations
-// separated by one barrier each: iteration i computes S of block i, the
-// softmax of block i-1 and the P.V product of block i-2.
+// Each wave holds only its own role's operands in a register ring of RK
+// (QK) or RV (PV) blocks, filled with buffer loads. The stages are skewed
+// across iterations separated by one barrier each: iteration i computes the
+// softmax of block i-1 and S of block i, and the P.V product of block i-2.
+// Every iteration issues the same number of loads (past the walk through
+// empty buffer resources, which read nothing), so the compiler's wait before
+// a ring slot is consumed leaves the younger slots in flight.
 // The running max is updated lazily: only when a block's max exceeds it by
 // more than 2^8 (log2 units) are O and the row sums rescaled, so p <= 256;
 // the result is the same softmax, normalised by the same reference at the end.
@@ -45,14 +51,16 @@ constexpr int kH = 64;
 constexpr int kD = 256;
 constexpr float kLazy = 8.0f;           // rescale only when the max grows by > 2^8
 
-template <bool FP8, int RING>
+template <bool FP8>
 struct Cfg {
   static constexpr int kBlockBytes = kBlockTokens * kD * (FP8 ? 1 : 2);
   static constexpr int kLoads = FP8 ? 4 : 8;     // 16-byte loads per lane per block (K or V)
   static constexpr int kSlot = kLoads + (FP8 ? 2 : 0);   // + K and V scales (QK waves, FP8)
-  static constexpr int kRing = RING;             // blocks of registers per wave
-  static constexpr int kUnroll = RING % 2 ? 2 * RING : RING;   // multiple of the ring and of 2
 };
+
+// Unroll of a loop over blocks that keeps ring slots (ring of R) and
+// parities static: a multiple of R and of 2.
+constexpr int unroll_for(int r) { return r % 2 ? 2 * r : r; }
 
 // d offset of operand k-step s for lane group g (the K and Q sides agree).
 template <bool FP8>
@@ -74,13 +82,21 @@ __device__ __forceinline__ uint32_t keep_bf16(uint32_t word, bool lo_ok, bool hi
   return (lo_ok ? (word & 0xffffu) : 0u) | (hi_ok ? (word & 0xffff0000u) : 0u);
 }
 
+// Buffer-resource word 3 for untyped dword loads (32-bit data format).
+constexpr int kRsrcFlags = 0x00020000;
+
+// 16-byte load through a buffer resource; a resource with zero records makes
+// it a load that returns zeros and touches no memory.
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 }  // namespace
 
-template <bool FP8, int RING>
+// RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
+template <bool FP8, int RK, int RV>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
-  using C = Cfg<FP8, RING>;
-  constexpr int R = C::kRing;
-  constexpr int U = C::kUnroll;
+  using C = Cfg<FP8>;
   __shared__ __attribute__((aligned(16))) uint4 q_lds[4 * 8 * 64];      // 32 KB, operand order
   __shared__ __attribute__((aligned(16))) uint4 p_lds[2][4 * 2 * 64];   // 2 x 8 KB, operand order
   __shared__ __attribute__((aligned(16))) float red[2][kH * 4];         // block max [head][QK wave]
@@ -90,275 +106,375 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   __shared__ float m_lds[kH];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const bool is_qk = w < 4;
+  // wave index as a scalar: the role branches below are uniform per wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int ww = w & 3;                 // QK: token group; PV: feature group of 64
-  const int split = blockIdx.x % a.num_splits;
-  const int b = blockIdx.x / a.num_splits;
 
-  int L = a.seq_lens[b];
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8). Remap so
+  // that each XCD runs a contiguous range of (sequence, split) pairs: the
+  // splits of one sequence then share one L2 for their query reads.
+  int id = blockIdx.x;
+  if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+  const int split = id % a.num_splits;
+  const int b = id / a.num_splits;
+
+  int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[b];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int t0 = split * a.chunk_tokens;
   const int t1 = min(t0 + a.chunk_tokens, L);
   const int blk0 = t0 >> 6;
   const int N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;   // blocks to walk
 
-  // QK state (lane holds heads 16ht + c)
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
-  // acc: PV waves: O^T, lane holds O^T[64ww + 16dt + 4g + i][16ht + c];
-  // QK waves: acc[parity][ht] keeps S of the last block until its softmax.
-  // One array for both roles keeps the register budget of either role.
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if (N > 0) {
-    // Q -> LDS in operand order: block (ht, s), lane (gg, cc) holds
-    // Q[ht*16+cc][qk_dim(s, gg) .. +8].
-    const uint16_t* qb = a.q + static_cast<size_t>(b) * kH * kD;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int idx = tid + 512 * r;
-      const int ln = idx & 63, blk = idx >> 6;
-      const int ht = blk >> 3, s = blk & 7;
-      const int gg = ln >> 4, cc = ln & 15;
-      q_lds[idx] = *reinterpret_cast<const uint4*>(qb + (ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
+  // Q rows of this sequence -> LDS in operand order: block (ht, s), lane
+  // (gg, cc) holds Q[ht*16+cc][qk_dim(s, gg) .. +8]. Each role loads them
+  // between the first ring block and the rest, so staging Q waits for Q and
+  // block 0 only.
+  uint4 qv0, qv1, qv2, qv3;
+  auto q_src = [&](int r) __attribute__((always_inline)) -> const uint4* {
+    const int idx = tid + 512 * r;
+    const int ln = idx & 63, blk = idx >> 6;
+    const int ht = blk >> 3, s = blk & 7;
+    const int gg = ln >> 4, cc = ln & 15;
+    return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
+                                          (ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
+  };
+  auto load_q = [&]() __attribute__((always_inline)) {
+    qv0 = *q_src(0); qv1 = *q_src(1); qv2 = *q_src(2); qv3 = *q_src(3);
+  };
+  auto store_q = [&]() __attribute__((always_inline)) {
+    q_lds[tid] = qv0; q_lds[tid + 512] = qv1; q_lds[tid + 1024] = qv2; q_lds[tid + 1536] = qv3;
+  };
+  // prologue of either role: ring blocks 0 .. R-1 and Q, then Q -> LDS. The
+  // QK waves need K block 0 with Q and load it first; the PV waves load Q
+  // first (V block 0 is used two iterations later).
+  auto prologue = [&](auto r_c, auto k_first_c, auto&& issue) __attribute__((always_inline)) {
+    constexpr int RR = decltype(r_c)::value;
+    constexpr bool kFirst = decltype(k_first_c)::value;
+    if (N > 0) {
+      if constexpr (kFirst) {
+        issue(std::integral_constant<int, 0>{}, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      load_q();
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<kFirst ? 1 : 0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
+      __builtin_amdgcn_sched_barrier(0);
+      store_q();
     }
+  };
 
-    const int* bt_row = a.block_table ? a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
-                                      : nullptr;
-    auto phys = [&](int n) -> size_t {   // physical id of the workgroup's n-th block
-      const int j = blk0 + n;
-      int id = bt_row ? bt_row[j] : b * a.max_blocks_per_seq + j;
-      id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-      return static_cast<size_t>(id);
-    };
+  // Block-table reads go through the constant address space: the table is
+  // read-only here, so a uniform index becomes a scalar load that does not
+  // join the vector-memory counter the K/V ring waits on.
+  using cint = const __attribute__((address_space(4))) int;
+  cint* bt_row = a.block_table
+                     ? (cint*)a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
+                     : nullptr;
+  auto phys = [&](int n) __attribute__((always_inline)) -> size_t {   // physical id of the workgroup's n-th block
+    const int j = blk0 + n;
+    int pid = bt_row ? bt_row[j] : b * a.max_blocks_per_seq + j;
+    pid = pid < 0 ? 0 : (pid >= a.num_blocks ? a.num_blocks - 1 : pid);
+    return static_cast<size_t>(pid);
+  };
+  auto tokens_in = [&](int n) __attribute__((always_inline)) { return t1 - (blk0 + n) * kBlockTokens; };   // valid tokens of block n (>= 1)
 
-    // Register rings: QK waves keep K blocks (+ FP8 scales), PV waves V blocks.
-    uint4 ring[R][C::kSlot];
+  // Every wave passes the same barriers: one after staging Q, one per
+  // iteration i = 0 .. N+1, one before the epilogue.
+  if (w < 4) {
+    // ================= QK waves: S = K.Q^T, online softmax, P^T -> LDS
+    constexpr int R = RK;
+    constexpr int U = unroll_for(RK);
+    float m_run[4], l_run[4];            // per head 16ht + c, log2 units of scaled logits
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
+    const float cl2 = a.scale_log2;      // > 0
+    uint4 ring[R][C::kSlot];             // K units of 16 tokens (+ FP8 K, V scales)
+    f32x4_t sb[2][4];                    // raw logits of the last two blocks, by parity
+    uint4 vkeep[2];                      // FP8: V scales of the last two blocks, by parity
+    vkeep[0] = vkeep[1] = make_uint4(0u, 0u, 0u, 0u);
+    // Loads block n into a ring slot; n >= N (past the walk) issues the same
+    // number of loads through empty resources, which return zeros and read
+    // nothing, so the loop's load count is the same on every path.
     auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
-      const size_t pb = phys(n);
-      if (is_qk) {
-        // units (tg = ww, s): K[16ww + c][..], 1 KB contiguous per load
-        const uint8_t* kp = a.k + pb * C::kBlockBytes + (ww * C::kLoads) * 1024 + lane * 16;
-        static_for<0, C::kLoads>([&](auto sc) {
-          constexpr int s = decltype(sc)::value;
-          ring[slot][s] = *reinterpret_cast<const uint4*>(kp + s * 1024);
-        });
-        if constexpr (FP8) {
-          ring[slot][4] = *reinterpret_cast<const uint4*>(a.k_scale + pb * kBlockTokens + 16 * ww + 4 * g);
-          ring[slot][5] = *reinterpret_cast<const uint4*>(a.v_scale + pb * kBlockTokens + 16 * ww + 4 * g);
-        }
-      } else {
-        // bf16 units (fg = 4ww + s/2, ks = s%2); FP8 units fg = 4ww + s
-        const uint8_t* vp = a.v + pb * C::kBlockBytes + (ww * C::kLoads) * 1024 + lane * 16;
-        static_for<0, C::kLoads>([&](auto sc) {
-          constexpr int s = decltype(sc)::value;
-          ring[slot][s] = *reinterpret_cast<const uint4*>(vp + s * 1024);
-        });
+      const bool real = n < N;
+      const size_t pb = phys(real ? n : 0);
+      // units (tg = ww, s): K[16ww + c][..], 1 KB contiguous per load
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.k) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
+      const int vo = (ww * C::kLoads) * 1024 + lane * 16;
+      static_for<0, C::kLoads>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        ring[slot][s] = buf_load16(rk, vo + s * 1024);
+      });
+      if constexpr (FP8) {
+        const int so = (16 * ww + 4 * g) * 4;
+        const int nr = real ? kBlockTokens * 4 : 0;
+        const auto rks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.k_scale) + pb * kBlockTokens, 0, nr, kRsrcFlags);
+        const auto rvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.v_scale) + pb * kBlockTokens, 0, nr, kRsrcFlags);
+        ring[slot][4] = buf_load16(rks, so);
+        ring[slot][5] = buf_load16(rvs, so);
       }
     };
-    static_for<0, R>([&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      if (r < N) issue(rc, r);
-    });
+    // S^T of block n (16 tokens x 64 heads of this wave) -> sb[par], block max -> red
+    auto scores = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
+      constexpr int par = decltype(par_c)::value;
+      f32x4_t s_acc[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      static_for<0, 8>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        bf16x8_t kop;
+        if constexpr (FP8) {
+          const uint4 u = ring[slot][s >> 1];
+          kop = (s & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
+        } else {
+          kop = as_bf16x8(ring[slot][s]);
+        }
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
+      });
+      if constexpr (FP8) {
+        const uint4 k4 = ring[slot][4];
+        const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
+                             __uint_as_float(k4.w)};
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s_acc[ht][e] *= ks[e];
+        vkeep[par] = ring[slot][5];   // the slot is refilled below
+      }
+      const int lim = tokens_in(n);
+      if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
+        const int tt0 = 16 * ww + 4 * g;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s_acc[ht][e] = (tt0 + e < lim) ? s_acc[ht][e] : -INFINITY;
+      }
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        float m = fmaxf(fmaxf(s_acc[ht][0], s_acc[ht][1]), fmaxf(s_acc[ht][2], s_acc[ht][3]));
+        m = rows4_max(m);
+        if (g == 0) red[par][(ht * 16 + c) * 4 + ww] = m;
+        sb[par][ht] = s_acc[ht];
+      }
+    };
+    // softmax of block n (its logits in sb[par]): P^T -> p_lds[par], rescale factors
+    auto softmax = [&](auto par_c) __attribute__((always_inline)) {
+      constexpr int par = decltype(par_c)::value;
+      float vs[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) {
+        const uint4 v4 = vkeep[par];
+        vs[0] = __uint_as_float(v4.x); vs[1] = __uint_as_float(v4.y);
+        vs[2] = __uint_as_float(v4.z); vs[3] = __uint_as_float(v4.w);
+      }
+      bool rescale = false;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const float4 r4 = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
+        // block max over all 64 tokens (finite: every walked block has a valid token)
+        const float tz = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)) * cl2;
+        float alpha = 1.0f;
+        if (tz > m_run[ht] + kLazy) {          // also true for the first block
+          alpha = __builtin_amdgcn_exp2f(m_run[ht] - tz);
+          m_run[ht] = tz;
+          rescale = true;
+        }
+        const float nm = -m_run[ht];
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[par][ht][e], cl2, nm));
+        l_run[ht] = l_run[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        if constexpr (FP8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] *= vs[e];
+        }
+        if (ww == 0 && g == 0) alpha_lds[par][ht * 16 + c] = alpha;
+        // P^T into operand block (ht, ks) of buffer par
+        int ks, gr;
+        if constexpr (FP8) { ks = g >> 1; gr = ww; }
+        else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
+        uint2 pk;
+        pk.x = pack_bf16x2(p[0], p[1]);
+        pk.y = pack_bf16x2(p[2], p[3]);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[par]) +
+                       ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
+        *reinterpret_cast<uint2*>(dst) = pk;
+      }
+      if (ww == 0) {
+        const bool any = __ballot(rescale) != 0ull;
+        if (lane == 0) flag_lds[par] = any ? 1 : 0;
+      }
+    };
+
+    // Every iteration issues the same loads (empty ones past the walk), so
+    // every path into a consumer has the same loads in flight and the wait
+    // before it leaves R-1 blocks outstanding.
+    prologue(std::integral_constant<int, R>{}, std::true_type{}, issue);
     __syncthreads();   // Q staged
 
-    uint4 vkeep[2];                       // FP8: V scales of the last two blocks, by parity
-    vkeep[0] = vkeep[1] = make_uint4(0u, 0u, 0u, 0u);
-    for (int base = 0; base < N + 2; base += U) {
+    // iteration 0: S of block 0
+    if (N > 0) {
+      scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, 0);
+      issue(std::integral_constant<int, 0>{}, R);
+    }
+    __syncthreads();
+    // iterations 1 .. : softmax(i-1) and S(i) in one straight block, so the
+    // matrix-core and vector work can interleave; groups of U keep ring slots
+    // and parities static (i = base + r with base = 1 mod U)
+    int base = 1;
+    for (; base + U <= N; base += U) {
       static_for<0, U>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        constexpr int rs = r % R;                 // ring slot of block i
-        constexpr int rs2 = (r + 2 * R - 2) % R;  // ... of block i-2
-        constexpr int par = r & 1, par1 = (r + 1) & 1;
-        const int i = base + r;                   // base is a multiple of U: i = r mod R, mod 2
-        if (i < N + 2) {
-          if (is_qk) {
-            // ---- S^T of block i
-            if (i < N) {
-              f32x4_t s_acc[4];
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-              static_for<0, 8>([&](auto sc) {
-                constexpr int s = decltype(sc)::value;
-                bf16x8_t kop;
-                if constexpr (FP8) {
-                  const uint4 u = ring[rs][s >> 1];
-                  kop = (s & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
-                } else {
-                  kop = as_bf16x8(ring[rs][s]);
-                }
-#pragma unroll
-                for (int ht = 0; ht < 4; ++ht)
-                  s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
-              });
-              // scale, mask, local max over this wave's 16 tokens
-              const int lim = t1 - (blk0 + i) * kBlockTokens;
-              const int tt0 = 16 * ww + 4 * g;
-              float kscv[4] = {1.f, 1.f, 1.f, 1.f};
-              if constexpr (FP8) {
-                const uint4 k4 = ring[rs][4];
-                kscv[0] = __uint_as_float(k4.x); kscv[1] = __uint_as_float(k4.y);
-                kscv[2] = __uint_as_float(k4.z); kscv[3] = __uint_as_float(k4.w);
-              }
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht) {
-                float m = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  float sv = s_acc[ht][e] * a.scale_log2;
-                  if constexpr (FP8) sv *= kscv[e];
-                  sv = (tt0 + e < lim) ? sv : -INFINITY;
-                  s_acc[ht][e] = sv;
-                  m = fmaxf(m, sv);
-                }
-                m = rows4_max(m);
-                if (g == 0) red[i & 1][(ht * 16 + c) * 4 + ww] = m;
-              }
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht) acc[par][ht] = s_acc[ht];
-              // the slot is refilled below; the softmax of this block (next
-              // iteration) still needs its V scales
-              if constexpr (FP8) vkeep[par] = ring[rs][5];
-              if (i + R < N) issue(std::integral_constant<int, rs>{}, i + R);
-            }
-            // ---- softmax of block i-1
-            if (i >= 1 && i - 1 < N) {
-              const int n = i - 1;
-              const int lim = t1 - (blk0 + n) * kBlockTokens;
-              const int tt0 = 16 * ww + 4 * g;
-              float vscv[4] = {1.f, 1.f, 1.f, 1.f};
-              if constexpr (FP8) {
-                const uint4 v4 = vkeep[par1];
-                vscv[0] = __uint_as_float(v4.x); vscv[1] = __uint_as_float(v4.y);
-                vscv[2] = __uint_as_float(v4.z); vscv[3] = __uint_as_float(v4.w);
-              }
-              bool rescale = false;
-              float4 rr[4];
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht) rr[ht] = reinterpret_cast<const float4*>(red[n & 1])[ht * 16 + c];
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht) {
-                const float4 r4 = rr[ht];
-                const float tmax = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w));
-                float alpha = 1.0f;
-                if (tmax > m_run[ht] + kLazy) {          // also true for the first block
-                  alpha = __builtin_amdgcn_exp2f(m_run[ht] - tmax);
-                  m_run[ht] = tmax;
-                  rescale = true;
-                }
-                float p[4], psum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const bool ok = tt0 + e < lim;
-                  const float ex = __builtin_amdgcn_exp2f(acc[par1][ht][e] - m_run[ht]);
-                  psum += ok ? ex : 0.f;
-                  float pv = ex;
-                  if constexpr (FP8) pv *= vscv[e];
-                  p[e] = ok ? pv : 0.f;
-                }
-                l_run[ht] = l_run[ht] * alpha + psum;
-                if (ww == 0 && g == 0) alpha_lds[n & 1][ht * 16 + c] = alpha;
-                // P^T into operand block (ht, ks) of buffer n&1
-                int ks, gr;
-                if constexpr (FP8) { ks = g >> 1; gr = ww; }
-                else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
-                uint2 pk;
-                pk.x = pack_bf16x2(p[0], p[1]);
-                pk.y = pack_bf16x2(p[2], p[3]);
-                uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[n & 1]) +
-                               ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
-                *reinterpret_cast<uint2*>(dst) = pk;
-              }
-              if (ww == 0) {
-                const bool any = __ballot(rescale) != 0ull;
-                if (lane == 0) flag_lds[n & 1] = any ? 1 : 0;
-              }
-            }
-          } else {
-            // ---- O^T += V^T . P^T of block i-2
-            if (i >= 2 && i - 2 < N) {
-              const int n = i - 2;
-              constexpr int slot = rs2;
-              if (flag_lds[n & 1]) {
-#pragma unroll
-                for (int ht = 0; ht < 4; ++ht) {
-                  const float al = alpha_lds[n & 1][ht * 16 + c];
-#pragma unroll
-                  for (int dt = 0; dt < 4; ++dt) acc[dt][ht] *= al;
-                }
-              }
-              const int lim = t1 - (blk0 + n) * kBlockTokens;
-              if (lim < kBlockTokens) {
-                // tokens past the end: zero their V so 0 * (garbage) cannot reach O
-                static_for<0, C::kLoads>([&](auto sc) {
-                  constexpr int s = decltype(sc)::value;
-                  uint4 u = ring[slot][s];
-                  if constexpr (FP8) {
-                    uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                      uint32_t msk = 0;
-#pragma unroll
-                      for (int e = 0; e < 4; ++e)
-                        if (g * 16 + q4 * 4 + e < lim) msk |= 0xffu << (8 * e);
-                      wd[q4] &= msk;
-                    }
-                    u = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                  } else {
-                    const int tb = (s & 1) * 32 + g * 8;      // unit (dt = s/2, ks = s%2)
-                    u.x = keep_bf16(u.x, tb + 0 < lim, tb + 1 < lim);
-                    u.y = keep_bf16(u.y, tb + 2 < lim, tb + 3 < lim);
-                    u.z = keep_bf16(u.z, tb + 4 < lim, tb + 5 < lim);
-                    u.w = keep_bf16(u.w, tb + 6 < lim, tb + 7 < lim);
-                  }
-                  ring[slot][s] = u;
-                });
-              }
-              static_for<0, 2>([&](auto ksc) {
-                constexpr int ks = decltype(ksc)::value;
-                bf16x8_t pop[4];
-#pragma unroll
-                for (int ht = 0; ht < 4; ++ht) pop[ht] = as_bf16x8(p_lds[n & 1][(ht * 2 + ks) * 64 + lane]);
-                static_for<0, 4>([&](auto dtc) {
-                  constexpr int dt = decltype(dtc)::value;
-                  bf16x8_t vop;
-                  if constexpr (FP8) {
-                    const uint4 u = ring[slot][dt];
-                    vop = ks ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
-                  } else {
-                    vop = as_bf16x8(ring[slot][dt * 2 + ks]);
-                  }
-#pragma unroll
-                  for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = mfma_16x16x32(vop, pop[ht], acc[dt][ht]);
-                });
-              });
-              if (n + R < N) issue(std::integral_constant<int, slot>{}, n + R);
-            }
-          }
-          __syncthreads();
-        }
+        constexpr int slot = (1 + r) % R, par = (1 + r) & 1, par1 = r & 1;
+        const int i = base + r;
+        softmax(std::integral_constant<int, par1>{});
+        scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
+        issue(std::integral_constant<int, slot>{}, i + R);
+        __syncthreads();
       });
     }
-  }
+    // the rest: i = base .. N+1 (at most U+1 iterations)
+    static_for<0, U + 1>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      constexpr int slot = (1 + r) % R, par = (1 + r) & 1, par1 = r & 1;
+      const int i = base + r;
+      if (i <= N + 1) {
+        if (i < N) {
+          softmax(std::integral_constant<int, par1>{});
+          scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
+          issue(std::integral_constant<int, slot>{}, i + R);
+        } else if (i == N) {
+          softmax(std::integral_constant<int, par1>{});
+        }
+        __syncthreads();
+      }
+    });
 
-  // ---- row sums (QK waves) -> LDS -> PV waves normalise and write
-  if (is_qk) {
+    // row sums -> LDS for the PV waves
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const float l = rows4_sum(l_run[ht]);
       if (g == 0) lred[(ht * 16 + c) * 4 + ww] = l;
       if (ww == 0 && g == 0) m_lds[ht * 16 + c] = m_run[ht];
     }
-  }
-  __syncthreads();
-  if (!is_qk) {
+    __syncthreads();
+  } else {
+    // ================= PV waves: O^T += V^T . P^T
+    constexpr int R = RV;
+    constexpr int U = unroll_for(RV);
+    // acc[dt][ht]: lane holds O^T[64ww + 16dt + 4g + i][16ht + c]
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 ring[R][C::kLoads];
+    auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {   // as for K
+      constexpr int slot = decltype(slot_c)::value;
+      const bool real = n < N;
+      const size_t pb = phys(real ? n : 0);
+      // bf16 units (fg = 4ww + s/2, ks = s%2); FP8 units fg = 4ww + s
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.v) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
+      const int vo = (ww * C::kLoads) * 1024 + lane * 16;
+      static_for<0, C::kLoads>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        ring[slot][s] = buf_load16(rv, vo + s * 1024);
+      });
+    };
+    auto pv = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
+      constexpr int par = decltype(par_c)::value;
+      if (flag_lds[par]) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const float al = alpha_lds[par][ht * 16 + c];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[dt][ht] *= al;
+        }
+      }
+      const int lim = tokens_in(n);
+      if (lim < kBlockTokens) {
+        // tokens past the end: zero their V so 0 * (stale data) cannot reach O
+        static_for<0, C::kLoads>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          uint4 u = ring[slot][s];
+          if constexpr (FP8) {
+            uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              uint32_t msk = 0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (g * 16 + q4 * 4 + e < lim) msk |= 0xffu << (8 * e);
+              wd[q4] &= msk;
+            }
+            u = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          } else {
+            const int tb = (s & 1) * 32 + g * 8;      // unit (dt = s/2, ks = s%2)
+            u.x = keep_bf16(u.x, tb + 0 < lim, tb + 1 < lim);
+            u.y = keep_bf16(u.y, tb + 2 < lim, tb + 3 < lim);
+            u.z = keep_bf16(u.z, tb + 4 < lim, tb + 5 < lim);
+            u.w = keep_bf16(u.w, tb + 6 < lim, tb + 7 < lim);
+          }
+          ring[slot][s] = u;
+        });
+      }
+      static_for<0, 2>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        bf16x8_t pop[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) pop[ht] = as_bf16x8(p_lds[par][(ht * 2 + ks) * 64 + lane]);
+        static_for<0, 4>([&](auto dtc) {
+          constexpr int dt = decltype(dtc)::value;
+          bf16x8_t vop;
+          if constexpr (FP8) {
+            const uint4 u = ring[slot][dt];
+            vop = ks ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
+          } else {
+            vop = as_bf16x8(ring[slot][dt * 2 + ks]);
+          }
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = mfma_16x16x32(vop, pop[ht], acc[dt][ht]);
+        });
+      });
+    };
+
+    prologue(std::integral_constant<int, R>{}, std::false_type{}, issue);
+    __syncthreads();   // Q staged
+    __syncthreads();   // iteration 0 (S of block 0 on the QK waves)
+    __syncthreads();   // iteration 1 (softmax of block 0)
+    // iteration n + 2: P.V of block n
+    int nb = 0;
+    for (; nb + U <= N; nb += U) {
+      static_for<0, U>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int slot = r % R, par = r & 1;
+        const int n = nb + r;
+        pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
+        issue(std::integral_constant<int, slot>{}, n + R);
+        __syncthreads();
+      });
+    }
+    static_for<0, U>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      constexpr int slot = r % R, par = r & 1;
+      const int n = nb + r;
+      if (n < N) {
+        pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
+        issue(std::integral_constant<int, slot>{}, n + R);
+        __syncthreads();
+      }
+    });
+
+    __syncthreads();   // row sums staged
     float lsum[4], mh[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -413,9 +529,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(B * a.num_splits)), block(512);
   if (fp8)
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 2, 3>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

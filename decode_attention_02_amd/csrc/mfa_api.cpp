@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "kernels.h"
@@ -123,7 +124,7 @@ const char* mfa_status_str(int s) {
     case MFA_ERR_SHAPE: return "size out of range or inconsistent";
     case MFA_ERR_DTYPE: return "unsupported dtype or dtype combination";
     case MFA_ERR_ALIGN: return "device pointer not 16-byte aligned";
-    case MFA_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
+    case MFA_ERR_UNSUPPORTED: return "the library has no kernel for this shape";
     case MFA_ERR_WORKSPACE: return "workspace missing or too small";
     case MFA_ERR_HIP: return "HIP runtime reported a launch failure";
     default: return "unknown status";
@@ -292,7 +293,7 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   if (static_cast<long long>(num_splits) * chunk_tokens < max_seq_len) return MFA_ERR_SHAPE;
   if (static_cast<long long>(B) * num_splits > 0x7fffffffll) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
-  if (!(sm_scale == sm_scale)) return MFA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return MFA_ERR_SHAPE;
   const bool mfma = mfma_shape(H, d, cache->dtype);
   if (mfma) {
     if (q_dtype != MFA_BF16) return MFA_ERR_DTYPE;

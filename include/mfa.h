@@ -95,7 +95,7 @@ typedef enum {
   MFA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent        */
   MFA_ERR_DTYPE = 3,        /* unsupported dtype or dtype combination        */
   MFA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned       */
-  MFA_ERR_UNSUPPORTED = 5,  /* valid request this build has no kernel for    */
+  MFA_ERR_UNSUPPORTED = 5,  /* valid request the library has no kernel for  */
   MFA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required    */
   MFA_ERR_HIP = 7           /* the HIP runtime reported a launch failure     */
 } mfa_status;
@@ -210,7 +210,8 @@ size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
  * seq_lens   [B] int32 device: tokens of sequence b to attend (0..max_seq_len;
  *            0 gives zeros)
  * max_seq_len host upper bound of seq_lens (sizes the launch)
- * sm_scale   logit scale (1/sqrt(d) for scaled dot products)
+ * sm_scale   logit scale, positive and finite (1/sqrt(d) for scaled dot
+ *            products); anything else is MFA_ERR_SHAPE
  * num_splits >= 1 KV splits per sequence; split j covers tokens
  *            [j*chunk_tokens, min((j+1)*chunk_tokens, seq_len)). Requires
  *            chunk_tokens % 64 == 0 and num_splits*chunk_tokens >= max_seq_len.

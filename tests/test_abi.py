@@ -59,8 +59,8 @@ def _cache(**kw):
 
 
 def _attn(lib, cache, q=P, qdt=BF16, B=4, H=64, seq=P, maxlen=512, ns=1, chunk=512, ws=None,
-          wsb=0, out=P, odt=BF16):
-    return lib.mfa_decode_attn(q, qdt, B, H, ctypes.byref(cache), seq, maxlen, 0.0625, ns, chunk,
+          wsb=0, out=P, odt=BF16, scale=0.0625):
+    return lib.mfa_decode_attn(q, qdt, B, H, ctypes.byref(cache), seq, maxlen, scale, ns, chunk,
                                ws, wsb, out, odt, None)
 
 
@@ -84,6 +84,8 @@ def test_decode_attn_validation(lib):
     assert _attn(lib, _cache(dtype=FP8)) == NULL                 # fp8 without scales
     assert _attn(lib, _cache(dtype=FP8, k_scale=P, v_scale=P), H=32) == UNSUP
     assert _attn(lib, _cache(head_dim=96)) == SHAPE
+    for bad in (0.0, -0.0625, float("inf"), float("nan")):
+        assert _attn(lib, c, scale=bad) == SHAPE                 # scale must be positive, finite
 
 
 def test_kv_append_validation(lib):

@@ -31,15 +31,16 @@ struct GemmPlan {
   int ks;            // K slices
 };
 
-// Column tiles of 32 (64 when N is not a multiple of 32... it always is for
-// the admitted shapes); K is halved until the grid reaches 512 workgroups or
-// a slice would drop below 8 k-steps of 32.
+// Wide outputs (>= 512 tiles of 32 columns) run one K slice on 32-column
+// tiles; narrower ones use 64-column tiles and halve K until the grid reaches
+// 256 workgroups or a slice would drop below 16 k-steps of 32 (two per wave).
 GemmPlan plan_gemm(int N, int K) {
-  GemmPlan p{N % 32 == 0 ? 2 : 4, 1};
+  if (N % 32 == 0 && N / 32 >= 512) return GemmPlan{2, 1};
+  GemmPlan p{N % 64 == 0 ? 4 : 2, 1};
   const int tiles = N / (16 * p.ntiles);
   const int steps = K / 32;
-  while (static_cast<long long>(tiles) * p.ks < 512 && steps % (p.ks * 2) == 0 &&
-         steps / (p.ks * 2) >= 8)
+  while (static_cast<long long>(tiles) * p.ks < 256 && steps % (p.ks * 2) == 0 &&
+         steps / (p.ks * 2) >= 16)
     p.ks *= 2;
   return p;
 }

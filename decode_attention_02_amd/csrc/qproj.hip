@@ -21,44 +21,57 @@ namespace mfa {
 // Skinny bf16 product on the matrix cores: part[ks][m][n] = sum over the K
 // slice ks of A[m][k] * W[n][k] for m < M <= 64.
 //
-// A workgroup owns NT*16 output columns and one K slice; its four waves take
-// interleaved 32-wide k-steps of that slice, so every wave streams distinct
-// weight bytes. Per k-step a wave loads NT weight fragments (lane: 16
-// contiguous bytes of one weight row) and MT activation fragments (lane: 16
-// bytes of one activation row; the activations are small and stay in L2),
-// keeping PD k-steps of loads in flight. The four waves' accumulators are
-// summed through LDS at the end; the sum is written as fp32 partials, or as
-// bf16 directly when the product has a single K slice.
+// A workgroup of 8 waves owns NT*16 output columns and one K slice; the
+// waves take interleaved 32-wide k-steps of that slice, so every wave
+// streams distinct weight bytes. Per k-step a wave loads NT weight fragments
+// (lane: 16 contiguous bytes of one weight row) through buffer resources and
+// MT activation fragments (lane: 16 bytes of one activation row; the
+// activations are small and stay in L2), keeping PD k-steps of loads in
+// flight. The eight waves' accumulators are summed through LDS at the end;
+// the sum is written as fp32 partials, or as bf16 directly when the product
+// has a single K slice.
 // Weights: row-major [N][K] (PACKED = false) or packed in operand order
 // (PACKED = true): 1 KB unit (nt = n/16, kt = k/32) at unit index
 // nt*(K/32) + kt, lane 16*((k%32)/8) + n%16 holding W[n][8*(k/8) .. +8], so
 // that each wave-wide weight load reads 1 KB of contiguous memory.
+constexpr int kGemmWaves = 8;
+
 template <int MT, int NT, int PD, bool PACKED>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
-                                                          const uint16_t* __restrict__ W,
-                                                          float* __restrict__ part,
-                                                          uint16_t* __restrict__ out_bf16, int M,
-                                                          int N, int K, int kchunk) {
+__global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float* __restrict__ part,
+    uint16_t* __restrict__ out_bf16, int M, int N, int K, int kchunk) {
   constexpr int TM = MT * 16, TN = NT * 16;
   constexpr int kPad = TN + 4;                       // padded LDS row (floats)
-  __shared__ __attribute__((aligned(16))) float red[4][TM * kPad];
+  __shared__ __attribute__((aligned(16))) float red[kGemmWaves][TM * kPad];
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int n0 = blockIdx.x * TN;
   const int ks = blockIdx.y;
   const int kbeg = ks * kchunk;
   const int nsteps = kchunk / 32;                    // k-steps in the slice
-  const int mine = (nsteps - w + 3) / 4;             // k-steps of this wave: w, w+4, ...
+  const int mine = (nsteps - w + kGemmWaves - 1) / kGemmWaves;   // k-steps w, w+8, ...
 
-  const uint16_t* wp[NT];
-  const int ksteps = K / 32;
+  // one buffer resource per 16-row weight tile, covering this K slice; the
+  // lane offset of k-step kk is wofs + kk * kstep_bytes
+  __amdgpu_buffer_rsrc_t wr[NT];
+  int wofs;
+  constexpr int kStepBytes = PACKED ? 1024 : 64;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    if constexpr (PACKED)
-      wp[nt] = W + (static_cast<size_t>((n0 / 16 + nt) * ksteps + kbeg / 32) * 64 + lane) * 8;
-    else
-      wp[nt] = W + static_cast<size_t>(n0 + nt * 16 + c) * K + kbeg + g * 8;
+    const uint16_t* base;
+    int bytes;
+    if constexpr (PACKED) {
+      base = W + static_cast<size_t>((n0 / 16 + nt) * (K / 32) + kbeg / 32) * 64 * 8;
+      bytes = nsteps * 1024;
+    } else {
+      base = W + static_cast<size_t>(n0 + nt * 16) * K + kbeg;
+      bytes = (15 * K + kchunk) * 2;
+    }
+    wr[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
   }
+  if constexpr (PACKED) wofs = lane * 16;
+  else wofs = (c * K + g * 8) * 2;
   const uint16_t* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -74,12 +87,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
 
   uint4 wb[PD][NT], ab[PD][MT];
   auto issue = [&](int slot, int j) {                // j-th k-step of this wave
-    const int koff = (w + 4 * j) * 32;
+    const int kk = w + kGemmWaves * j;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      wb[slot][nt] = *reinterpret_cast<const uint4*>(wp[nt] + (PACKED ? koff * 16 : koff));
+      wb[slot][nt] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr[nt], wofs + kk * kStepBytes, 0, 0));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + koff);
+    for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + kk * 32);
   };
 #pragma unroll
   for (int p = 0; p < PD; ++p)
@@ -99,7 +113,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
     }
   }
 
-  // accumulator lane holds C[mt*16 + 4g + i][nt*16 + c]; sum the four waves
+  // accumulator lane holds C[mt*16 + 4g + i][nt*16 + c]; sum the waves
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -107,7 +121,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w][(mt * 16 + 4 * g + i) * kPad + nt * 16 + c] = acc[mt][nt][i];
   __syncthreads();
-  constexpr int kPer = TM * TN / 256;                // outputs per thread (contiguous in n)
+  constexpr int kPer = TM * TN / (kGemmWaves * 64);  // outputs per thread (contiguous in n)
+  static_assert(kPer == 1 || kPer % 2 == 0, "one or pairs of outputs per thread");
   const int e0 = tid * kPer;
   const int m = e0 / TN, nl = e0 % TN;
   if (m < M) {
@@ -115,17 +130,27 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int o = m * kPad + nl + j;
-      v[j] = (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][o];
+      v[j] = sum;
     }
     if (out_bf16) {
       uint16_t* dst = out_bf16 + static_cast<size_t>(m) * N + n0 + nl;
+      if constexpr (kPer == 1) {
+        dst[0] = f32_to_bf16(v[0]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < kPer; j += 2) *reinterpret_cast<uint32_t*>(dst + j) = pack_bf16x2(v[j], v[j + 1]);
+        for (int j = 0; j < kPer; j += 2) *reinterpret_cast<uint32_t*>(dst + j) = pack_bf16x2(v[j], v[j + 1]);
+      }
     } else {
       float* dst = part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl;
+      if constexpr (kPer == 1) {
+        dst[0] = v[0];
+      } else {
 #pragma unroll
-      for (int j = 0; j < kPer; j += 4)
-        *reinterpret_cast<float4*>(dst + j) = make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+        for (int j = 0; j < kPer; j += 2) *reinterpret_cast<float2*>(dst + j) = make_float2(v[j], v[j + 1]);
+      }
     }
   }
 }
@@ -220,7 +245,7 @@ template <bool PACKED>
 static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                                 int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
   const int kchunk = K / ksplit;
-  dim3 block(256);
+  dim3 block(kGemmWaves * 64);
   if (ntiles == 4) {
     dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
     if (M <= 16)
@@ -228,7 +253,7 @@ static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* par
     else if (M <= 32)
       hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 2, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 3, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
   } else {
     dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
     if (M <= 16)

@@ -178,13 +178,13 @@ def main():
             step.attend(q, T["seq_lens"])
 
     def one(i):
-        """One decode step on buffer set i % rotate: qproj, append, attention, combine."""
+        """One decode step on buffer set i % rotate (DecodeStep: query path,
+        KV append, attention, split combine)."""
         step, wts = sets[i % rotate]
-        q = step.query(T["x"], *wts) if w.has_qproj else T["q"]
-        step.append(T["k_new"], T["v_new"], T["prefill_lens"])
-        attention(i, q)
-        if step.num_splits > 1:
-            mfa.combine_splits(step.split_ws, B, w.heads, w.head_dim, step.num_splits, out=step.out)
+        if w.has_qproj:
+            step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts)
+        else:
+            step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
 
     q_fixed = [sets[r][0].q if w.has_qproj else T["q"] for r in range(rotate)]
 

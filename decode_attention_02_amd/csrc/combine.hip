@@ -25,22 +25,13 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
   const int f = (threadIdx.x % tpb) * 4;
   if (h >= H) return;
   const size_t row0 = static_cast<size_t>(b) * S;
-  // Loads are issued in batches of 8 splits before any is used, so their
-  // latencies overlap (every split's partials are valid memory, empty ones too).
-  constexpr int kBatch = 8;
-  float mstar = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    float2 ml[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      ml[j] = s0 + j < S ? *reinterpret_cast<const float2*>(part_ml + ((row0 + s0 + j) * H + h) * 2)
-                         : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (ml[j].y > 0.f) mstar = fmaxf(mstar, ml[j].x);
-  }
+  // One pass: each batch of up to 16 splits is loaded at once (every split's
+  // partials are valid memory, empty ones too), then merged against a running
+  // max; when a batch raises the max, the sums so far are rescaled by
+  // exp(old - new), the same identity that merges the splits themselves.
+  constexpr int kBatch = 16;
+  float mrun = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
     float2 ml[kBatch];
     float4 o[kBatch];
@@ -52,10 +43,20 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
       o[j] = in ? *reinterpret_cast<const float4*>(part_o + ((row0 + s0 + j) * H + h) * d + f)
                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (ml[j].y > 0.f) bmax = fmaxf(bmax, ml[j].x);   // empty splits carry no weight
+    if (bmax > mrun) {
+      const float sc = mrun == -INFINITY ? 0.f : expf(mrun - bmax);
+      den *= sc;
+      num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+      mrun = bmax;
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (ml[j].y > 0.f) {              // empty splits contribute nothing, whatever they hold
-        const float wgt = expf(ml[j].x - mstar);
+      if (ml[j].y > 0.f) {
+        const float wgt = expf(ml[j].x - mrun);
         den = fmaf(wgt, ml[j].y, den);
         num.x = fmaf(wgt, o[j].x, num.x);
         num.y = fmaf(wgt, o[j].y, num.y);

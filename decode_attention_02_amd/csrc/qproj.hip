@@ -173,12 +173,25 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) cv[ch][j] = 0.f;
     if (j0 < R) {
-      for (int ks = 0; ks < ksplit; ++ks) {
-        const float* p = part + (static_cast<size_t>(ks) * M + m) * R + j0;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        cv[ch][0] += a.x; cv[ch][1] += a.y; cv[ch][2] += a.z; cv[ch][3] += a.w;
-        cv[ch][4] += b.x; cv[ch][5] += b.y; cv[ch][6] += b.z; cv[ch][7] += b.w;
+      // slices in groups of 8 with all loads of a group in flight at once
+      // (the sum stays in slice order)
+      for (int k0 = 0; k0 < ksplit; k0 += 8) {
+        float4 a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (k0 + u < ksplit) {
+            const float* p = part + (static_cast<size_t>(k0 + u) * M + m) * R + j0;
+            a[u] = *reinterpret_cast<const float4*>(p);
+            b[u] = *reinterpret_cast<const float4*>(p + 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (k0 + u < ksplit) {
+            cv[ch][0] += a[u].x; cv[ch][1] += a[u].y; cv[ch][2] += a[u].z; cv[ch][3] += a[u].w;
+            cv[ch][4] += b[u].x; cv[ch][5] += b[u].y; cv[ch][6] += b[u].z; cv[ch][7] += b[u].w;
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss = fmaf(cv[ch][j], cv[ch][j], ss);

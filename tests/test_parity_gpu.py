@@ -240,6 +240,67 @@ def test_qproj_packed_matches_oracle(gpu_lib, B):
     check_bf16(to_np(q_rm), orun.query(inp), f"qproj row-major B={B}")
 
 
+def test_qproj_split_k_and_reuse(gpu_lib):
+    """A query shape whose up-projection is split over K (partials summed by
+    the reduction kernel) and whose down-projection is not; repeated calls on
+    one workspace are bit-identical (no state carried between calls)."""
+    import decode_attention_02_amd as mfa
+    w = dataclasses.replace(W[2], batch=3, hidden=256, q_rank=2048, heads=4, head_dim=64,
+                            context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=23)
+    T = workloads.to_torch(inp)
+    ws = torch.zeros(mfa.qproj_workspace_bytes(3, 256, 2048, 4, 64, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    say("qproj split-K up-projection, workspace reuse")
+    outs = [mfa.qproj(T["x"], T["w_qdown"], T["g"], T["w_qup"], 4, 64, workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    check_bf16(to_np(outs[0]), orun.query(inp), "qproj split-K up")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    # the same workspace then serves a smaller batch of another shape
+    w2 = dataclasses.replace(W[2], batch=2, hidden=512, q_rank=256, heads=64, head_dim=256,
+                             context=65)
+    inp2 = workloads.make_inputs(2, workload=w2, seed=24)
+    T2 = workloads.to_torch(inp2)
+    ws2 = torch.zeros(mfa.qproj_workspace_bytes(2, 512, 256, 64, 256, torch.bfloat16),
+                      dtype=torch.uint8, device="cuda")
+    a = mfa.qproj(T2["x"], T2["w_qdown"], T2["g"], T2["w_qup"], 64, 256, workspace=ws2)
+    b = mfa.qproj(T2["x"], T2["w_qdown"], T2["g"], T2["w_qup"], 64, 256, workspace=ws2)
+    torch.cuda.synchronize()
+    check_bf16(to_np(a), orun.query(inp2), "qproj reuse")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_replay_matches_eager(gpu_lib):
+    """The whole step (query path, append, attention, combine) captured in a
+    HIP graph: every replay, with eager work and synchronisations in between,
+    equals the eager step bit for bit."""
+    w = dataclasses.replace(W[2], batch=4, hidden=1024, q_rank=512, context=300)
+    inp = workloads.make_inputs(2, workload=w, seed=25)
+    T, cache, step = setup(inp, num_splits=3)
+    say("graph replay vs eager")
+    _, eager = run(T, step)
+    eager = eager.clone()
+    wts = (T["w_qdown"], T["g"], T["w_qup"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts)
+    for r in range(3):
+        step.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+    check_bf16(to_np(eager), orun.decode_step(inp)["o"], "graph step")
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

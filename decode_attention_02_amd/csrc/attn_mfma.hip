@@ -512,8 +512,16 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         for (int dt = 0; dt < 4; ++dt) {
           const int f = 64 * ww + 16 * dt + 4 * g;
           const f32x4_t v = acc[dt][ht];
-          *reinterpret_cast<float4*>(a.part_o + (row * kH + head) * kD + f) =
-              make_float4(v[0], v[1], v[2], v[3]);
+          const size_t po = (row * kH + head) * kD + f;
+          if (a.part_bf16) {
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.part_o) + po) = pk;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.part_o) + po) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
         if (ww == 0 && g == 0) {
           float2 ml;

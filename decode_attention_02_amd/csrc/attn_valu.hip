@@ -130,7 +130,10 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < kMaxPerThread; ++r) {
       const int e = tid + 256 * r;
-      if (e < HD) a.part_o[row * HD + e] = o[r];
+      if (e < HD) {
+        if (a.part_bf16) static_cast<uint16_t*>(a.part_o)[row * HD + e] = f32_to_bf16(o[r]);
+        else static_cast<float*>(a.part_o)[row * HD + e] = o[r];
+      }
     }
     if (tid < H) {
       a.part_ml[(row * H + tid) * 2 + 0] = m_s[tid];

@@ -13,7 +13,9 @@ namespace mfa {
 
 // One workgroup of 256 threads covers 1024/d heads of one sequence; a thread
 // owns 4 consecutive features of one head and reads one float4 per split.
-__global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restrict__ part_o,
+// Partial o is bf16 (PBF16) or fp32; m and l are fp32.
+template <bool PBF16>
+__global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int S, int H, int d, void* out,
                                                           int out_f32) {
@@ -40,8 +42,16 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
       const bool in = s0 + j < S;
       ml[j] = in ? *reinterpret_cast<const float2*>(part_ml + ((row0 + s0 + j) * H + h) * 2)
                  : make_float2(-INFINITY, 0.f);
-      o[j] = in ? *reinterpret_cast<const float4*>(part_o + ((row0 + s0 + j) * H + h) * d + f)
-                : make_float4(0.f, 0.f, 0.f, 0.f);
+      const size_t po = ((row0 + s0 + j) * H + h) * d + f;
+      if constexpr (PBF16) {
+        const uint2 u = in ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(part_o) + po)
+                           : make_uint2(0u, 0u);
+        o[j] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+      } else {
+        o[j] = in ? *reinterpret_cast<const float4*>(static_cast<const float*>(part_o) + po)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     float bmax = -INFINITY;
 #pragma unroll
@@ -78,13 +88,18 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
   }
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
-                          int num_splits, void* out, int out_f32, hipStream_t stream) {
+hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml, int B, int H,
+                          int d, int num_splits, void* out, int out_f32, hipStream_t stream) {
   if (d % 4 || d > 1024) return hipErrorInvalidValue;
   const int hpb = 256 / (d / 4);
   const int groups = (H + hpb - 1) / hpb;
-  hipLaunchKernelGGL(mfa_combine_kernel, dim3(static_cast<unsigned>(B * groups)), dim3(256), 0,
-                     stream, part_o, part_ml, num_splits, H, d, out, out_f32);
+  const dim3 grid(static_cast<unsigned>(B * groups));
+  if (part_bf16)
+    hipLaunchKernelGGL(mfa_combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_ml,
+                       num_splits, H, d, out, out_f32);
+  else
+    hipLaunchKernelGGL(mfa_combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_ml,
+                       num_splits, H, d, out, out_f32);
   return hipGetLastError();
 }
 

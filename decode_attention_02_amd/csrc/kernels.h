@@ -28,7 +28,8 @@ struct AttnArgs {
   int kv_f32;                 // VALU kernel: cache dtype (else bf16)
   float sm_scale;             // VALU kernel (natural exp)
   float scale_log2;           // matrix-core kernel: sm_scale * log2(e)
-  float* part_o;              // [B][S][H][d] when num_splits > 1
+  void* part_o;               // [B][S][H][d] when num_splits > 1: bf16 or fp32
+  int part_bf16;              // part_o element type: bf16 (1) or fp32 (0)
   float* part_ml;             // [B][S][H][2]
   void* out;                  // [B][H][d] when num_splits == 1
   int out_f32;
@@ -37,7 +38,7 @@ struct AttnArgs {
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
+hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml, int B, int H, int d,
                           int num_splits, void* out, int out_f32, hipStream_t stream);
 
 struct AppendArgs {

@@ -331,7 +331,8 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   const size_t rows = static_cast<size_t>(B) * num_splits * H;
   if (num_splits > 1) {
-    a.part_o = static_cast<float*>(workspace);
+    a.part_o = workspace;
+    a.part_bf16 = out_dtype == MFA_BF16;
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + round_up(rows * d * 4, 256));
   }
   a.out = out;
@@ -341,7 +342,7 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
                       : mfa::launch_decode_valu(a, B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
   if (num_splits > 1 && out) {
-    e = mfa::launch_combine(a.part_o, a.part_ml, B, H, d, num_splits, out, a.out_f32, st);
+    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, B, H, d, num_splits, out, a.out_f32, st);
     if (e != hipSuccess) return MFA_ERR_HIP;
   }
   return MFA_OK;
@@ -356,11 +357,10 @@ mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B) * num_splits * H;
-  const float* po = static_cast<const float*>(workspace);
   const float* pml =
       reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + round_up(rows * d * 4, 256));
-  return from_hip(mfa::launch_combine(po, pml, B, H, d, num_splits, out,
-                                      out_dtype == MFA_F32, as_stream(stream)));
+  return from_hip(mfa::launch_combine(workspace, out_dtype == MFA_BF16, pml, B, H, d, num_splits,
+                                      out, out_dtype == MFA_F32, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -197,10 +197,14 @@ mfa_status mfa_kv_append(const void *k_new, const void *v_new, int in_dtype,
 mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
                            int *num_splits, int *chunk_tokens);
 
-/* Bytes of split workspace for mfa_decode_attn / mfa_combine:
- * part_o fp32 [B][num_splits][H][d] followed by part_ml fp32
- * [B][num_splits][H][2] (running max m in natural-log units of the scaled
- * logits, then l = sum_t exp(s_t - m)). 0 when num_splits == 1. */
+/* Bytes of split workspace for mfa_decode_attn / mfa_combine: the
+ * unnormalised partial outputs part_o [B][num_splits][H][d] at offset 0,
+ * then part_ml fp32 [B][num_splits][H][2] (running max m in natural-log
+ * units of the scaled logits, then l = sum_t exp(s_t - m)) at offset
+ * round_up(B*num_splits*H*d*4, 256). part_o holds bf16 values when the
+ * out_dtype of the call is MFA_BF16 and fp32 values when it is MFA_F32, so
+ * mfa_combine must be called with the out_dtype mfa_decode_attn was given.
+ * 0 when num_splits == 1. */
 size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
 
 /*

@@ -118,12 +118,14 @@ def test_split_counts_agree(gpu_lib):
         assert rel_l2(res[s], res[1]) <= 2 * REL_L2_BF16
 
 
-def test_combine_standalone(gpu_lib):
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_combine_standalone(gpu_lib, out_dtype):
     """mfa_combine on drawn partials (some splits empty) against the oracle's
-    log-sum-exp merge; fp32 output."""
+    log-sum-exp merge. With fp32 output the partial outputs are fp32, with
+    bf16 output they are bf16 (the workspace format of each case)."""
     import decode_attention_02_amd as mfa
     rng = np.random.default_rng(77)
-    B, S, H, d = 3, 5, 64, 256
+    B, S, H, d = 3, 20, 64, 256                # 20 splits: two load batches
     o = rng.standard_normal((B, S, H, d)).astype(np.float32)
     m = (rng.standard_normal((B, S, H)) * 3).astype(np.float32)
     l = rng.uniform(0.5, 40, size=(B, S, H)).astype(np.float32)
@@ -134,15 +136,22 @@ def test_combine_standalone(gpu_lib):
     ws = np.zeros(nbytes, dtype=np.uint8)
     rows = B * S * H
     off = -(-rows * d * 4 // 256) * 256
-    ws[:rows * d * 4] = o.reshape(-1).view(np.uint8)
+    if out_dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(o)
+        o = (bits.astype(np.uint32) << 16).view(np.float32)   # the values the kernel reads
+        ws[:rows * d * 2] = bits.reshape(-1).view(np.uint8)
+    else:
+        ws[:rows * d * 4] = o.reshape(-1).view(np.uint8)
     ws[off:off + rows * 8] = np.stack([m, l], axis=-1).reshape(-1).view(np.uint8)
-    say("combine standalone")
-    out = mfa.combine_splits(torch.from_numpy(ws).cuda(), B, H, d, S, out_dtype=torch.float32)
+    say(f"combine standalone {out_dtype}")
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = mfa.combine_splits(torch.from_numpy(ws).cuda(), B, H, d, S, out_dtype=tdt)
     torch.cuda.synchronize()
     got = to_np(out)
+    tol = 1e-6 if out_dtype == "f32" else 4e-3    # bf16: the output rounding alone
     for b in range(B):
         want = omfa.combine([(o[b, s], m[b, s], l[b, s]) for s in range(S)])
-        assert rel_l2(got[b], want) <= 1e-6
+        assert rel_l2(got[b], want) <= tol
     assert np.all(got[0, 0] == 0)
 
 

@@ -35,6 +35,30 @@ class KVCacheDesc(ctypes.Structure):
     ]
 
 
+class StepArgs(ctypes.Structure):
+    """mirror of ``mfa_step_args``"""
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("w_qdown", ctypes.c_void_p), ("w_qup", ctypes.c_void_p),
+        ("q_norm_w", ctypes.c_void_p),
+        ("hidden", ctypes.c_int), ("q_rank", ctypes.c_int), ("weight_layout", ctypes.c_int),
+        ("eps", ctypes.c_float),
+        ("qproj_workspace", ctypes.c_void_p), ("qproj_workspace_bytes", ctypes.c_size_t),
+        ("q", ctypes.c_void_p),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("kv_in_dtype", ctypes.c_int),
+        ("pos", ctypes.c_void_p),
+        ("cache", ctypes.POINTER(KVCacheDesc)),
+        ("seq_lens", ctypes.c_void_p),
+        ("max_seq_len", ctypes.c_int),
+        ("sm_scale", ctypes.c_float),
+        ("num_splits", ctypes.c_int), ("chunk_tokens", ctypes.c_int),
+        ("split_workspace", ctypes.c_void_p), ("split_workspace_bytes", ctypes.c_size_t),
+        ("out", ctypes.c_void_p),
+        ("out_dtype", ctypes.c_int),
+    ]
+
+
 _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _pdesc = ctypes.POINTER(KVCacheDesc)
 _pi = ctypes.POINTER(ctypes.c_int)
@@ -51,6 +75,7 @@ SIGNATURES = {
     "mfa_split_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_decode_attn": (_i, [_p, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p, _i, _p]),
     "mfa_combine": (_i, [_p, _sz, _i, _i, _i, _i, _p, _i, _p]),
+    "mfa_decode_step": (_i, [ctypes.POINTER(StepArgs), _p]),
 }
 
 _LIB = None

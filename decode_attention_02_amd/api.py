@@ -209,3 +209,11 @@ def combine_splits(workspace: torch.Tensor, batch: int, heads: int, head_dim: in
                                          head_dim, num_splits, _ptr(out), _DTYPES[out.dtype],
                                          _stream(workspace.device)))
     return out
+
+
+def decode_step(args: "_lib.StepArgs", device) -> None:
+    """Run a prepared ``mfa_step_args`` (mfa_decode_step) on the current
+    stream of ``device``. The caller keeps the tensors the struct points to
+    alive."""
+    lib = _lib.load()
+    check("mfa_decode_step", lib.mfa_decode_step(ctypes.byref(args), _stream(device)))

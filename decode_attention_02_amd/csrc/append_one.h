@@ -1,0 +1,98 @@
+// One new token of one sequence written into the KV cache by one wave
+// (the decode-step case of the KV append): lane l owns features
+// l*EPT .. l*EPT+EPT-1. F32/BF16 caches copy bits; FP8 caches quantise the
+// token: amax over its d values, scale = amax/448 (one correctly rounded
+// fp32 division, 1 when amax = 0), code = RNE e4m3 of the correctly rounded
+// quotient x/scale ("Step-3 is Large yet Affordable" summary page, §5: the
+// 8-bit cache that raises arithmetic intensity; §7: attention instances own
+// their KV caches). Element positions follow kv_layout.h.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+#include "kv_layout.h"
+
+namespace mfa {
+
+__device__ __forceinline__ float append_load_in(const void* p, size_t i, int in_f32) {
+  return in_f32 ? reinterpret_cast<const float*>(p)[i]
+                : bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+// Token pos[b] of sequence b (n_new == 1); positions outside the table or
+// mapped to no block write nothing.
+template <int CACHE, int EPT>   // CACHE: 0 f32, 1 bf16, 2 fp8
+__device__ __forceinline__ void append_token_wave(const AppendArgs& a, int b, int lane) {
+  const int p0 = a.pos[b];
+  if (p0 < 0) return;
+  const int j = p0 / kBlockTokens;
+  if (j >= a.max_blocks_per_seq) return;
+  const int id = a.block_table ? a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + j]
+                               : b * a.max_blocks_per_seq + j;
+  if (id < 0 || id >= a.num_blocks) return;
+  const int d = a.d;
+  const int off = p0 & 63;
+  const size_t row = static_cast<size_t>(b) * d;
+  float xk[EPT], xv[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    xk[e] = append_load_in(a.k_new, row + lane * EPT + e, a.in_f32);
+    xv[e] = append_load_in(a.v_new, row + lane * EPT + e, a.in_f32);
+  }
+  const size_t esz = CACHE == 0 ? 4 : (CACHE == 1 ? 2 : 1);
+  uint8_t* kb = a.k + static_cast<size_t>(id) * kBlockTokens * d * esz;
+  uint8_t* vb = a.v + static_cast<size_t>(id) * kBlockTokens * d * esz;
+  if constexpr (CACHE == 2) {
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) { ak = fmaxf(ak, fabsf(xk[e])); av = fmaxf(av, fabsf(xv[e])); }
+    ak = wave_max(ak);
+    av = wave_max(av);
+    const float sk = ak > 0.f ? ak / 448.0f : 1.0f;
+    const float sv = av > 0.f ? av / 448.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      kb[k_off_fp8(off, f, d)] = static_cast<uint8_t>(encode_e4m3_rne(xk[e] / sk));
+      vb[v_off_fp8(off, f)] = static_cast<uint8_t>(encode_e4m3_rne(xv[e] / sv));
+    }
+    if (lane == 0) {
+      a.k_scale[static_cast<size_t>(id) * kBlockTokens + off] = sk;
+      a.v_scale[static_cast<size_t>(id) * kBlockTokens + off] = sv;
+    }
+  } else if constexpr (CACHE == 1) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      *reinterpret_cast<uint16_t*>(kb + k_off_bf16(off, f, d)) = f32_to_bf16(xk[e]);  // exact
+      *reinterpret_cast<uint16_t*>(vb + v_off_bf16(off, f)) = f32_to_bf16(xv[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = lane * EPT + e;
+      *reinterpret_cast<float*>(kb + k_off_f32(off, f, d)) = xk[e];
+      *reinterpret_cast<float*>(vb + v_off_f32(off, f)) = xv[e];
+    }
+  }
+}
+
+// Runtime dispatch over cache dtype and head dim.
+__device__ __forceinline__ void append_token(const AppendArgs& a, int b, int lane) {
+  const int ept = a.d >> 6;
+  if (a.cache_dtype == 1) {
+    if (ept == 4) append_token_wave<1, 4>(a, b, lane);
+    else if (ept == 2) append_token_wave<1, 2>(a, b, lane);
+    else append_token_wave<1, 1>(a, b, lane);
+  } else if (a.cache_dtype == 2) {
+    if (ept == 4) append_token_wave<2, 4>(a, b, lane);
+    else if (ept == 2) append_token_wave<2, 2>(a, b, lane);
+    else append_token_wave<2, 1>(a, b, lane);
+  } else {
+    if (ept == 4) append_token_wave<0, 4>(a, b, lane);
+    else if (ept == 2) append_token_wave<0, 2>(a, b, lane);
+    else append_token_wave<0, 1>(a, b, lane);
+  }
+}
+
+}  // namespace mfa

@@ -504,12 +504,15 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         }
       }
     } else {
+      // an empty split writes only (m, l) = (-inf, 0): the combine gives it
+      // no weight and never uses its o
       const size_t row = static_cast<size_t>(b) * a.num_splits + split;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         const int head = ht * 16 + c;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
+          if (N == 0) break;
           const int f = 64 * ww + 16 * dt + 4 * g;
           const f32x4_t v = acc[dt][ht];
           const size_t po = (row * kH + head) * kD + f;

@@ -72,8 +72,11 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, u
 // Row-major bf16 W [N][K] -> operand-order packed weight (N % 16 == 0, K % 32 == 0).
 hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
+// With append set, the same launch also writes one new KV token per
+// sequence (append->n_new == 1, see append_one.h).
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
-                                 float eps, void* out, int out_f32, hipStream_t stream);
+                                 float eps, void* out, int out_f32, const AppendArgs* append,
+                                 hipStream_t stream);
 // out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
 hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
                               int out_f32, hipStream_t stream);

@@ -12,6 +12,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "kv_layout.h"
+#include "append_one.h"
 
 namespace mfa {
 
@@ -118,59 +119,10 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
   }
 }
 
-// Decode-step append (one new token per sequence): one wave per sequence,
-// lane l owns features l*EPT .. l*EPT+EPT-1.
+// Decode-step append (one new token per sequence): one wave per sequence.
 template <int CACHE, int EPT>   // CACHE: 0 f32, 1 bf16, 2 fp8
 __global__ __launch_bounds__(64) void kv_append_one_kernel(AppendArgs a) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const Span sp = block_span(a, b, 0);
-  if (sp.lo >= sp.hi || sp.blk < 0) return;
-  const int d = a.d;
-  const int off = sp.lo & 63;
-  const size_t row = static_cast<size_t>(b) * d;   // n_new == 1
-  float xk[EPT], xv[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    xk[e] = load_in(a.k_new, row + lane * EPT + e, a.in_f32);
-    xv[e] = load_in(a.v_new, row + lane * EPT + e, a.in_f32);
-  }
-  const size_t esz = CACHE == 0 ? 4 : (CACHE == 1 ? 2 : 1);
-  uint8_t* kb = a.k + static_cast<size_t>(sp.blk) * kBlockTokens * d * esz;
-  uint8_t* vb = a.v + static_cast<size_t>(sp.blk) * kBlockTokens * d * esz;
-  if constexpr (CACHE == 2) {
-    float ak = 0.f, av = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) { ak = fmaxf(ak, fabsf(xk[e])); av = fmaxf(av, fabsf(xv[e])); }
-    ak = wave_max(ak);
-    av = wave_max(av);
-    const float sk = ak > 0.f ? ak / 448.0f : 1.0f;
-    const float sv = av > 0.f ? av / 448.0f : 1.0f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int f = lane * EPT + e;
-      kb[k_off_fp8(off, f, d)] = static_cast<uint8_t>(encode_e4m3_rne(xk[e] / sk));
-      vb[v_off_fp8(off, f)] = static_cast<uint8_t>(encode_e4m3_rne(xv[e] / sv));
-    }
-    if (lane == 0) {
-      a.k_scale[static_cast<size_t>(sp.blk) * kBlockTokens + off] = sk;
-      a.v_scale[static_cast<size_t>(sp.blk) * kBlockTokens + off] = sv;
-    }
-  } else if constexpr (CACHE == 1) {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int f = lane * EPT + e;
-      *reinterpret_cast<uint16_t*>(kb + k_off_bf16(off, f, d)) = f32_to_bf16(xk[e]);  // exact
-      *reinterpret_cast<uint16_t*>(vb + v_off_bf16(off, f)) = f32_to_bf16(xv[e]);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int f = lane * EPT + e;
-      *reinterpret_cast<float*>(kb + k_off_f32(off, f, d)) = xk[e];
-      *reinterpret_cast<float*>(vb + v_off_f32(off, f)) = xv[e];
-    }
-  }
+  append_token_wave<CACHE, EPT>(a, blockIdx.x, threadIdx.x);
 }
 
 template <int CACHE>

@@ -146,73 +146,106 @@ mfa_status mfa_pack_weight(const void* w, void* packed, int N, int K, int dtype,
                                           static_cast<uint16_t*>(packed), N, K, as_stream(stream)));
 }
 
-mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, const void* w_qup,
-                     void* q_out, void* workspace, size_t workspace_bytes, int B, int hidden,
-                     int q_rank, int H, int d, float eps, int dtype, int weight_layout,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// A validated query-path call.
+struct QprojCall {
+  const void *x, *w_qdown, *w_qup;
+  const float* q_norm_w;
+  void* q_out;
+  uint8_t* ws;
+  int B, hidden, q_rank, HD, dtype;
+  bool packed;
+  float eps;
+  QprojPlan p;
+};
+
+mfa_status prepare_qproj(const void* x, const void* w_qdown, const float* q_norm_w,
+                         const void* w_qup, void* q_out, void* workspace, size_t workspace_bytes,
+                         int B, int hidden, int q_rank, int H, int d, float eps, int dtype,
+                         int weight_layout, QprojCall* c) {
   if (!x || !w_qdown || !q_norm_w || !w_qup || !q_out) return MFA_ERR_NULL;
   const mfa_status sh = check_qproj_shape(B, hidden, q_rank, H, d, dtype);
   if (sh != MFA_OK) return sh;
   if (weight_layout != MFA_WEIGHTS_ROWMAJOR && weight_layout != MFA_WEIGHTS_PACKED)
     return MFA_ERR_SHAPE;
   if (weight_layout == MFA_WEIGHTS_PACKED && dtype != MFA_BF16) return MFA_ERR_DTYPE;
-  const bool packed = weight_layout == MFA_WEIGHTS_PACKED;
   if (!aligned16(x) || !aligned16(w_qdown) || !aligned16(q_norm_w) || !aligned16(w_qup) ||
       !aligned16(q_out) || (workspace && !aligned16(workspace)))
     return MFA_ERR_ALIGN;
   if (!(eps >= 0.f)) return MFA_ERR_SHAPE;
-  const int HD = H * d;
-  const QprojPlan p = plan_qproj(B, hidden, q_rank, HD, dtype);
+  c->p = plan_qproj(B, hidden, q_rank, H * d, dtype);
   if (!workspace) return MFA_ERR_WORKSPACE;
-  if (workspace_bytes < p.total) return MFA_ERR_WORKSPACE;
+  if (workspace_bytes < c->p.total) return MFA_ERR_WORKSPACE;
+  c->x = x;
+  c->w_qdown = w_qdown;
+  c->w_qup = w_qup;
+  c->q_norm_w = q_norm_w;
+  c->q_out = q_out;
+  c->ws = static_cast<uint8_t*>(workspace);
+  c->B = B;
+  c->hidden = hidden;
+  c->q_rank = q_rank;
+  c->HD = H * d;
+  c->dtype = dtype;
+  c->packed = weight_layout == MFA_WEIGHTS_PACKED;
+  c->eps = eps;
+  return MFA_OK;
+}
 
-  hipStream_t st = as_stream(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const size_t esz = dtype == MFA_BF16 ? 2 : 4;
-  for (int r0 = 0; r0 < B; r0 += p.rows) {
-    const int M = (B - r0) < p.rows ? (B - r0) : p.rows;
-    const uint8_t* xa = static_cast<const uint8_t*>(x) + static_cast<size_t>(r0) * hidden * esz;
-    uint8_t* qo = static_cast<uint8_t*>(q_out) + static_cast<size_t>(r0) * HD * esz;
+// Enqueues the query path; a single-token KV append (append != nullptr)
+// rides in the first RMSNorm launch.
+mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipStream_t st) {
+  const QprojPlan& p = c.p;
+  const size_t esz = c.dtype == MFA_BF16 ? 2 : 4;
+  for (int r0 = 0; r0 < c.B; r0 += p.rows) {
+    const int M = (c.B - r0) < p.rows ? (c.B - r0) : p.rows;
+    const uint8_t* xa = static_cast<const uint8_t*>(c.x) + static_cast<size_t>(r0) * c.hidden * esz;
+    uint8_t* qo = static_cast<uint8_t*>(c.q_out) + static_cast<size_t>(r0) * c.HD * esz;
     hipError_t e;
-    if (dtype == MFA_BF16) {
-      float* pd = reinterpret_cast<float*>(ws + p.off_part_down);
-      uint16_t* n = reinterpret_cast<uint16_t*>(ws + p.off_n);
+    if (c.dtype == MFA_BF16) {
+      float* pd = reinterpret_cast<float*>(c.ws + p.off_part_down);
+      uint16_t* n = reinterpret_cast<uint16_t*>(c.ws + p.off_n);
       e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
-                                static_cast<const uint16_t*>(w_qdown), pd, nullptr, M, q_rank,
-                                hidden, p.down.ks, p.down.ntiles, packed, st);
+                                static_cast<const uint16_t*>(c.w_qdown), pd, nullptr, M, c.q_rank,
+                                c.hidden, p.down.ks, p.down.ntiles, c.packed, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, q_norm_w, M, q_rank, eps, n, 0, st);
+      e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, c.q_norm_w, M, c.q_rank, c.eps, n, 0,
+                                     r0 == 0 ? append : nullptr, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       if (p.up.ks == 1) {
-        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), nullptr,
-                                  reinterpret_cast<uint16_t*>(qo), M, HD, q_rank, 1, p.up.ntiles,
-                                  packed, st);
+        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(c.w_qup), nullptr,
+                                  reinterpret_cast<uint16_t*>(qo), M, c.HD, c.q_rank, 1,
+                                  p.up.ntiles, c.packed, st);
       } else {
-        float* pu = reinterpret_cast<float*>(ws + p.off_part_up);
-        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(w_qup), pu, nullptr, M, HD,
-                                  q_rank, p.up.ks, p.up.ntiles, packed, st);
+        float* pu = reinterpret_cast<float*>(c.ws + p.off_part_up);
+        e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(c.w_qup), pu, nullptr, M, c.HD,
+                                  c.q_rank, p.up.ks, p.up.ntiles, c.packed, st);
         if (e != hipSuccess) return MFA_ERR_HIP;
-        e = mfa::launch_reduce_cast(pu, p.up.ks, M, HD, qo, 0, st);
+        e = mfa::launch_reduce_cast(pu, p.up.ks, M, c.HD, qo, 0, st);
       }
       if (e != hipSuccess) return MFA_ERR_HIP;
     } else {
-      float* c = reinterpret_cast<float*>(ws + p.off_part_down);
-      float* n = reinterpret_cast<float*>(ws + p.off_n);
+      float* cc = reinterpret_cast<float*>(c.ws + p.off_part_down);
+      float* n = reinterpret_cast<float*>(c.ws + p.off_n);
       e = mfa::launch_gemv_f32(reinterpret_cast<const float*>(xa),
-                               static_cast<const float*>(w_qdown), c, M, q_rank, hidden, st);
+                               static_cast<const float*>(c.w_qdown), cc, M, c.q_rank, c.hidden, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(c, 1, q_norm_w, M, q_rank, eps, n, 1, st);
+      e = mfa::launch_rmsnorm_reduce(cc, 1, c.q_norm_w, M, c.q_rank, c.eps, n, 1,
+                                     r0 == 0 ? append : nullptr, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_gemv_f32(n, static_cast<const float*>(w_qup), reinterpret_cast<float*>(qo),
-                               M, HD, q_rank, st);
+      e = mfa::launch_gemv_f32(n, static_cast<const float*>(c.w_qup), reinterpret_cast<float*>(qo),
+                               M, c.HD, c.q_rank, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
     }
   }
   return MFA_OK;
 }
 
-mfa_status mfa_kv_append(const void* k_new, const void* v_new, int in_dtype, const int32_t* pos,
-                         int n_new, int B, const mfa_kv_cache* cache, void* stream) {
+mfa_status prepare_append(const void* k_new, const void* v_new, int in_dtype, const int32_t* pos,
+                          int n_new, int B, const mfa_kv_cache* cache, mfa::AppendArgs* a) {
   if (!k_new || !v_new || !pos) return MFA_ERR_NULL;
   const mfa_status cs = check_cache(cache);
   if (cs != MFA_OK) return cs;
@@ -225,22 +258,46 @@ mfa_status mfa_kv_append(const void* k_new, const void* v_new, int in_dtype, con
   if (!cache->block_table &&
       static_cast<long long>(B) * cache->max_blocks_per_seq > cache->num_blocks)
     return MFA_ERR_SHAPE;
-  mfa::AppendArgs a{};
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.in_f32 = in_dtype == MFA_F32;
-  a.pos = pos;
-  a.n_new = n_new;
-  a.B = B;
-  a.k = static_cast<uint8_t*>(cache->k);
-  a.v = static_cast<uint8_t*>(cache->v);
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
-  a.block_table = cache->block_table;
-  a.num_blocks = cache->num_blocks;
-  a.max_blocks_per_seq = cache->max_blocks_per_seq;
-  a.d = cache->head_dim;
-  a.cache_dtype = cache->dtype == MFA_F32 ? 0 : (cache->dtype == MFA_BF16 ? 1 : 2);
+  *a = mfa::AppendArgs{};
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->in_f32 = in_dtype == MFA_F32;
+  a->pos = pos;
+  a->n_new = n_new;
+  a->B = B;
+  a->k = static_cast<uint8_t*>(cache->k);
+  a->v = static_cast<uint8_t*>(cache->v);
+  a->k_scale = cache->k_scale;
+  a->v_scale = cache->v_scale;
+  a->block_table = cache->block_table;
+  a->num_blocks = cache->num_blocks;
+  a->max_blocks_per_seq = cache->max_blocks_per_seq;
+  a->d = cache->head_dim;
+  a->cache_dtype = cache->dtype == MFA_F32 ? 0 : (cache->dtype == MFA_BF16 ? 1 : 2);
+  return MFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfa_status mfa_qproj(const void* x, const void* w_qdown, const float* q_norm_w, const void* w_qup,
+                     void* q_out, void* workspace, size_t workspace_bytes, int B, int hidden,
+                     int q_rank, int H, int d, float eps, int dtype, int weight_layout,
+                     void* stream) {
+  QprojCall c{};
+  const mfa_status st = prepare_qproj(x, w_qdown, q_norm_w, w_qup, q_out, workspace,
+                                      workspace_bytes, B, hidden, q_rank, H, d, eps, dtype,
+                                      weight_layout, &c);
+  if (st != MFA_OK) return st;
+  return launch_qproj(c, nullptr, as_stream(stream));
+}
+
+mfa_status mfa_kv_append(const void* k_new, const void* v_new, int in_dtype, const int32_t* pos,
+                         int n_new, int B, const mfa_kv_cache* cache, void* stream) {
+  mfa::AppendArgs a;
+  const mfa_status st = prepare_append(k_new, v_new, in_dtype, pos, n_new, B, cache, &a);
+  if (st != MFA_OK) return st;
   return from_hip(mfa::launch_kv_append(a, as_stream(stream)));
 }
 
@@ -273,10 +330,21 @@ size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits) {
   return round_up(rows * d * 4, 256) + rows * 2 * 4;
 }
 
-mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
-                           const int32_t* seq_lens, int max_seq_len, float sm_scale,
-                           int num_splits, int chunk_tokens, void* workspace,
-                           size_t workspace_bytes, void* out, int out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct AttnCall {
+  mfa::AttnArgs a;
+  bool mfma, fp8;
+  int B, H, d, num_splits;
+  void* out;
+};
+
+mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
+                        const int32_t* seq_lens, int max_seq_len, float sm_scale, int num_splits,
+                        int chunk_tokens, void* workspace, size_t workspace_bytes, void* out,
+                        int out_dtype, AttnCall* c) {
   if (!q || !seq_lens) return MFA_ERR_NULL;
   const mfa_status cs = check_cache(cache);
   if (cs != MFA_OK) return cs;
@@ -295,8 +363,8 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   if (static_cast<long long>(B) * num_splits > 0x7fffffffll) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return MFA_ERR_SHAPE;
-  const bool mfma = mfma_shape(H, d, cache->dtype);
-  if (mfma) {
+  c->mfma = mfma_shape(H, d, cache->dtype);
+  if (c->mfma) {
     if (q_dtype != MFA_BF16) return MFA_ERR_DTYPE;
   } else if (valu_shape(H, d, cache->dtype)) {
     if (q_dtype != MFA_BF16 && q_dtype != MFA_F32) return MFA_ERR_DTYPE;
@@ -310,7 +378,8 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
     if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   }
 
-  mfa::AttnArgs a{};
+  mfa::AttnArgs& a = c->a;
+  a = mfa::AttnArgs{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint8_t*>(cache->k);
   a.v = static_cast<const uint8_t*>(cache->v);
@@ -337,15 +406,71 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   }
   a.out = out;
   a.out_f32 = out_dtype == MFA_F32;
-  hipStream_t st = as_stream(stream);
-  hipError_t e = mfma ? mfa::launch_decode_mfma(a, cache->dtype == MFA_FP8_E4M3, B, st)
-                      : mfa::launch_decode_valu(a, B, st);
+  c->fp8 = cache->dtype == MFA_FP8_E4M3;
+  c->B = B;
+  c->H = H;
+  c->d = d;
+  c->num_splits = num_splits;
+  c->out = out;
+  return MFA_OK;
+}
+
+mfa_status launch_attn(const AttnCall& c, hipStream_t st) {
+  const mfa::AttnArgs& a = c.a;
+  hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st) : mfa::launch_decode_valu(a, c.B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
-  if (num_splits > 1 && out) {
-    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, B, H, d, num_splits, out, a.out_f32, st);
+  if (c.num_splits > 1 && c.out) {
+    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, c.B, c.H, c.d, c.num_splits, c.out,
+                            a.out_f32, st);
     if (e != hipSuccess) return MFA_ERR_HIP;
   }
   return MFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
+                           const int32_t* seq_lens, int max_seq_len, float sm_scale,
+                           int num_splits, int chunk_tokens, void* workspace,
+                           size_t workspace_bytes, void* out, int out_dtype, void* stream) {
+  AttnCall c;
+  const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
+                                     num_splits, chunk_tokens, workspace, workspace_bytes, out,
+                                     out_dtype, &c);
+  if (st != MFA_OK) return st;
+  return launch_attn(c, as_stream(stream));
+}
+
+mfa_status mfa_decode_step(const mfa_step_args* s, void* stream) {
+  if (!s) return MFA_ERR_NULL;
+  const bool has_qproj = s->x != nullptr;
+  QprojCall qc{};
+  if (has_qproj) {
+    const mfa_status st = prepare_qproj(s->x, s->w_qdown, s->q_norm_w, s->w_qup, s->q,
+                                        s->qproj_workspace, s->qproj_workspace_bytes, s->B,
+                                        s->hidden, s->q_rank, s->H, s->d, s->eps, s->dtype,
+                                        s->weight_layout, &qc);
+    if (st != MFA_OK) return st;
+  }
+  mfa::AppendArgs ap;
+  mfa_status st = prepare_append(s->k_new, s->v_new, s->kv_in_dtype, s->pos, 1, s->B, s->cache, &ap);
+  if (st != MFA_OK) return st;
+  AttnCall ac;
+  st = prepare_attn(s->q, s->dtype, s->B, s->H, s->cache, s->seq_lens, s->max_seq_len, s->sm_scale,
+                    s->num_splits, s->chunk_tokens, s->split_workspace, s->split_workspace_bytes,
+                    s->out, s->out_dtype, &ac);
+  if (st != MFA_OK) return st;
+  if (s->cache->head_dim != s->d) return MFA_ERR_SHAPE;
+  hipStream_t hs = as_stream(stream);
+  if (has_qproj) {
+    st = launch_qproj(qc, &ap, hs);            // the append rides in the RMSNorm launch
+    if (st != MFA_OK) return st;
+  } else if (mfa::launch_kv_append(ap, hs) != hipSuccess) {
+    return MFA_ERR_HIP;
+  }
+  return launch_attn(ac, hs);
 }
 
 mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int H, int d,

@@ -13,6 +13,7 @@
 // splits K across workgroups when the output alone cannot fill the chip,
 // and leaves fp32 partials that the RMSNorm pass sums (down product) or
 // writes bf16 directly (up product, one K slice).
+#include "append_one.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -157,14 +158,27 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
 
 // c[m][:] = sum of the K-slice partials; n = c / sqrt(mean(c^2) + eps) * g.
 // One workgroup per row; each thread owns 8 consecutive columns per 2048.
+// With APPEND, workgroups M.. of the grid write the decode step's new KV
+// tokens instead (wave w of workgroup M + j appends sequences 4j + w,
+// 4j + w + 4*(gridDim.x - M), ...): the two small, latency-bound jobs share
+// one launch and their memory latencies overlap.
+template <bool APPEND>
 __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __restrict__ part,
                                                              int ksplit, const float* __restrict__ g,
                                                              int M, int R, float eps, void* out,
-                                                             int out_f32) {
+                                                             int out_f32, AppendArgs app) {
   constexpr int kMaxChunks = 4;        // R <= 8192 = 4 chunks of 2048
   __shared__ float wsum[4];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
+  if constexpr (APPEND) {
+    if (m >= M) {
+      const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int per = (gridDim.x - M) * 4;
+      for (int b = (m - M) * 4 + w; b < app.B; b += per) append_token(app, b, tid & 63);
+      return;
+    }
+  }
   float cv[kMaxChunks][8];
   float ss = 0.f;
 #pragma unroll
@@ -254,27 +268,34 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
   if (lane == 0) out[static_cast<size_t>(m) * N + n] = acc;
 }
 
+template <int MT, int NT, int PD, bool PACKED>
+static void launch_gemm_shape(dim3 grid, const uint16_t* A, const uint16_t* W, float* part,
+                              uint16_t* out_bf16, int M, int N, int K, int kchunk,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED>), grid, dim3(kGemmWaves * 64), 0,
+                     stream, A, W, part, out_bf16, M, N, K, kchunk);
+}
+
 template <bool PACKED>
 static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                                 int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
   const int kchunk = K / ksplit;
-  dim3 block(kGemmWaves * 64);
   if (ntiles == 4) {
     dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<1, 4, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<2, 4, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, 4, 3, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<4, 4, 3, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
   } else {
     dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, 8, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<1, 2, 8, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 6, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<2, 2, 6, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, 2, 4, PACKED>), grid, block, 0, stream, A, W, part, out_bf16, M, N, K, kchunk);
+      launch_gemm_shape<4, 2, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
   }
 }
 
@@ -310,9 +331,16 @@ hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipS
 }
 
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
-                                 float eps, void* out, int out_f32, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_reduce_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream,
-                     part, ksplit, g, M, R, eps, out, out_f32);
+                                 float eps, void* out, int out_f32, const AppendArgs* append,
+                                 hipStream_t stream) {
+  if (append) {
+    const int extra = (append->B + 3) / 4 < 16 ? (append->B + 3) / 4 : 16;
+    hipLaunchKernelGGL(rmsnorm_reduce_kernel<true>, dim3(static_cast<unsigned>(M + extra)),
+                       dim3(256), 0, stream, part, ksplit, g, M, R, eps, out, out_f32, *append);
+  } else {
+    hipLaunchKernelGGL(rmsnorm_reduce_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(256), 0,
+                       stream, part, ksplit, g, M, R, eps, out, out_f32, AppendArgs{});
+  }
   return hipGetLastError();
 }
 

@@ -82,7 +82,50 @@ class DecodeStep:
                                workspace=self.split_ws)
 
     def __call__(self, k_new, v_new, pos, seq_lens, x=None, weights=None, q=None):
-        """q from x and weights=(w_qdown, g, w_qup) (or given), append, attend."""
+        """q from x and weights=(w_qdown, g, w_qup) (or given), append, attend,
+        as one mfa_decode_step call (the library shares launches between the
+        stages). Returns ``out``."""
+        args = _lib.StepArgs()
+        args.B, args.H, args.d = self.B, self.H, self.d
+        args.dtype = api._DTYPES[self.act_dtype]
+        if q is None:
+            w_qdown, g, w_qup = weights
+            for t, n in ((x, "x"), (w_qdown, "w_qdown"), (g, "g"), (w_qup, "w_qup")):
+                api._dev(t, n)
+            args.x, args.w_qdown, args.w_qup = x.data_ptr(), w_qdown.data_ptr(), w_qup.data_ptr()
+            args.q_norm_w = g.data_ptr()
+            args.hidden, args.q_rank = self.hidden, self.q_rank
+            args.weight_layout = (api.MFA_WEIGHTS_PACKED if self.packed_weights
+                                  else api.MFA_WEIGHTS_ROWMAJOR)
+            args.eps = self.eps
+            args.qproj_workspace = self.qproj_ws.data_ptr()
+            args.qproj_workspace_bytes = self.qproj_ws.numel()
+            q = self.q
+        for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (pos, "pos"),
+                     (seq_lens, "seq_lens")):
+            api._dev(t, n)
+        if pos.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+            raise ValueError("pos and seq_lens must be int32")
+        args.q = q.data_ptr()
+        args.k_new, args.v_new = k_new.data_ptr(), v_new.data_ptr()
+        args.kv_in_dtype = api._DTYPES[k_new.dtype]
+        args.pos = pos.data_ptr()
+        args.cache = ctypes.pointer(self._desc)
+        args.seq_lens = seq_lens.data_ptr()
+        args.max_seq_len = self.max_seq_len
+        args.sm_scale = self.sm_scale
+        args.num_splits, args.chunk_tokens = self.num_splits, self.chunk_tokens
+        if self.split_ws is not None:
+            args.split_workspace = self.split_ws.data_ptr()
+            args.split_workspace_bytes = self.split_ws.numel()
+        args.out = self.out.data_ptr()
+        args.out_dtype = api._DTYPES[self.out_dtype]
+        api.decode_step(args, self.out.device)
+        return self.out
+
+    def staged(self, k_new, v_new, pos, seq_lens, x=None, weights=None, q=None):
+        """The same step as four separate calls (mfa_qproj, mfa_kv_append,
+        mfa_decode_attn, mfa_combine)."""
         if q is None:
             q = self.query(x, *weights)
         self.append(k_new, v_new, pos)

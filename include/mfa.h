@@ -247,6 +247,52 @@ mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
                        int H, int d, int num_splits, void *out, int out_dtype,
                        void *stream);
 
+/*
+ * One whole decode step on one stream, equal to
+ *   mfa_qproj (when x != NULL) -> mfa_kv_append (one token per sequence)
+ *   -> mfa_decode_attn (with out: attention and split combine)
+ * with the same arguments, in that order, and with the same results.
+ * It exists so the stages can share launches: with a query path, the KV
+ * append runs inside the query path's normalisation launch instead of on
+ * its own.
+ * Every stage's arguments are checked (as by the separate calls) before
+ * anything is launched.
+ *   B, H, d      batch, query heads, head dim (d must equal cache->head_dim)
+ *   dtype        MFA_BF16 or MFA_F32: x, weights and q (as in mfa_qproj and
+ *                the q_dtype of mfa_decode_attn)
+ *   x ... q_rank, eps, weight_layout, qproj_workspace(_bytes): as in
+ *                mfa_qproj; x == NULL skips the query path and q is an input
+ *   q            [B][H][d] device: written by the query path, read by the
+ *                attention
+ *   k_new, v_new [B][d] of kv_in_dtype; pos [B] int32: as in mfa_kv_append
+ *                with n_new == 1
+ *   cache ... out_dtype: as in mfa_decode_attn
+ */
+typedef struct {
+  int B, H, d, dtype;
+  const void *x, *w_qdown, *w_qup;
+  const float *q_norm_w;
+  int hidden, q_rank, weight_layout;
+  float eps;
+  void *qproj_workspace;
+  size_t qproj_workspace_bytes;
+  void *q;
+  const void *k_new, *v_new;
+  int kv_in_dtype;
+  const int32_t *pos;
+  const mfa_kv_cache *cache;
+  const int32_t *seq_lens;
+  int max_seq_len;
+  float sm_scale;
+  int num_splits, chunk_tokens;
+  void *split_workspace;
+  size_t split_workspace_bytes;
+  void *out;
+  int out_dtype;
+} mfa_step_args;
+
+mfa_status mfa_decode_step(const mfa_step_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,3 +145,59 @@ def test_plan_and_split_workspace(lib):
     assert lib.mfa_combine(None, 0, 4, 64, 256, 32, P, BF16, None) == NULL
     assert lib.mfa_combine(P, 16, 4, 64, 256, 32, P, BF16, None) == WS
     assert lib.mfa_combine(P, 1 << 30, 4, 64, 256, 1, P, BF16, None) == SHAPE
+
+
+def _c_layout(struct, fields):
+    """sizeof and offsetof of a struct of mfa.h, from a C program built by gcc."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    body = "".join(f'  printf("%zu\\n", offsetof({struct}, {f}));\n' for f in fields)
+    src = ("#include <stdio.h>\n#include <stddef.h>\n#include \"mfa.h\"\nint main(void) {\n"
+           f'  printf("%zu\\n", sizeof({struct}));\n{body}  return 0;\n}}\n')
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        with open(c, "w") as f:
+            f.write(src)
+        subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), "-o", exe, c])
+        return [int(v) for v in subprocess.check_output([exe]).split()]
+
+
+@pytest.mark.parametrize("struct,mirror", [("mfa_kv_cache", _lib.KVCacheDesc),
+                                            ("mfa_step_args", _lib.StepArgs)])
+def test_struct_layout_matches_header(struct, mirror):
+    names = [f[0] for f in mirror._fields_]
+    got = _c_layout(struct, names)
+    assert got[0] == ctypes.sizeof(mirror)
+    for n, off in zip(names, got[1:]):
+        assert getattr(mirror, n).offset == off, n
+
+
+def test_decode_step_validation(lib):
+    assert lib.mfa_decode_step(None, None) == NULL
+    c = _cache()
+    a = _lib.StepArgs()
+    a.B, a.H, a.d, a.dtype = 4, 64, 256, BF16
+    a.q, a.k_new, a.v_new, a.kv_in_dtype, a.pos = P, P, P, BF16, P
+    a.cache = ctypes.pointer(c)
+    a.seq_lens, a.max_seq_len, a.sm_scale = P, 512, 0.0625
+    a.num_splits, a.chunk_tokens = 1, 512
+    a.out, a.out_dtype = P, BF16
+    ok = lambda: lib.mfa_decode_step(ctypes.byref(a), None)
+    a.k_new = None
+    assert ok() == NULL                                          # append arguments checked
+    a.k_new = P
+    a.sm_scale = -1.0
+    assert ok() == SHAPE                                         # attention arguments checked
+    a.sm_scale = 0.0625
+    a.d = 128
+    assert ok() == SHAPE                                         # d must be the cache's
+    a.d = 256
+    a.x, a.w_qdown, a.w_qup, a.q_norm_w = P, P, P, P
+    a.hidden, a.q_rank = 7000, 2048
+    assert ok() == SHAPE                                         # query-path arguments checked
+    a.hidden = 7168
+    a.qproj_workspace, a.qproj_workspace_bytes = None, 0
+    assert ok() == WS

@@ -310,6 +310,36 @@ def test_graph_replay_matches_eager(gpu_lib):
     check_bf16(to_np(eager), orun.decode_step(inp)["o"], "graph step")
 
 
+@pytest.mark.parametrize("idx,shrink", [(2, dict(batch=6, hidden=1024, q_rank=512, context=300)),
+                                        (4, dict(batch=3, context=400)),
+                                        (1, {})])
+def test_fused_step_matches_staged(gpu_lib, idx, shrink):
+    """mfa_decode_step (KV append inside the query down-projection launch on
+    the bf16 path) gives bit-identical outputs and cache contents to the four
+    separate calls."""
+    w = dataclasses.replace(W[idx], **shrink)
+    inp = workloads.make_inputs(idx, workload=w, seed=26)
+    say(f"fused vs staged: {w.name} {shrink}")
+    outs, caches = [], []
+    for mode in ("fused", "staged"):
+        T, cache, step = setup(inp, num_splits=3 if w.context and w.context > 256 else None)
+        fn = step if mode == "fused" else step.staged
+        if w.has_qproj:
+            out = fn(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"],
+                     weights=(T["w_qdown"], T["g"], T["w_qup"]))
+        else:
+            out = fn(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+        torch.cuda.synchronize()
+        outs.append(out.detach().cpu().clone())
+        rows = list(cache_rows(cache))
+        if cache.dtype == "fp8":
+            rows += [cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()]
+        caches.append(rows)
+    assert torch.equal(outs[0].view(torch.uint8), outs[1].view(torch.uint8))
+    for a, b in zip(*caches):
+        assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

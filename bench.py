@@ -262,7 +262,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (traffic / (attn_avg * 1e-3) / 1e9) if traffic else None,
-                     "kernel": "mfa_decode_mfma_kernel", "kernel_avg_us": attn_avg * 1e3,
+                     "traffic_bytes_per_launch": traffic,
+                     "kernel": ("mfa_decode_mfma_kernel"
+                                if (w.heads == 64 and w.head_dim == 256 and w.kv_dtype != "f32")
+                                else "mfa_decode_valu_kernel"),
+                     "kernel_avg_us": attn_avg * 1e3,
                      "algorithmic_bytes_per_launch": kv_bytes},
         "step_kv_plus_weights_GBps": (kv_bytes + w_bytes) / (ms * 1e-3) / 1e9,
     }

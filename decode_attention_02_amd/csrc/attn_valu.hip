@@ -3,7 +3,7 @@
 // and for fp32 caches. All arithmetic is fp32. Same semantics as the
 // matrix-core kernel: all H heads attend to the one shared K/V head
 // ("Step-3 is Large yet Affordable" summary page, §2 and §5), online softmax
-// over 8-token tiles, natural exp.
+// over 16- or 32-token tiles, natural exp.
 #include "device_common.h"
 #include "kernels.h"
 #include "kv_layout.h"
@@ -11,17 +11,19 @@
 namespace mfa {
 
 namespace {
-constexpr int kT = 8;            // tokens per tile
 constexpr int kMaxHD = 8192;     // H*d limit (q staged in LDS)
 constexpr int kMaxPerThread = kMaxHD / 256;
 }
 
-template <int D>
+// KT tokens per tile; the next tile's K and V are loaded into registers
+// while the current one is computed.
+template <int D, int KT>
 __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
+  constexpr int kPer = KT * D / 256;           // K (and V) elements per thread per tile
   __shared__ float q_s[kMaxHD];
-  __shared__ float k_s[kT][D];
-  __shared__ float v_s[kT][D];
-  __shared__ float p_s[64][kT];
+  __shared__ float k_s[KT][D];
+  __shared__ float v_s[KT][D];
+  __shared__ float p_s[64][KT];
   __shared__ float alpha_s[64], m_s[64], l_s[64];
 
   const int H = a.heads;
@@ -44,11 +46,12 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
   for (int r = 0; r < kMaxPerThread; ++r) o[r] = 0.f;
   const int* bt_row = a.block_table ? a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
                                     : nullptr;
-  __syncthreads();
-
-  for (int tt = t0; tt < t1; tt += kT) {
-    const int n = min(kT, t1 - tt);
-    for (int i = tid; i < kT * D; i += 256) {
+  float kr[kPer], vr[kPer];
+  auto load_tile = [&](int tt) {               // element i = tid + 256 r: token i / D, dim i % D
+    const int n = min(KT, t1 - tt);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + 256 * r;
       const int t = i / D, j = i % D;
       float kv = 0.f, vv = 0.f;
       if (t < n) {
@@ -68,12 +71,25 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
           vv = bf16_to_f32(*reinterpret_cast<const uint16_t*>(vb + v_off_bf16(off, j)));
         }
       }
-      k_s[t][j] = kv;
-      v_s[t][j] = vv;
+      kr[r] = kv;
+      vr[r] = vv;
+    }
+  };
+  if (t0 < t1) load_tile(t0);
+  __syncthreads();
+
+  for (int tt = t0; tt < t1; tt += KT) {
+    const int n = min(KT, t1 - tt);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + 256 * r;
+      k_s[i / D][i % D] = kr[r];
+      v_s[i / D][i % D] = vr[r];
     }
     __syncthreads();
-    for (int i = tid; i < H * kT; i += 256) {
-      const int h = i / kT, t = i % kT;
+    if (tt + KT < t1) load_tile(tt + KT);       // in flight during this tile
+    for (int i = tid; i < H * KT; i += 256) {
+      const int h = i / KT, t = i % KT;
       float s = -INFINITY;
       if (t < n) {
         float acc = 0.f;
@@ -89,7 +105,7 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
       for (int t = 0; t < n; ++t) mx = fmaxf(mx, p_s[h][t]);
       const float al = expf(m_s[h] - mx);
       float sum = 0.f;
-      for (int t = 0; t < kT; ++t) {
+      for (int t = 0; t < KT; ++t) {
         const float p = t < n ? expf(p_s[h][t] - mx) : 0.f;
         p_s[h][t] = p;
         sum += p;
@@ -145,9 +161,9 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(B * a.num_splits)), block(256);
   switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL(mfa_decode_valu_kernel<64>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(mfa_decode_valu_kernel<128>, grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(mfa_decode_valu_kernel<256>, grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((mfa_decode_valu_kernel<64, 32>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((mfa_decode_valu_kernel<128, 32>), grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((mfa_decode_valu_kernel<256, 16>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

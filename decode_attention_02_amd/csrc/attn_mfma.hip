@@ -94,16 +94,20 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 }  // namespace
 
 // RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
-template <bool FP8, int RK, int RV>
+// HT: 16-head tiles per workgroup (4: all 64 heads; 2: half of them, two
+// workgroups per (sequence, split) reading the same K/V blocks).
+template <bool FP8, int RK, int RV, int HT>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   using C = Cfg<FP8>;
-  __shared__ __attribute__((aligned(16))) uint4 q_lds[4 * 8 * 64];      // 32 KB, operand order
-  __shared__ __attribute__((aligned(16))) uint4 p_lds[2][4 * 2 * 64];   // 2 x 8 KB, operand order
-  __shared__ __attribute__((aligned(16))) float red[2][kH * 4];         // block max [head][QK wave]
-  __shared__ __attribute__((aligned(16))) float alpha_lds[2][kH];
+  constexpr int kHW = 16 * HT;                                          // heads of this workgroup
+  constexpr int kHS = kH / kHW;                                         // workgroups per split
+  __shared__ __attribute__((aligned(16))) uint4 q_lds[HT * 8 * 64];     // HT x 8 KB, operand order
+  __shared__ __attribute__((aligned(16))) uint4 p_lds[2][HT * 2 * 64];  // 2 x HT x 2 KB, operand order
+  __shared__ __attribute__((aligned(16))) float red[2][kHW * 4];        // block max [head][QK wave]
+  __shared__ __attribute__((aligned(16))) float alpha_lds[2][kHW];
   __shared__ int flag_lds[2];
-  __shared__ __attribute__((aligned(16))) float lred[kH * 4];           // row sums [head][QK wave]
-  __shared__ float m_lds[kH];
+  __shared__ __attribute__((aligned(16))) float lred[kHW * 4];          // row sums [head][QK wave]
+  __shared__ float m_lds[kHW];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: the role branches below are uniform per wave
@@ -112,12 +116,16 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int ww = w & 3;                 // QK: token group; PV: feature group of 64
 
   // Workgroups are dispatched round-robin over the 8 XCDs (id % 8). Remap so
-  // that each XCD runs a contiguous range of (sequence, split) pairs: the
-  // splits of one sequence then share one L2 for their query reads.
+  // that each XCD runs a contiguous range of (sequence, split, head group)
+  // triples: the head groups of a split then read the same K/V blocks
+  // through one L2 at about the same time, and the splits of a sequence
+  // share that L2 for their query reads.
   int id = blockIdx.x;
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-  const int split = id % a.num_splits;
-  const int b = id / a.num_splits;
+  const int hg = id % kHS;
+  const int split = (id / kHS) % a.num_splits;
+  const int b = id / kHS / a.num_splits;
+  const int h0 = hg * kHW;                                              // first head
 
   int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[b];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
@@ -126,10 +134,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int blk0 = t0 >> 6;
   const int N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;   // blocks to walk
 
-  // Q rows of this sequence -> LDS in operand order: block (ht, s), lane
-  // (gg, cc) holds Q[ht*16+cc][qk_dim(s, gg) .. +8]. Each role loads them
-  // between the first ring block and the rest, so staging Q waits for Q and
-  // block 0 only.
+  // Q rows of the workgroup's heads -> LDS in operand order: block (ht, s),
+  // lane (gg, cc) holds Q[h0+ht*16+cc][qk_dim(s, gg) .. +8]. Each role loads
+  // them between the first ring block and the rest, so staging Q waits for Q
+  // and block 0 only.
   uint4 qv0, qv1, qv2, qv3;
   auto q_src = [&](int r) __attribute__((always_inline)) -> const uint4* {
     const int idx = tid + 512 * r;
@@ -137,13 +145,15 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     const int ht = blk >> 3, s = blk & 7;
     const int gg = ln >> 4, cc = ln & 15;
     return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
-                                          (ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
+                                          (h0 + ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
   };
-  auto load_q = [&]() __attribute__((always_inline)) {
-    qv0 = *q_src(0); qv1 = *q_src(1); qv2 = *q_src(2); qv3 = *q_src(3);
+  auto load_q = [&]() __attribute__((always_inline)) {             // HT loads per thread
+    qv0 = *q_src(0); qv1 = *q_src(1);
+    if constexpr (HT == 4) { qv2 = *q_src(2); qv3 = *q_src(3); }
   };
   auto store_q = [&]() __attribute__((always_inline)) {
-    q_lds[tid] = qv0; q_lds[tid + 512] = qv1; q_lds[tid + 1024] = qv2; q_lds[tid + 1536] = qv3;
+    q_lds[tid] = qv0; q_lds[tid + 512] = qv1;
+    if constexpr (HT == 4) { q_lds[tid + 1024] = qv2; q_lds[tid + 1536] = qv3; }
   };
   // prologue of either role: ring blocks 0 .. R-1 and Q, then Q -> LDS. The
   // QK waves need K block 0 with Q and load it first; the PV waves load Q
@@ -185,12 +195,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // ================= QK waves: S = K.Q^T, online softmax, P^T -> LDS
     constexpr int R = RK;
     constexpr int U = unroll_for(RK);
-    float m_run[4], l_run[4];            // per head 16ht + c, log2 units of scaled logits
+    float m_run[HT], l_run[HT];          // per head h0 + 16ht + c, log2 units of scaled logits
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
+    for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
     const float cl2 = a.scale_log2;      // > 0
     uint4 ring[R][C::kSlot];             // K units of 16 tokens (+ FP8 K, V scales)
-    f32x4_t sb[2][4];                    // raw logits of the last two blocks, by parity
+    f32x4_t sb[2][HT];                   // raw logits of the last two blocks, by parity
     uint4 vkeep[2];                      // FP8: V scales of the last two blocks, by parity
     vkeep[0] = vkeep[1] = make_uint4(0u, 0u, 0u, 0u);
     // Loads block n into a ring slot; n >= N (past the walk) issues the same
@@ -219,13 +229,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         ring[slot][5] = buf_load16(rvs, so);
       }
     };
-    // S^T of block n (16 tokens x 64 heads of this wave) -> sb[par], block max -> red
+    // S^T of block n (16 tokens x kHW heads of this wave) -> sb[par], block max -> red
     auto scores = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int par = decltype(par_c)::value;
-      f32x4_t s_acc[4];
+      f32x4_t s_acc[HT];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HT; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       static_for<0, 8>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         bf16x8_t kop;
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
           kop = as_bf16x8(ring[slot][s]);
         }
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
           s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
       });
       if constexpr (FP8) {
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
                              __uint_as_float(k4.w)};
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s_acc[ht][e] *= ks[e];
         vkeep[par] = ring[slot][5];   // the slot is refilled below
@@ -253,12 +263,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
         const int tt0 = 16 * ww + 4 * g;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s_acc[ht][e] = (tt0 + e < lim) ? s_acc[ht][e] : -INFINITY;
       }
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int ht = 0; ht < HT; ++ht) {
         float m = fmaxf(fmaxf(s_acc[ht][0], s_acc[ht][1]), fmaxf(s_acc[ht][2], s_acc[ht][3]));
         m = rows4_max(m);
         if (g == 0) red[par][(ht * 16 + c) * 4 + ww] = m;
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
       bool rescale = false;
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int ht = 0; ht < HT; ++ht) {
         const float4 r4 = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
         // block max over all 64 tokens (finite: every walked block has a valid token)
         const float tz = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)) * cl2;
@@ -359,7 +369,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 
     // row sums -> LDS for the PV waves
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
+    for (int ht = 0; ht < HT; ++ht) {
       const float l = rows4_sum(l_run[ht]);
       if (g == 0) lred[(ht * 16 + c) * 4 + ww] = l;
       if (ww == 0 && g == 0) m_lds[ht * 16 + c] = m_run[ht];
@@ -370,11 +380,11 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     constexpr int R = RV;
     constexpr int U = unroll_for(RV);
     // acc[dt][ht]: lane holds O^T[64ww + 16dt + 4g + i][16ht + c]
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][HT];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HT; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     uint4 ring[R][C::kLoads];
     auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {   // as for K
       constexpr int slot = decltype(slot_c)::value;
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       constexpr int par = decltype(par_c)::value;
       if (flag_lds[par]) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < HT; ++ht) {
           const float al = alpha_lds[par][ht * 16 + c];
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) acc[dt][ht] *= al;
@@ -429,9 +439,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
       static_for<0, 2>([&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
-        bf16x8_t pop[4];
+        bf16x8_t pop[HT];
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) pop[ht] = as_bf16x8(p_lds[par][(ht * 2 + ks) * 64 + lane]);
+        for (int ht = 0; ht < HT; ++ht) pop[ht] = as_bf16x8(p_lds[par][(ht * 2 + ks) * 64 + lane]);
         static_for<0, 4>([&](auto dtc) {
           constexpr int dt = decltype(dtc)::value;
           bf16x8_t vop;
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
             vop = as_bf16x8(ring[slot][dt * 2 + ks]);
           }
 #pragma unroll
-          for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = mfma_16x16x32(vop, pop[ht], acc[dt][ht]);
+          for (int ht = 0; ht < HT; ++ht) acc[dt][ht] = mfma_16x16x32(vop, pop[ht], acc[dt][ht]);
         });
       });
     };
@@ -475,18 +485,18 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     });
 
     __syncthreads();   // row sums staged
-    float lsum[4], mh[4];
+    float lsum[HT], mh[HT];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
+    for (int ht = 0; ht < HT; ++ht) {
       const float4 r4 = reinterpret_cast<const float4*>(lred)[ht * 16 + c];
       lsum[ht] = (r4.x + r4.y) + (r4.z + r4.w);
       mh[ht] = m_lds[ht * 16 + c];
     }
     if (a.num_splits == 1) {
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int ht = 0; ht < HT; ++ht) {
         const float inv = lsum[ht] > 0.f ? 1.0f / lsum[ht] : 0.f;
-        const int head = ht * 16 + c;
+        const int head = h0 + ht * 16 + c;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int f = 64 * ww + 16 * dt + 4 * g;
@@ -508,8 +518,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       // no weight and never uses its o
       const size_t row = static_cast<size_t>(b) * a.num_splits + split;
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const int head = ht * 16 + c;
+      for (int ht = 0; ht < HT; ++ht) {
+        const int head = h0 + ht * 16 + c;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           if (N == 0) break;
@@ -538,11 +548,20 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(B * a.num_splits)), block(512);
-  if (fp8)
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 2, 3>), grid, block, 0, stream, a);
+  // Two head groups per (sequence, split) while the grid stays within one
+  // workgroup per compute unit (256), and only when the XCD remap keeps both
+  // groups of a split on one XCD (pairs a multiple of 8): they then read the
+  // K/V blocks once from HBM and twice from that XCD's L2.
+  const long long pairs = static_cast<long long>(B) * a.num_splits;
+  const bool half = pairs * 2 <= 256 && pairs % 8 == 0;
+  const dim3 grid(static_cast<unsigned>(pairs * (half ? 2 : 1))), block(512);
+  if (fp8) {
+    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4>), grid, block, 0, stream, a);
+  } else {
+    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 4, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 2, 3, 4>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -37,6 +37,9 @@ SMALL = [
     ("bf16-paged", 3, dict(), [1, 62, 63, 64, 65, 127, 300, 777]),
     ("fp8-paged", 4, dict(), [0, 63, 64, 190, 513]),
     ("fp8-contig", 4, dict(paged=False), [255, 70, 3]),
+    # 8 sequences: batch x splits is a multiple of 8, which runs the
+    # two-head-group attention launch (as do the 8 bf16-paged sequences)
+    ("fp8-paged-8", 4, dict(), [0, 1, 63, 64, 65, 190, 513, 1000]),
 ]
 
 

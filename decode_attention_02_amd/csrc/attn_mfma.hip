@@ -269,7 +269,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        float m = fmaxf(fmaxf(s_acc[ht][0], s_acc[ht][1]), fmaxf(s_acc[ht][2], s_acc[ht][3]));
+        float m = max_nonan(max3_nonan(s_acc[ht][0], s_acc[ht][1], s_acc[ht][2]), s_acc[ht][3]);
         m = rows4_max(m);
         if (g == 0) red[par][(ht * 16 + c) * 4 + ww] = m;
         sb[par][ht] = s_acc[ht];
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       for (int ht = 0; ht < HT; ++ht) {
         const float4 r4 = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
         // block max over all 64 tokens (finite: every walked block has a valid token)
-        const float tz = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)) * cl2;
+        const float tz = max_nonan(max3_nonan(r4.x, r4.y, r4.z), r4.w) * cl2;
         float alpha = 1.0f;
         if (tz > m_run[ht] + kLazy) {          // also true for the first block
           alpha = __builtin_amdgcn_exp2f(m_run[ht] - tz);

@@ -89,13 +89,29 @@ __device__ __forceinline__ uint32_t encode_e4m3_rne(float y) {
 // Max / sum over the four 16-lane rows of a wave: lane c of every row gets
 // the result for column c (rows are swapped pairwise by the gfx950 permlane
 // swaps, so no LDS round trip is involved).
+// Maximum of non-NaN floats (finite or infinite) as one v_max_f32 / v_max3_f32.
+// fmaxf must quiet signalling NaNs first, which costs one extra
+// instruction per operand the compiler cannot prove canonical (every matrix-
+// core result and LDS value); the callers below never hold NaNs.
+__device__ __forceinline__ float max_nonan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nonan(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Max over the 4 lanes l, l^16, l^32, l^48 (non-NaN inputs).
 __device__ __forceinline__ float rows4_max(float v) {
   const int iv = __float_as_int(v);
   auto p = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
-  v = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  v = max_nonan(__int_as_float(p[0]), __int_as_float(p[1]));
   const int iw = __float_as_int(v);
   auto q = __builtin_amdgcn_permlane32_swap(iw, iw, false, false);
-  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+  return max_nonan(__int_as_float(q[0]), __int_as_float(q[1]));
 }
 
 __device__ __forceinline__ float rows4_sum(float v) {

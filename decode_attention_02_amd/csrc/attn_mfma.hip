@@ -236,8 +236,23 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       f32x4_t s_acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // bf16: the Q operands of k-step s+1 are read from LDS while step s
+      // multiplies (FP8 has no registers to spare for that; its operand
+      // conversions fill the gaps instead)
+      constexpr bool kQdb = !FP8;
+      bf16x8_t qop[2][HT];
+      if constexpr (kQdb) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) qop[0][ht] = as_bf16x8(q_lds[(ht * 8) * 64 + lane]);
+      }
       static_for<0, 8>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
+        if constexpr (kQdb && s + 1 < 8) {
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            qop[(s + 1) & 1][ht] = as_bf16x8(q_lds[(ht * 8 + s + 1) * 64 + lane]);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's products
+        }
         bf16x8_t kop;
         if constexpr (FP8) {
           const uint4 u = ring[slot][s >> 1];
@@ -246,8 +261,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
           kop = as_bf16x8(ring[slot][s]);
         }
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
+        for (int ht = 0; ht < HT; ++ht) {
+          if constexpr (kQdb) s_acc[ht] = mfma_16x16x32(kop, qop[s & 1][ht], s_acc[ht]);
+          else s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
+        }
       });
       if constexpr (FP8) {
         const uint4 k4 = ring[slot][4];
@@ -267,12 +284,18 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) s_acc[ht][e] = (tt0 + e < lim) ? s_acc[ht][e] : -INFINITY;
       }
+      // per-head max over the wave's 16 tokens; lane row g ends with the max
+      // of tile g (HT 4) or g/2 (HT 2), so one store per lane covers them all
+      float mt[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        float m = max_nonan(max3_nonan(s_acc[ht][0], s_acc[ht][1], s_acc[ht][2]), s_acc[ht][3]);
-        m = rows4_max(m);
-        if (g == 0) red[par][(ht * 16 + c) * 4 + ww] = m;
+        mt[ht] = max_nonan(max3_nonan(s_acc[ht][0], s_acc[ht][1], s_acc[ht][2]), s_acc[ht][3]);
         sb[par][ht] = s_acc[ht];
+      }
+      if constexpr (HT == 4) {
+        red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
+      } else {
+        red[par][((g >> 1) * 16 + c) * 4 + ww] = rows4_max_t2(mt[0], mt[1]);
       }
     };
     // softmax of block n (its logits in sb[par]): P^T -> p_lds[par], rescale factors
@@ -285,14 +308,17 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         vs[2] = __uint_as_float(v4.z); vs[3] = __uint_as_float(v4.w);
       }
       bool rescale = false;
+      float4 r4[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) r4[ht] = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
+      float alpha[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const float4 r4 = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
         // block max over all 64 tokens (finite: every walked block has a valid token)
-        const float tz = max_nonan(max3_nonan(r4.x, r4.y, r4.z), r4.w) * cl2;
-        float alpha = 1.0f;
+        const float tz = max_nonan(max3_nonan(r4[ht].x, r4[ht].y, r4[ht].z), r4[ht].w) * cl2;
+        alpha[ht] = 1.0f;
         if (tz > m_run[ht] + kLazy) {          // also true for the first block
-          alpha = __builtin_amdgcn_exp2f(m_run[ht] - tz);
+          alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - tz);
           m_run[ht] = tz;
           rescale = true;
         }
@@ -300,12 +326,11 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[par][ht][e], cl2, nm));
-        l_run[ht] = l_run[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        l_run[ht] = l_run[ht] * alpha[ht] + ((p[0] + p[1]) + (p[2] + p[3]));
         if constexpr (FP8) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) p[e] *= vs[e];
         }
-        if (ww == 0 && g == 0) alpha_lds[par][ht * 16 + c] = alpha;
         // P^T into operand block (ht, ks) of buffer par
         int ks, gr;
         if constexpr (FP8) { ks = g >> 1; gr = ww; }
@@ -317,7 +342,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
                        ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
         *reinterpret_cast<uint2*>(dst) = pk;
       }
-      if (ww == 0) {
+      if (ww == 0) {   // rescale factors: lane row g stores tile g (HT 4) or g/2 (HT 2)
+        if constexpr (HT == 4) {
+          const float al = g == 0 ? alpha[0] : g == 1 ? alpha[1] : g == 2 ? alpha[2] : alpha[3];
+          alpha_lds[par][g * 16 + c] = al;
+        } else {
+          alpha_lds[par][(g >> 1) * 16 + c] = g < 2 ? alpha[0] : alpha[1];
+        }
         const bool any = __ballot(rescale) != 0ull;
         if (lane == 0) flag_lds[par] = any ? 1 : 0;
       }

@@ -86,9 +86,6 @@ __device__ __forceinline__ uint32_t encode_e4m3_rne(float y) {
   return code | sign;
 }
 
-// Max / sum over the four 16-lane rows of a wave: lane c of every row gets
-// the result for column c (rows are swapped pairwise by the gfx950 permlane
-// swaps, so no LDS round trip is involved).
 // Maximum of non-NaN floats (finite or infinite) as one v_max_f32 / v_max3_f32.
 // fmaxf must quiet signalling NaNs first, which costs one extra
 // instruction per operand the compiler cannot prove canonical (every matrix-
@@ -104,7 +101,9 @@ __device__ __forceinline__ float max3_nonan(float a, float b, float c) {
   return r;
 }
 
-// Max over the 4 lanes l, l^16, l^32, l^48 (non-NaN inputs).
+// Max / sum over the four 16-lane rows of a wave: lane c of every row gets
+// the result for column c (rows are swapped pairwise by the gfx950 permlane
+// swaps, so no LDS round trip is involved). rows4_max takes non-NaN inputs.
 __device__ __forceinline__ float rows4_max(float v) {
   const int iv = __float_as_int(v);
   auto p = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
@@ -112,6 +111,35 @@ __device__ __forceinline__ float rows4_max(float v) {
   const int iw = __float_as_int(v);
   auto q = __builtin_amdgcn_permlane32_swap(iw, iw, false, false);
   return max_nonan(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+
+// The 16-lane rows of the wave as rows 0..3. permlane32 / permlane16 swap
+// (vdst a, vsrc b) exchange a's rows {2,3} with b's rows {0,1}, resp. a's odd
+// rows with b's even rows; swap_max returns the lane-wise max of the two
+// results:
+//   32: rows (max(a0,a2), max(a1,a3), max(b0,b2), max(b1,b3))
+//   16: rows (max(a0,a1), max(b0,b1), max(a2,a3), max(b2,b3))
+__device__ __forceinline__ float swap32_max(float a, float b) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(a), __float_as_int(b), false, false);
+  return max_nonan(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+__device__ __forceinline__ float swap16_max(float a, float b) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(a), __float_as_int(b), false, false);
+  return max_nonan(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+
+// Column max of four per-lane values v[0..3] (one per 16-wide column tile)
+// over the four rows, transposed: lane (row g, column c) returns
+// max over rows of v[g] at column c. Three swaps instead of eight.
+__device__ __forceinline__ float rows4_max_t4(float v0, float v1, float v2, float v3) {
+  const float x = swap32_max(v0, v2);     // rows: v0(0,2) v0(1,3) v2(0,2) v2(1,3)
+  const float y = swap32_max(v1, v3);     // rows: v1(0,2) v1(1,3) v3(0,2) v3(1,3)
+  return swap16_max(x, y);                // rows: v0 v1 v2 v3, each over all rows
+}
+// Two values: lane (row g, column c) returns the column max of v[g / 2].
+__device__ __forceinline__ float rows4_max_t2(float v0, float v1) {
+  const float x = swap32_max(v0, v1);     // rows: v0(0,2) v0(1,3) v1(0,2) v1(1,3)
+  return swap16_max(x, x);                // rows: v0 v0 v1 v1
 }
 
 __device__ __forceinline__ float rows4_sum(float v) {

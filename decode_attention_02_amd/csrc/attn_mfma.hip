@@ -135,43 +135,44 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;   // blocks to walk
 
   // Q rows of the workgroup's heads -> LDS in operand order: block (ht, s),
-  // lane (gg, cc) holds Q[h0+ht*16+cc][qk_dim(s, gg) .. +8]. Each role loads
-  // them between the first ring block and the rest, so staging Q waits for Q
-  // and block 0 only.
-  uint4 qv0, qv1, qv2, qv3;
+  // lane (gg, cc) holds Q[h0+ht*16+cc][qk_dim(s, gg) .. +8]. The QK waves
+  // load all of it, ahead of their first K blocks, and stage it before the
+  // first barrier; the PV waves issue their first V blocks only after that
+  // barrier. The first requests of every compute unit are then the ones the
+  // first iteration waits for (Q and K block 0), not V blocks needed two
+  // iterations later.
+  constexpr int kQLoads = 2 * HT;                                       // 16-byte loads per QK thread
+  static_assert(kQLoads == 4 || kQLoads == 8, "Q staging covers two or four head tiles");
   auto q_src = [&](int r) __attribute__((always_inline)) -> const uint4* {
-    const int idx = tid + 512 * r;
+    const int idx = tid + 256 * r;
     const int ln = idx & 63, blk = idx >> 6;
     const int ht = blk >> 3, s = blk & 7;
     const int gg = ln >> 4, cc = ln & 15;
     return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
                                           (h0 + ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
   };
-  auto load_q = [&]() __attribute__((always_inline)) {             // HT loads per thread
-    qv0 = *q_src(0); qv1 = *q_src(1);
-    if constexpr (HT == 4) { qv2 = *q_src(2); qv3 = *q_src(3); }
-  };
-  auto store_q = [&]() __attribute__((always_inline)) {
-    q_lds[tid] = qv0; q_lds[tid + 512] = qv1;
-    if constexpr (HT == 4) { q_lds[tid + 1024] = qv2; q_lds[tid + 1536] = qv3; }
-  };
-  // prologue of either role: ring blocks 0 .. R-1 and Q, then Q -> LDS. The
-  // QK waves need K block 0 with Q and load it first; the PV waves load Q
-  // first (V block 0 is used two iterations later).
-  auto prologue = [&](auto r_c, auto k_first_c, auto&& issue) __attribute__((always_inline)) {
+  // prologue of either role: the QK waves load Q, then ring blocks 0 .. R-1,
+  // then stage Q; the PV waves fill their ring after the Q barrier
+  auto prologue_qk = [&](auto r_c, auto&& issue) __attribute__((always_inline)) {
     constexpr int RR = decltype(r_c)::value;
-    constexpr bool kFirst = decltype(k_first_c)::value;
     if (N > 0) {
-      if constexpr (kFirst) {
-        issue(std::integral_constant<int, 0>{}, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      // named registers, not an array: an array held across the scheduling
+      // barriers below would be left in scratch memory
+      uint4 q0, q1, q2, q3, q4, q5, q6, q7;
+      q0 = *q_src(0); q1 = *q_src(1); q2 = *q_src(2); q3 = *q_src(3);
+      if constexpr (kQLoads == 8) { q4 = *q_src(4); q5 = *q_src(5); q6 = *q_src(6); q7 = *q_src(7); }
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
+      __builtin_amdgcn_sched_barrier(0);
+      q_lds[tid] = q0; q_lds[tid + 256] = q1; q_lds[tid + 512] = q2; q_lds[tid + 768] = q3;
+      if constexpr (kQLoads == 8) {
+        q_lds[tid + 1024] = q4; q_lds[tid + 1280] = q5; q_lds[tid + 1536] = q6; q_lds[tid + 1792] = q7;
       }
-      load_q();
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<kFirst ? 1 : 0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
-      __builtin_amdgcn_sched_barrier(0);
-      store_q();
     }
+  };
+  auto prologue_pv = [&](auto r_c, auto&& issue) __attribute__((always_inline)) {
+    constexpr int RR = decltype(r_c)::value;
+    if (N > 0) static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
   };
 
   // Block-table reads go through the constant address space: the table is
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // Every iteration issues the same loads (empty ones past the walk), so
     // every path into a consumer has the same loads in flight and the wait
     // before it leaves R-1 blocks outstanding.
-    prologue(std::integral_constant<int, R>{}, std::true_type{}, issue);
+    prologue_qk(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // Q staged
 
     // iteration 0: S of block 0
@@ -488,8 +489,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       });
     };
 
-    prologue(std::integral_constant<int, R>{}, std::false_type{}, issue);
     __syncthreads();   // Q staged
+    prologue_pv(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // iteration 0 (S of block 0 on the QK waves)
     __syncthreads();   // iteration 1 (softmax of block 0)
     // iteration n + 2: P.V of block n

@@ -65,18 +65,23 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 64. With ksplit > 1 writes fp32
 // partials part[ks][M][N] (K slice ks); with ksplit == 1 and out_bf16 set,
 // writes bf16 C directly. ntiles (2 or 4) = 16-column tiles per workgroup.
-// Requires N % (16*ntiles) == 0 and (K/ksplit) % 32 == 0.
+// Requires N % (16*ntiles) == 0 and (K/ksplit) % 32 == 0. packed / a_packed:
+// W / A in operand order (qproj.hip); a packed A holds gemm_row_tiles(M)
+// 16-row tiles per 32-wide k-step.
+int gemm_row_tiles(int M);
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
-                            int M, int N, int K, int ksplit, int ntiles, bool packed,
+                            int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
                             hipStream_t stream);
 // Row-major bf16 W [N][K] -> operand-order packed weight (N % 16 == 0, K % 32 == 0).
 hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
+// out_tiles > 0 (bf16 only): n is written as the packed GEMM activation
+// operand with out_tiles 16-row tiles; 0: row-major [M][R].
 // With append set, the same launch also writes one new KV token per
 // sequence (append->n_new == 1, see append_one.h).
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
-                                 float eps, void* out, int out_f32, const AppendArgs* append,
-                                 hipStream_t stream);
+                                 float eps, void* out, int out_f32, int out_tiles,
+                                 const AppendArgs* append, hipStream_t stream);
 // out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
 hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
                               int out_f32, hipStream_t stream);

@@ -59,7 +59,9 @@ QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype) {
     p.up = plan_gemm(HD, q_rank);
     p.off_part_down = 0;
     p.off_n = round_up(static_cast<size_t>(p.down.ks) * p.rows * q_rank * 4, 256);
-    p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 2, 256);
+    // n is the up-projection's packed activation operand: whole 16-row tiles
+    p.off_part_up = p.off_n + round_up(static_cast<size_t>(16 * mfa::gemm_row_tiles(p.rows)) *
+                                           q_rank * 2, 256);
     p.total = p.off_part_up +
               (p.up.ks > 1 ? round_up(static_cast<size_t>(p.up.ks) * p.rows * HD * 4, 256) : 0);
   } else {
@@ -210,19 +212,19 @@ mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipSt
       uint16_t* n = reinterpret_cast<uint16_t*>(c.ws + p.off_n);
       e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
                                 static_cast<const uint16_t*>(c.w_qdown), pd, nullptr, M, c.q_rank,
-                                c.hidden, p.down.ks, p.down.ntiles, c.packed, st);
+                                c.hidden, p.down.ks, p.down.ntiles, c.packed, false, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, c.q_norm_w, M, c.q_rank, c.eps, n, 0,
-                                     r0 == 0 ? append : nullptr, st);
+                                     mfa::gemm_row_tiles(M), r0 == 0 ? append : nullptr, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       if (p.up.ks == 1) {
         e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(c.w_qup), nullptr,
                                   reinterpret_cast<uint16_t*>(qo), M, c.HD, c.q_rank, 1,
-                                  p.up.ntiles, c.packed, st);
+                                  p.up.ntiles, c.packed, true, st);
       } else {
         float* pu = reinterpret_cast<float*>(c.ws + p.off_part_up);
         e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(c.w_qup), pu, nullptr, M, c.HD,
-                                  c.q_rank, p.up.ks, p.up.ntiles, c.packed, st);
+                                  c.q_rank, p.up.ks, p.up.ntiles, c.packed, true, st);
         if (e != hipSuccess) return MFA_ERR_HIP;
         e = mfa::launch_reduce_cast(pu, p.up.ks, M, c.HD, qo, 0, st);
       }
@@ -233,7 +235,7 @@ mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipSt
       e = mfa::launch_gemv_f32(reinterpret_cast<const float*>(xa),
                                static_cast<const float*>(c.w_qdown), cc, M, c.q_rank, c.hidden, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(cc, 1, c.q_norm_w, M, c.q_rank, c.eps, n, 1,
+      e = mfa::launch_rmsnorm_reduce(cc, 1, c.q_norm_w, M, c.q_rank, c.eps, n, 1, 0,
                                      r0 == 0 ? append : nullptr, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       e = mfa::launch_gemv_f32(n, static_cast<const float*>(c.w_qup), reinterpret_cast<float*>(qo),

@@ -35,9 +35,14 @@ namespace mfa {
 // (PACKED = true): 1 KB unit (nt = n/16, kt = k/32) at unit index
 // nt*(K/32) + kt, lane 16*((k%32)/8) + n%16 holding W[n][8*(k/8) .. +8], so
 // that each wave-wide weight load reads 1 KB of contiguous memory.
+// Activations: row-major [M][K] (PA = false) or packed in operand order
+// (PA = true, written so by the RMSNorm pass): 1 KB unit (kt = k/32,
+// mt = m/16) at unit index kt*MT + mt, lane 16*((k%32)/8) + m%16 holding
+// A[m][8*(k/8) .. +8]; rows M .. 16*MT-1 of the last tile are don't-care
+// (they feed only output rows that are not written).
 constexpr int kGemmWaves = 8;
 
-template <int MT, int NT, int PD, bool PACKED>
+template <int MT, int NT, int PD, bool PACKED, bool PA>
 __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float* __restrict__ part,
     uint16_t* __restrict__ out_bf16, int M, int N, int K, int kchunk) {
@@ -93,8 +98,14 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     for (int nt = 0; nt < NT; ++nt)
       wb[slot][nt] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(wr[nt], wofs + kk * kStepBytes, 0, 0));
+    if constexpr (PA) {
+      const uint16_t* au = A + static_cast<size_t>((kbeg / 32 + kk) * MT) * 64 * 8 + lane * 8;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + kk * 32);
+      for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(au + mt * 64 * 8);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ab[slot][mt] = *reinterpret_cast<const uint4*>(ap[mt] + kk * 32);
+    }
   };
 #pragma unroll
   for (int p = 0; p < PD; ++p)
@@ -166,7 +177,8 @@ template <bool APPEND>
 __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __restrict__ part,
                                                              int ksplit, const float* __restrict__ g,
                                                              int M, int R, float eps, void* out,
-                                                             int out_f32, AppendArgs app) {
+                                                             int out_f32, int out_tiles,
+                                                             AppendArgs app) {
   constexpr int kMaxChunks = 4;        // R <= 8192 = 4 chunks of 2048
   __shared__ float wsum[4];
   const int m = blockIdx.x;
@@ -234,7 +246,11 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
         pk.y = pack_bf16x2(v[2], v[3]);
         pk.z = pack_bf16x2(v[4], v[5]);
         pk.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + o) = pk;
+        // packed: unit (kt, mt) = (j0 / 32, m / 16), lane 16 * ((j0 % 32) / 8) + m % 16
+        const size_t po = out_tiles
+            ? (static_cast<size_t>((j0 >> 5) * out_tiles + (m >> 4)) * 64 + ((j0 >> 3) & 3) * 16 + (m & 15)) * 8
+            : o;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + po) = pk;
       }
     }
   }
@@ -268,42 +284,50 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
   if (lane == 0) out[static_cast<size_t>(m) * N + n] = acc;
 }
 
-template <int MT, int NT, int PD, bool PACKED>
+template <int MT, int NT, int PD, bool PACKED, bool PA>
 static void launch_gemm_shape(dim3 grid, const uint16_t* A, const uint16_t* W, float* part,
                               uint16_t* out_bf16, int M, int N, int K, int kchunk,
                               hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED>), grid, dim3(kGemmWaves * 64), 0,
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED, PA>), grid, dim3(kGemmWaves * 64), 0,
                      stream, A, W, part, out_bf16, M, N, K, kchunk);
 }
 
-template <bool PACKED>
+template <bool PACKED, bool PA>
 static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                                 int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
   const int kchunk = K / ksplit;
   if (ntiles == 4) {
     dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      launch_gemm_shape<1, 4, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<1, 4, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else if (M <= 32)
-      launch_gemm_shape<2, 4, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<2, 4, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else
-      launch_gemm_shape<4, 4, 3, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<4, 4, 3, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
   } else {
     dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
     if (M <= 16)
-      launch_gemm_shape<1, 2, 8, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<1, 2, 8, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else if (M <= 32)
-      launch_gemm_shape<2, 2, 6, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<2, 2, 6, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
     else
-      launch_gemm_shape<4, 2, 4, PACKED>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+      launch_gemm_shape<4, 2, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
   }
 }
 
+int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
-                            int M, int N, int K, int ksplit, int ntiles, bool packed,
+                            int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
                             hipStream_t stream) {
-  if (packed) launch_gemm_variant<true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
-  else launch_gemm_variant<false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+  if (M < 1 || M > 64) return hipErrorInvalidValue;
+  if (a_packed) {
+    if (packed) launch_gemm_variant<true, true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+  } else {
+    if (packed) launch_gemm_variant<true, false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+  }
   return hipGetLastError();
 }
 
@@ -331,15 +355,17 @@ hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipS
 }
 
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
-                                 float eps, void* out, int out_f32, const AppendArgs* append,
-                                 hipStream_t stream) {
+                                 float eps, void* out, int out_f32, int out_tiles,
+                                 const AppendArgs* append, hipStream_t stream) {
+  if (out_tiles && (out_f32 || out_tiles * 16 < M || R % 32)) return hipErrorInvalidValue;
   if (append) {
     const int extra = (append->B + 3) / 4 < 16 ? (append->B + 3) / 4 : 16;
     hipLaunchKernelGGL(rmsnorm_reduce_kernel<true>, dim3(static_cast<unsigned>(M + extra)),
-                       dim3(256), 0, stream, part, ksplit, g, M, R, eps, out, out_f32, *append);
+                       dim3(256), 0, stream, part, ksplit, g, M, R, eps, out, out_f32, out_tiles,
+                       *append);
   } else {
     hipLaunchKernelGGL(rmsnorm_reduce_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(256), 0,
-                       stream, part, ksplit, g, M, R, eps, out, out_f32, AppendArgs{});
+                       stream, part, ksplit, g, M, R, eps, out, out_f32, out_tiles, AppendArgs{});
   }
   return hipGetLastError();
 }

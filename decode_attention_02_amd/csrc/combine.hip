@@ -14,6 +14,10 @@ namespace mfa {
 // One workgroup of 256 threads covers 1024/d heads of one sequence; a thread
 // owns 4 consecutive features of one head and reads one float4 per split.
 // Partial o is bf16 (PBF16) or fp32; m and l are fp32.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8); the remap
+// gives each XCD a contiguous range of sequences, the same range whose
+// splits the attention kernel ran there, so the partials are read through
+// the L2 they were written to.
 template <bool PBF16>
 __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
@@ -22,8 +26,10 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
   const int tpb = d >> 2;                        // threads per head
   const int hpb = 256 / tpb;                     // heads per workgroup
   const int groups = (H + hpb - 1) / hpb;
-  const int b = blockIdx.x / groups;
-  const int h = (blockIdx.x % groups) * hpb + threadIdx.x / tpb;
+  int id = blockIdx.x;
+  if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+  const int b = id / groups;
+  const int h = (id % groups) * hpb + threadIdx.x / tpb;
   const int f = (threadIdx.x % tpb) * 4;
   if (h >= H) return;
   const size_t row0 = static_cast<size_t>(b) * S;

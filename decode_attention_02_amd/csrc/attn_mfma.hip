@@ -103,11 +103,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   constexpr int kHS = kH / kHW;                                         // workgroups per split
   __shared__ __attribute__((aligned(16))) uint4 q_lds[HT * 8 * 64];     // HT x 8 KB, operand order
   __shared__ __attribute__((aligned(16))) uint4 p_lds[2][HT * 2 * 64];  // 2 x HT x 2 KB, operand order
+  __shared__ __attribute__((aligned(16))) f32x4_t s_lds[2][4 * HT * 64]; // logits by (QK wave, tile, lane)
   __shared__ __attribute__((aligned(16))) float red[2][kHW * 4];        // block max [head][QK wave]
-  __shared__ __attribute__((aligned(16))) float alpha_lds[2][kHW];
-  __shared__ int flag_lds[2];
-  __shared__ __attribute__((aligned(16))) float lred[kHW * 4];          // row sums [head][QK wave]
-  __shared__ float m_lds[kHW];
+  __shared__ __attribute__((aligned(16))) uint4 vs_lds[2][16];          // FP8 V scales by (QK wave, row)
+  __shared__ __attribute__((aligned(16))) float lred[kHW * 4];          // row sums [head][PV wave]
 
   const int tid = threadIdx.x;
   // wave index as a scalar: the role branches below are uniform per wave
@@ -193,17 +192,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // Every wave passes the same barriers: one after staging Q, one per
   // iteration i = 0 .. N+1, one before the epilogue.
   if (w < 4) {
-    // ================= QK waves: S = K.Q^T, online softmax, P^T -> LDS
+    // ================= QK waves: S = K.Q^T -> LDS, per-wave block max
     constexpr int R = RK;
     constexpr int U = unroll_for(RK);
-    float m_run[HT], l_run[HT];          // per head h0 + 16ht + c, log2 units of scaled logits
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
-    const float cl2 = a.scale_log2;      // > 0
     uint4 ring[R][C::kSlot];             // K units of 16 tokens (+ FP8 K, V scales)
-    f32x4_t sb[2][HT];                   // raw logits of the last two blocks, by parity
-    uint4 vkeep[2];                      // FP8: V scales of the last two blocks, by parity
-    vkeep[0] = vkeep[1] = make_uint4(0u, 0u, 0u, 0u);
     // Loads block n into a ring slot; n >= N (past the walk) issues the same
     // number of loads through empty resources, which return zeros and read
     // nothing, so the loop's load count is the same on every path.
@@ -230,7 +222,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         ring[slot][5] = buf_load16(rvs, so);
       }
     };
-    // S^T of block n (16 tokens x kHW heads of this wave) -> sb[par], block max -> red
+    // S^T of block n (16 tokens x kHW heads of this wave) -> s_lds[par], the
+    // wave's per-head max -> red[par] (FP8: V scales -> vs_lds[par])
     auto scores = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int par = decltype(par_c)::value;
@@ -238,8 +231,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       // bf16: the Q operands of k-step s+1 are read from LDS while step s
-      // multiplies (FP8 has no registers to spare for that; its operand
-      // conversions fill the gaps instead)
+      // multiplies (FP8: its operand conversions fill the gaps instead)
       constexpr bool kQdb = !FP8;
       bf16x8_t qop[2][HT];
       if constexpr (kQdb) {
@@ -275,7 +267,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s_acc[ht][e] *= ks[e];
-        vkeep[par] = ring[slot][5];   // the slot is refilled below
+        vs_lds[par][ww * 4 + g] = ring[slot][5];   // same value from the 16 lanes of a row
       }
       const int lim = tokens_in(n);
       if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
@@ -291,67 +283,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         mt[ht] = max_nonan(max3_nonan(s_acc[ht][0], s_acc[ht][1], s_acc[ht][2]), s_acc[ht][3]);
-        sb[par][ht] = s_acc[ht];
+        s_lds[par][(ww * HT + ht) * 64 + lane] = s_acc[ht];
       }
       if constexpr (HT == 4) {
         red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
       } else {
         red[par][((g >> 1) * 16 + c) * 4 + ww] = rows4_max_t2(mt[0], mt[1]);
-      }
-    };
-    // softmax of block n (its logits in sb[par]): P^T -> p_lds[par], rescale factors
-    auto softmax = [&](auto par_c) __attribute__((always_inline)) {
-      constexpr int par = decltype(par_c)::value;
-      float vs[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (FP8) {
-        const uint4 v4 = vkeep[par];
-        vs[0] = __uint_as_float(v4.x); vs[1] = __uint_as_float(v4.y);
-        vs[2] = __uint_as_float(v4.z); vs[3] = __uint_as_float(v4.w);
-      }
-      bool rescale = false;
-      float4 r4[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) r4[ht] = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
-      float alpha[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        // block max over all 64 tokens (finite: every walked block has a valid token)
-        const float tz = max_nonan(max3_nonan(r4[ht].x, r4[ht].y, r4[ht].z), r4[ht].w) * cl2;
-        alpha[ht] = 1.0f;
-        if (tz > m_run[ht] + kLazy) {          // also true for the first block
-          alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - tz);
-          m_run[ht] = tz;
-          rescale = true;
-        }
-        const float nm = -m_run[ht];
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[par][ht][e], cl2, nm));
-        l_run[ht] = l_run[ht] * alpha[ht] + ((p[0] + p[1]) + (p[2] + p[3]));
-        if constexpr (FP8) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] *= vs[e];
-        }
-        // P^T into operand block (ht, ks) of buffer par
-        int ks, gr;
-        if constexpr (FP8) { ks = g >> 1; gr = ww; }
-        else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
-        uint2 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
-        uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[par]) +
-                       ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
-        *reinterpret_cast<uint2*>(dst) = pk;
-      }
-      if (ww == 0) {   // rescale factors: lane row g stores tile g (HT 4) or g/2 (HT 2)
-        if constexpr (HT == 4) {
-          const float al = g == 0 ? alpha[0] : g == 1 ? alpha[1] : g == 2 ? alpha[2] : alpha[3];
-          alpha_lds[par][g * 16 + c] = al;
-        } else {
-          alpha_lds[par][(g >> 1) * 16 + c] = g < 2 ? alpha[0] : alpha[1];
-        }
-        const bool any = __ballot(rescale) != 0ull;
-        if (lane == 0) flag_lds[par] = any ? 1 : 0;
       }
     };
 
@@ -360,23 +297,14 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // before it leaves R-1 blocks outstanding.
     prologue_qk(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // Q staged
-
-    // iteration 0: S of block 0
-    if (N > 0) {
-      scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, 0);
-      issue(std::integral_constant<int, 0>{}, R);
-    }
-    __syncthreads();
-    // iterations 1 .. : softmax(i-1) and S(i) in one straight block, so the
-    // matrix-core and vector work can interleave; groups of U keep ring slots
-    // and parities static (i = base + r with base = 1 mod U)
-    int base = 1;
+    // iterations i = 0 .. N+1, S(i) for i < N; groups of U keep ring slots
+    // and parities static (i = base + r, base a multiple of U)
+    int base = 0;
     for (; base + U <= N; base += U) {
       static_for<0, U>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        constexpr int slot = (1 + r) % R, par = (1 + r) & 1, par1 = r & 1;
+        constexpr int slot = r % R, par = r & 1;
         const int i = base + r;
-        softmax(std::integral_constant<int, par1>{});
         scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
         issue(std::integral_constant<int, slot>{}, i + R);
         __syncthreads();
@@ -385,38 +313,34 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // the rest: i = base .. N+1 (at most U+1 iterations)
     static_for<0, U + 1>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
-      constexpr int slot = (1 + r) % R, par = (1 + r) & 1, par1 = r & 1;
+      constexpr int slot = r % R, par = r & 1;
       const int i = base + r;
       if (i <= N + 1) {
         if (i < N) {
-          softmax(std::integral_constant<int, par1>{});
           scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
           issue(std::integral_constant<int, slot>{}, i + R);
-        } else if (i == N) {
-          softmax(std::integral_constant<int, par1>{});
         }
         __syncthreads();
       }
     });
-
-    // row sums -> LDS for the PV waves
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const float l = rows4_sum(l_run[ht]);
-      if (g == 0) lred[(ht * 16 + c) * 4 + ww] = l;
-      if (ww == 0 && g == 0) m_lds[ht * 16 + c] = m_run[ht];
-    }
-    __syncthreads();
+    __syncthreads();   // row sums staged (by the PV waves)
   } else {
-    // ================= PV waves: O^T += V^T . P^T
+    // ================= PV waves: online softmax, O^T += V^T . P^T
     constexpr int R = RV;
     constexpr int U = unroll_for(RV);
+    const float cl2 = a.scale_log2;      // > 0
     // acc[dt][ht]: lane holds O^T[64ww + 16dt + 4g + i][16ht + c]
     f32x4_t acc[4][HT];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // running max per head h0 + 16ht + c (log2 units of scaled logits; the
+    // same in every PV wave) and this wave's partial row sums over the
+    // tokens of its softmax share
+    float m_run[HT], l_run[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
     uint4 ring[R][C::kLoads];
     auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {   // as for K
       constexpr int slot = decltype(slot_c)::value;
@@ -434,14 +358,6 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     auto pv = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int par = decltype(par_c)::value;
-      if (flag_lds[par]) {
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          const float al = alpha_lds[par][ht * 16 + c];
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[dt][ht] *= al;
-        }
-      }
       const int lim = tokens_in(n);
       if (lim < kBlockTokens) {
         // tokens past the end: zero their V so 0 * (stale data) cannot reach O
@@ -489,11 +405,71 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       });
     };
 
+    // softmax of block n for this wave's 16 tokens (those QK wave ww
+    // scored): block max from all four QK waves, lazy update of the running
+    // max (O rescaled here, so the next products add to a consistent sum),
+    // P^T (bf16, FP8: times the V scales) -> p_lds[par]
+    auto softmax = [&](auto par_c) __attribute__((always_inline)) {
+      constexpr int par = decltype(par_c)::value;
+      float4 r4[HT];
+      f32x4_t sv[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        r4[ht] = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
+        sv[ht] = s_lds[par][(ww * HT + ht) * 64 + lane];
+      }
+      float vs[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) {
+        const uint4 v4 = vs_lds[par][ww * 4 + g];
+        vs[0] = __uint_as_float(v4.x); vs[1] = __uint_as_float(v4.y);
+        vs[2] = __uint_as_float(v4.z); vs[3] = __uint_as_float(v4.w);
+      }
+      bool rescale = false;
+      float alpha[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        // block max over all 64 tokens (finite: every walked block has a valid token)
+        const float tz = max_nonan(max3_nonan(r4[ht].x, r4[ht].y, r4[ht].z), r4[ht].w) * cl2;
+        alpha[ht] = 1.0f;
+        if (tz > m_run[ht] + kLazy) {          // also true for the first block
+          alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - tz);
+          m_run[ht] = tz;
+          rescale = true;
+        }
+        const float nm = -m_run[ht];
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ht][e], cl2, nm));
+        l_run[ht] = l_run[ht] * alpha[ht] + ((p[0] + p[1]) + (p[2] + p[3]));
+        if constexpr (FP8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] *= vs[e];
+        }
+        // P^T into operand block (ht, ks) of buffer par
+        int ks, gr;
+        if constexpr (FP8) { ks = g >> 1; gr = ww; }
+        else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
+        uint2 pk;
+        pk.x = pack_bf16x2(p[0], p[1]);
+        pk.y = pack_bf16x2(p[2], p[3]);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[par]) +
+                       ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
+        *reinterpret_cast<uint2*>(dst) = pk;
+      }
+      if (__ballot(rescale) != 0ull) {   // uniform: every PV wave takes the same branch
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[dt][ht] *= alpha[ht];
+      }
+    };
+
     __syncthreads();   // Q staged
     prologue_pv(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // iteration 0 (S of block 0 on the QK waves)
-    __syncthreads();   // iteration 1 (softmax of block 0)
-    // iteration n + 2: P.V of block n
+    if (N > 0) softmax(std::integral_constant<int, 0>{});
+    __syncthreads();   // iteration 1
+    // iteration n + 2: P.V of block n, then the softmax of block n + 1
     int nb = 0;
     for (; nb + U <= N; nb += U) {
       static_for<0, U>([&](auto rc) {
@@ -502,6 +478,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         const int n = nb + r;
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
+        if (n + 1 < N) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       });
     }
@@ -512,17 +489,24 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       if (n < N) {
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
+        if (n + 1 < N) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       }
     });
 
+    // row sums: this wave's share -> LDS, then the total over the four
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const float l = rows4_sum(l_run[ht]);
+      if (g == 0) lred[(ht * 16 + c) * 4 + ww] = l;
+    }
     __syncthreads();   // row sums staged
     float lsum[HT], mh[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const float4 r4 = reinterpret_cast<const float4*>(lred)[ht * 16 + c];
       lsum[ht] = (r4.x + r4.y) + (r4.z + r4.w);
-      mh[ht] = m_lds[ht * 16 + c];
+      mh[ht] = m_run[ht];
     }
     if (a.num_splits == 1) {
 #pragma unroll
@@ -592,7 +576,7 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
     else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4>), grid, block, 0, stream, a);
   } else {
     if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 4, 2>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 2, 3, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, 4>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -519,13 +519,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
           const size_t o = (static_cast<size_t>(b) * kH + head) * kD + f;
           const f32x4_t v = acc[dt][ht] * inv;
           if (a.out_f32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            store_nt(reinterpret_cast<float*>(a.out) + o, make_float4(v[0], v[1], v[2], v[3]));
           } else {
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = pk;
+            store_nt(reinterpret_cast<uint16_t*>(a.out) + o, pk);
           }
         }
       }
@@ -546,17 +545,16 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.part_o) + po) = pk;
+            store_nt(static_cast<uint16_t*>(a.part_o) + po, pk);
           } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.part_o) + po) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            store_nt(static_cast<float*>(a.part_o) + po, make_float4(v[0], v[1], v[2], v[3]));
           }
         }
         if (ww == 0 && g == 0) {
           float2 ml;
           ml.x = mh[ht] * kLn2;     // natural-log units of the scaled logits
           ml.y = lsum[ht];
-          *reinterpret_cast<float2*>(a.part_ml + (row * kH + head) * 2) = ml;
+          store_nt(a.part_ml + (row * kH + head) * 2, ml);
         }
       }
     }

@@ -84,13 +84,12 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const size_t oi = (static_cast<size_t>(b) * H + h) * d + f;
   if (out_f32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) =
-        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    store_nt(reinterpret_cast<float*>(out) + oi, make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
   } else {
     uint2 pk;
     pk.x = pack_bf16x2(num.x * inv, num.y * inv);
     pk.y = pack_bf16x2(num.z * inv, num.w * inv);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = pk;
+    store_nt(reinterpret_cast<uint16_t*>(out) + oi, pk);
   }
 }
 

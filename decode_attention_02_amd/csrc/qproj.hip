@@ -150,18 +150,18 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     if (out_bf16) {
       uint16_t* dst = out_bf16 + static_cast<size_t>(m) * N + n0 + nl;
       if constexpr (kPer == 1) {
-        dst[0] = f32_to_bf16(v[0]);
+        __builtin_nontemporal_store(f32_to_bf16(v[0]), dst);
       } else {
 #pragma unroll
-        for (int j = 0; j < kPer; j += 2) *reinterpret_cast<uint32_t*>(dst + j) = pack_bf16x2(v[j], v[j + 1]);
+        for (int j = 0; j < kPer; j += 2) store_nt(dst + j, pack_bf16x2(v[j], v[j + 1]));
       }
     } else {
       float* dst = part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl;
       if constexpr (kPer == 1) {
-        dst[0] = v[0];
+        store_nt(dst, v[0]);
       } else {
 #pragma unroll
-        for (int j = 0; j < kPer; j += 2) *reinterpret_cast<float2*>(dst + j) = make_float2(v[j], v[j + 1]);
+        for (int j = 0; j < kPer; j += 2) store_nt(dst + j, make_float2(v[j], v[j + 1]));
       }
     }
   }

@@ -15,6 +15,7 @@ MFA_OK = 0
 MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
 MFA_WEIGHTS_ROWMAJOR, MFA_WEIGHTS_PACKED = 0, 1
 BLOCK_TOKENS = 64
+ABI_VERSION = 2
 STATUS_NAMES = {0: "MFA_OK", 1: "MFA_ERR_NULL", 2: "MFA_ERR_SHAPE", 3: "MFA_ERR_DTYPE",
                 4: "MFA_ERR_ALIGN", 5: "MFA_ERR_UNSUPPORTED", 6: "MFA_ERR_WORKSPACE",
                 7: "MFA_ERR_HIP"}
@@ -56,6 +57,7 @@ class StepArgs(ctypes.Structure):
         ("split_workspace", ctypes.c_void_p), ("split_workspace_bytes", ctypes.c_size_t),
         ("out", ctypes.c_void_p),
         ("out_dtype", ctypes.c_int),
+        ("w_kv", ctypes.c_void_p),
     ]
 
 
@@ -95,7 +97,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.mfa_abi_version() != 1:
+    if lib.mfa_abi_version() != ABI_VERSION:
         raise RuntimeError("libmfa.so ABI version mismatch")
     _LIB = lib
     return lib

@@ -21,24 +21,56 @@ __device__ __forceinline__ float append_load_in(const void* p, size_t i, int in_
 
 // Token pos[b] of sequence b (n_new == 1); positions outside the table or
 // mapped to no block write nothing.
+// With a projected token (kv_part set), k_out / v_out are written even when
+// the position maps to no block.
 template <int CACHE, int EPT>   // CACHE: 0 f32, 1 bf16, 2 fp8
 __device__ __forceinline__ void append_token_wave(const AppendArgs& a, int b, int lane) {
   const int p0 = a.pos[b];
+  const int d = a.d;
+  const size_t row = static_cast<size_t>(b) * d;
+  float xk[EPT], xv[EPT];
+  if (a.kv_part) {
+    // projected token: sum the K-slice partials in slice order, round to the
+    // activation dtype, keep a copy of the rounded values if asked
+    const size_t prow = static_cast<size_t>(b - a.kv_row0) * a.kv_stride + a.kv_col0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) { xk[e] = 0.f; xv[e] = 0.f; }
+    for (int ks = 0; ks < a.kv_ks; ++ks) {
+      const float* pr = a.kv_part + static_cast<size_t>(ks) * a.kv_rows * a.kv_stride + prow;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        xk[e] += pr[lane * EPT + e];
+        xv[e] += pr[d + lane * EPT + e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const size_t i = row + lane * EPT + e;
+      if (a.kv_round_bf16) {
+        const uint16_t kbits = f32_to_bf16(xk[e]), vbits = f32_to_bf16(xv[e]);
+        xk[e] = bf16_to_f32(kbits);
+        xv[e] = bf16_to_f32(vbits);
+        if (a.k_out) static_cast<uint16_t*>(a.k_out)[i] = kbits;
+        if (a.v_out) static_cast<uint16_t*>(a.v_out)[i] = vbits;
+      } else {
+        if (a.k_out) static_cast<float*>(a.k_out)[i] = xk[e];
+        if (a.v_out) static_cast<float*>(a.v_out)[i] = xv[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      xk[e] = append_load_in(a.k_new, row + lane * EPT + e, a.in_f32);
+      xv[e] = append_load_in(a.v_new, row + lane * EPT + e, a.in_f32);
+    }
+  }
   if (p0 < 0) return;
   const int j = p0 / kBlockTokens;
   if (j >= a.max_blocks_per_seq) return;
   const int id = a.block_table ? a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + j]
                                : b * a.max_blocks_per_seq + j;
   if (id < 0 || id >= a.num_blocks) return;
-  const int d = a.d;
   const int off = p0 & 63;
-  const size_t row = static_cast<size_t>(b) * d;
-  float xk[EPT], xv[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    xk[e] = append_load_in(a.k_new, row + lane * EPT + e, a.in_f32);
-    xv[e] = append_load_in(a.v_new, row + lane * EPT + e, a.in_f32);
-  }
   const size_t esz = CACHE == 0 ? 4 : (CACHE == 1 ? 2 : 1);
   uint8_t* kb = a.k + static_cast<size_t>(id) * kBlockTokens * d * esz;
   uint8_t* vb = a.v + static_cast<size_t>(id) * kBlockTokens * d * esz;

@@ -57,6 +57,21 @@ struct AppendArgs {
   int max_blocks_per_seq;
   int d;
   int cache_dtype;            // 0 f32, 1 bf16, 2 fp8
+  // K/V projection (decode step only, n_new == 1): when kv_part is set, the
+  // token of sequence b (kv_row0 <= b < kv_row0 + kv_rows) is not read from
+  // k_new / v_new but summed over kv_ks fp32 partial slices
+  //   k[f] = sum_ks kv_part[(ks * kv_rows + b - kv_row0) * kv_stride + kv_col0 + f]
+  // (v: columns kv_col0 + d + f), rounded to bf16 when kv_round_bf16, and
+  // also written to k_out / v_out ([B][d], the rounded dtype) when set.
+  const float* kv_part;
+  int kv_ks;
+  int kv_rows;
+  int kv_row0;
+  int kv_stride;
+  int kv_col0;
+  int kv_round_bf16;
+  void* k_out;
+  void* v_out;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
@@ -69,9 +84,11 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // W / A in operand order (qproj.hip); a packed A holds gemm_row_tiles(M)
 // 16-row tiles per 32-wide k-step.
 int gemm_row_tiles(int M);
+// W2 (nullable): columns N1 .. N-1 come from W2 (its rows 0 .. N-N1-1)
+// instead of W; N1 % (16*ntiles) == 0.
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
-                            hipStream_t stream);
+                            hipStream_t stream, const uint16_t* W2 = nullptr, int N1 = 0);
 // Row-major bf16 W [N][K] -> operand-order packed weight (N % 16 == 0, K % 32 == 0).
 hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.
@@ -79,9 +96,10 @@ hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipS
 // operand with out_tiles 16-row tiles; 0: row-major [M][R].
 // With append set, the same launch also writes one new KV token per
 // sequence (append->n_new == 1, see append_one.h).
+// part_stride: row stride of the partials (>= R; R when 0).
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
                                  float eps, void* out, int out_f32, int out_tiles,
-                                 const AppendArgs* append, hipStream_t stream);
+                                 const AppendArgs* append, hipStream_t stream, int part_stride = 0);
 // out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
 hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
                               int out_f32, hipStream_t stream);

@@ -47,29 +47,35 @@ GemmPlan plan_gemm(int N, int K) {
 
 struct QprojPlan {
   int rows;          // rows per pass
-  GemmPlan down, up;
-  size_t off_part_down, off_n, off_part_up, total;
+  GemmPlan down, down_kv, up;   // down_kv: down-projection with the K/V columns appended
+  size_t off_part_down, off_n, off_part_up, off_kv, total;
 };
 
-QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype) {
+// kvc: K/V projection columns (2d) the workspace must also hold.
+QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype, int kvc) {
   QprojPlan p{};
   p.rows = B < kRowsPerPass ? B : kRowsPerPass;
   if (dtype == MFA_BF16) {
     p.down = plan_gemm(q_rank, hidden);
+    p.down_kv = plan_gemm(q_rank + kvc, hidden);
     p.up = plan_gemm(HD, q_rank);
     p.off_part_down = 0;
-    p.off_n = round_up(static_cast<size_t>(p.down.ks) * p.rows * q_rank * 4, 256);
+    const size_t part_q = static_cast<size_t>(p.down.ks) * p.rows * q_rank * 4;
+    const size_t part_kv = static_cast<size_t>(p.down_kv.ks) * p.rows * (q_rank + kvc) * 4;
+    p.off_n = round_up(part_q > part_kv ? part_q : part_kv, 256);
     // n is the up-projection's packed activation operand: whole 16-row tiles
     p.off_part_up = p.off_n + round_up(static_cast<size_t>(16 * mfa::gemm_row_tiles(p.rows)) *
                                            q_rank * 2, 256);
     p.total = p.off_part_up +
               (p.up.ks > 1 ? round_up(static_cast<size_t>(p.up.ks) * p.rows * HD * 4, 256) : 0);
+    p.off_kv = 0;      // the K/V columns live in the down-projection's partials
   } else {
-    p.down = p.up = GemmPlan{0, 1};
+    p.down = p.down_kv = p.up = GemmPlan{0, 1};
     p.off_part_down = 0;
     p.off_n = round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
     p.off_part_up = p.off_n + round_up(static_cast<size_t>(p.rows) * q_rank * 4, 256);
-    p.total = p.off_part_up;
+    p.off_kv = p.off_part_up;                 // [rows][kvc] fp32 K/V projection
+    p.total = p.off_kv + round_up(static_cast<size_t>(p.rows) * kvc * 4, 256);
   }
   return p;
 }
@@ -136,7 +142,7 @@ const char* mfa_status_str(int s) {
 
 size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, int dtype) {
   if (check_qproj_shape(B, hidden, q_rank, H, d, dtype) != MFA_OK) return 0;
-  return plan_qproj(B, hidden, q_rank, H * d, dtype).total;
+  return plan_qproj(B, hidden, q_rank, H * d, dtype, 2 * d).total;
 }
 
 mfa_status mfa_pack_weight(const void* w, void* packed, int N, int K, int dtype, void* stream) {
@@ -162,6 +168,8 @@ struct QprojCall {
   bool packed;
   float eps;
   QprojPlan p;
+  const void* w_kv;  // K/V projection weights [kvc][hidden] or nullptr
+  int kvc;           // 2d with w_kv, else 0
 };
 
 mfa_status prepare_qproj(const void* x, const void* w_qdown, const float* q_norm_w,
@@ -178,7 +186,7 @@ mfa_status prepare_qproj(const void* x, const void* w_qdown, const float* q_norm
       !aligned16(q_out) || (workspace && !aligned16(workspace)))
     return MFA_ERR_ALIGN;
   if (!(eps >= 0.f)) return MFA_ERR_SHAPE;
-  c->p = plan_qproj(B, hidden, q_rank, H * d, dtype);
+  c->p = plan_qproj(B, hidden, q_rank, H * d, dtype, 2 * d);
   if (!workspace) return MFA_ERR_WORKSPACE;
   if (workspace_bytes < c->p.total) return MFA_ERR_WORKSPACE;
   c->x = x;
@@ -194,28 +202,51 @@ mfa_status prepare_qproj(const void* x, const void* w_qdown, const float* q_norm
   c->dtype = dtype;
   c->packed = weight_layout == MFA_WEIGHTS_PACKED;
   c->eps = eps;
+  c->w_kv = nullptr;
+  c->kvc = 0;
   return MFA_OK;
 }
 
 // Enqueues the query path; a single-token KV append (append != nullptr)
-// rides in the first RMSNorm launch.
+// rides in the first RMSNorm launch. With the K/V projection (c.w_kv), the
+// K/V columns ride in each pass's down-projection and every pass appends
+// its own rows from their partials.
 mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipStream_t st) {
   const QprojPlan& p = c.p;
   const size_t esz = c.dtype == MFA_BF16 ? 2 : 4;
+  const bool proj = c.w_kv != nullptr;
   for (int r0 = 0; r0 < c.B; r0 += p.rows) {
     const int M = (c.B - r0) < p.rows ? (c.B - r0) : p.rows;
     const uint8_t* xa = static_cast<const uint8_t*>(c.x) + static_cast<size_t>(r0) * c.hidden * esz;
     uint8_t* qo = static_cast<uint8_t*>(c.q_out) + static_cast<size_t>(r0) * c.HD * esz;
     hipError_t e;
+    mfa::AppendArgs ap{};
+    const mfa::AppendArgs* app = r0 == 0 ? append : nullptr;
+    if (proj) {
+      ap = *append;
+      ap.kv_rows = M;
+      ap.kv_row0 = r0;
+      ap.kv_round_bf16 = c.dtype == MFA_BF16;
+      app = &ap;
+    }
     if (c.dtype == MFA_BF16) {
       float* pd = reinterpret_cast<float*>(c.ws + p.off_part_down);
       uint16_t* n = reinterpret_cast<uint16_t*>(c.ws + p.off_n);
+      const GemmPlan& dp = proj ? p.down_kv : p.down;
+      const int N = c.q_rank + c.kvc;
       e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
-                                static_cast<const uint16_t*>(c.w_qdown), pd, nullptr, M, c.q_rank,
-                                c.hidden, p.down.ks, p.down.ntiles, c.packed, false, st);
+                                static_cast<const uint16_t*>(c.w_qdown), pd, nullptr, M, N,
+                                c.hidden, dp.ks, dp.ntiles, c.packed, false, st,
+                                static_cast<const uint16_t*>(c.w_kv), c.q_rank);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(pd, p.down.ks, c.q_norm_w, M, c.q_rank, c.eps, n, 0,
-                                     mfa::gemm_row_tiles(M), r0 == 0 ? append : nullptr, st);
+      if (proj) {
+        ap.kv_part = pd;
+        ap.kv_ks = dp.ks;
+        ap.kv_stride = N;
+        ap.kv_col0 = c.q_rank;
+      }
+      e = mfa::launch_rmsnorm_reduce(pd, dp.ks, c.q_norm_w, M, c.q_rank, c.eps, n, 0,
+                                     mfa::gemm_row_tiles(M), app, st, N);
       if (e != hipSuccess) return MFA_ERR_HIP;
       if (p.up.ks == 1) {
         e = mfa::launch_gemm_bf16(n, static_cast<const uint16_t*>(c.w_qup), nullptr,
@@ -235,8 +266,17 @@ mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipSt
       e = mfa::launch_gemv_f32(reinterpret_cast<const float*>(xa),
                                static_cast<const float*>(c.w_qdown), cc, M, c.q_rank, c.hidden, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
-      e = mfa::launch_rmsnorm_reduce(cc, 1, c.q_norm_w, M, c.q_rank, c.eps, n, 1, 0,
-                                     r0 == 0 ? append : nullptr, st);
+      if (proj) {
+        float* kv = reinterpret_cast<float*>(c.ws + p.off_kv);
+        e = mfa::launch_gemv_f32(reinterpret_cast<const float*>(xa),
+                                 static_cast<const float*>(c.w_kv), kv, M, c.kvc, c.hidden, st);
+        if (e != hipSuccess) return MFA_ERR_HIP;
+        ap.kv_part = kv;
+        ap.kv_ks = 1;
+        ap.kv_stride = c.kvc;
+        ap.kv_col0 = 0;
+      }
+      e = mfa::launch_rmsnorm_reduce(cc, 1, c.q_norm_w, M, c.q_rank, c.eps, n, 1, 0, app, st);
       if (e != hipSuccess) return MFA_ERR_HIP;
       e = mfa::launch_gemv_f32(n, static_cast<const float*>(c.w_qup), reinterpret_cast<float*>(qo),
                                M, c.HD, c.q_rank, st);
@@ -246,12 +286,17 @@ mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipSt
   return MFA_OK;
 }
 
+// projected: the token comes from the K/V projection (k_new, v_new are then
+// optional outputs).
 mfa_status prepare_append(const void* k_new, const void* v_new, int in_dtype, const int32_t* pos,
-                          int n_new, int B, const mfa_kv_cache* cache, mfa::AppendArgs* a) {
-  if (!k_new || !v_new || !pos) return MFA_ERR_NULL;
+                          int n_new, int B, const mfa_kv_cache* cache, mfa::AppendArgs* a,
+                          bool projected = false) {
+  if (!pos) return MFA_ERR_NULL;
+  if (!projected && (!k_new || !v_new)) return MFA_ERR_NULL;
   const mfa_status cs = check_cache(cache);
   if (cs != MFA_OK) return cs;
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(pos)) return MFA_ERR_ALIGN;
+  if ((k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) || !aligned4(pos))
+    return MFA_ERR_ALIGN;
   if (B < 1 || n_new < 1) return MFA_ERR_SHAPE;
   if (static_cast<long long>(n_new) > static_cast<long long>(cache->max_blocks_per_seq) * kBlock)
     return MFA_ERR_SHAPE;
@@ -276,6 +321,11 @@ mfa_status prepare_append(const void* k_new, const void* v_new, int in_dtype, co
   a->max_blocks_per_seq = cache->max_blocks_per_seq;
   a->d = cache->head_dim;
   a->cache_dtype = cache->dtype == MFA_F32 ? 0 : (cache->dtype == MFA_BF16 ? 1 : 2);
+  if (projected) {
+    a->k_new = a->v_new = nullptr;
+    a->k_out = const_cast<void*>(k_new);
+    a->v_out = const_cast<void*>(v_new);
+  }
   return MFA_OK;
 }
 
@@ -456,8 +506,18 @@ mfa_status mfa_decode_step(const mfa_step_args* s, void* stream) {
                                         s->weight_layout, &qc);
     if (st != MFA_OK) return st;
   }
+  const bool proj = s->w_kv != nullptr;
+  if (proj) {
+    if (!has_qproj) return MFA_ERR_NULL;                 // the projection needs x
+    if (!aligned16(s->w_kv)) return MFA_ERR_ALIGN;
+    if (s->kv_in_dtype != s->dtype) return MFA_ERR_DTYPE;
+    if (s->cache && s->cache->head_dim != s->d) return MFA_ERR_SHAPE;
+    qc.w_kv = s->w_kv;
+    qc.kvc = 2 * s->d;
+  }
   mfa::AppendArgs ap;
-  mfa_status st = prepare_append(s->k_new, s->v_new, s->kv_in_dtype, s->pos, 1, s->B, s->cache, &ap);
+  mfa_status st = prepare_append(s->k_new, s->v_new, s->kv_in_dtype, s->pos, 1, s->B, s->cache, &ap,
+                                 proj);
   if (st != MFA_OK) return st;
   AttnCall ac;
   st = prepare_attn(s->q, s->dtype, s->B, s->H, s->cache, s->seq_lens, s->max_seq_len, s->sm_scale,

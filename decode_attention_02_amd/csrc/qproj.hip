@@ -42,10 +42,14 @@ namespace mfa {
 // (they feed only output rows that are not written).
 constexpr int kGemmWaves = 8;
 
+// Columns N1 .. N-1 may come from a second weight matrix W2 (rows 0 ..
+// N-N1-1 of it; null W2: all from W), so two products that share A run as
+// one launch (the down-projection and the K/V projection share x).
 template <int MT, int NT, int PD, bool PACKED, bool PA>
 __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float* __restrict__ part,
-    uint16_t* __restrict__ out_bf16, int M, int N, int K, int kchunk) {
+    uint16_t* __restrict__ out_bf16, int M, int N, int K, int kchunk,
+    const uint16_t* __restrict__ W2, int N1) {
   constexpr int TM = MT * 16, TN = NT * 16;
   constexpr int kPad = TN + 4;                       // padded LDS row (floats)
   __shared__ __attribute__((aligned(16))) float red[kGemmWaves][TM * kPad];
@@ -63,15 +67,18 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
   __amdgpu_buffer_rsrc_t wr[NT];
   int wofs;
   constexpr int kStepBytes = PACKED ? 1024 : 64;
+  const bool second = W2 != nullptr && n0 >= N1;
+  const uint16_t* Wt = second ? W2 : W;
+  const int nw = second ? n0 - N1 : n0;              // first row of this tile in Wt
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const uint16_t* base;
     int bytes;
     if constexpr (PACKED) {
-      base = W + static_cast<size_t>((n0 / 16 + nt) * (K / 32) + kbeg / 32) * 64 * 8;
+      base = Wt + static_cast<size_t>((nw / 16 + nt) * (K / 32) + kbeg / 32) * 64 * 8;
       bytes = nsteps * 1024;
     } else {
-      base = W + static_cast<size_t>(n0 + nt * 16) * K + kbeg;
+      base = Wt + static_cast<size_t>(nw + nt * 16) * K + kbeg;
       bytes = (15 * K + kchunk) * 2;
     }
     wr[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
@@ -176,8 +183,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
 template <bool APPEND>
 __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __restrict__ part,
                                                              int ksplit, const float* __restrict__ g,
-                                                             int M, int R, float eps, void* out,
-                                                             int out_f32, int out_tiles,
+                                                             int M, int R, int pstride, float eps,
+                                                             void* out, int out_f32, int out_tiles,
                                                              AppendArgs app) {
   constexpr int kMaxChunks = 4;        // R <= 8192 = 4 chunks of 2048
   __shared__ float wsum[4];
@@ -187,7 +194,9 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
     if (m >= M) {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
       const int per = (gridDim.x - M) * 4;
-      for (int b = (m - M) * 4 + w; b < app.B; b += per) append_token(app, b, tid & 63);
+      const int first = app.kv_part ? app.kv_row0 : 0;
+      const int count = app.kv_part ? app.kv_rows : app.B;
+      for (int i = (m - M) * 4 + w; i < count; i += per) append_token(app, first + i, tid & 63);
       return;
     }
   }
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (k0 + u < ksplit) {
-            const float* p = part + (static_cast<size_t>(k0 + u) * M + m) * R + j0;
+            const float* p = part + (static_cast<size_t>(k0 + u) * M + m) * pstride + j0;
             a[u] = *reinterpret_cast<const float4*>(p);
             b[u] = *reinterpret_cast<const float4*>(p + 4);
           }
@@ -284,34 +293,32 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
   if (lane == 0) out[static_cast<size_t>(m) * N + n] = acc;
 }
 
+struct GemmCall {
+  const uint16_t *A, *W, *W2;
+  float* part;
+  uint16_t* out_bf16;
+  int M, N, K, kchunk, N1;
+};
+
 template <int MT, int NT, int PD, bool PACKED, bool PA>
-static void launch_gemm_shape(dim3 grid, const uint16_t* A, const uint16_t* W, float* part,
-                              uint16_t* out_bf16, int M, int N, int K, int kchunk,
-                              hipStream_t stream) {
+static void launch_gemm_shape(dim3 grid, const GemmCall& c, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED, PA>), grid, dim3(kGemmWaves * 64), 0,
-                     stream, A, W, part, out_bf16, M, N, K, kchunk);
+                     stream, c.A, c.W, c.part, c.out_bf16, c.M, c.N, c.K, c.kchunk, c.W2, c.N1);
 }
 
 template <bool PACKED, bool PA>
-static void launch_gemm_variant(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
-                                int M, int N, int K, int ksplit, int ntiles, hipStream_t stream) {
-  const int kchunk = K / ksplit;
+static void launch_gemm_variant(const GemmCall& c, int ksplit, int ntiles, hipStream_t stream) {
+  const int M = c.M;
   if (ntiles == 4) {
-    dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(ksplit));
-    if (M <= 16)
-      launch_gemm_shape<1, 4, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
-    else if (M <= 32)
-      launch_gemm_shape<2, 4, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
-    else
-      launch_gemm_shape<4, 4, 3, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+    dim3 grid(static_cast<unsigned>(c.N / 64), static_cast<unsigned>(ksplit));
+    if (M <= 16) launch_gemm_shape<1, 4, 4, PACKED, PA>(grid, c, stream);
+    else if (M <= 32) launch_gemm_shape<2, 4, 4, PACKED, PA>(grid, c, stream);
+    else launch_gemm_shape<4, 4, 3, PACKED, PA>(grid, c, stream);
   } else {
-    dim3 grid(static_cast<unsigned>(N / 32), static_cast<unsigned>(ksplit));
-    if (M <= 16)
-      launch_gemm_shape<1, 2, 8, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
-    else if (M <= 32)
-      launch_gemm_shape<2, 2, 6, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
-    else
-      launch_gemm_shape<4, 2, 4, PACKED, PA>(grid, A, W, part, out_bf16, M, N, K, kchunk, stream);
+    dim3 grid(static_cast<unsigned>(c.N / 32), static_cast<unsigned>(ksplit));
+    if (M <= 16) launch_gemm_shape<1, 2, 8, PACKED, PA>(grid, c, stream);
+    else if (M <= 32) launch_gemm_shape<2, 2, 6, PACKED, PA>(grid, c, stream);
+    else launch_gemm_shape<4, 2, 4, PACKED, PA>(grid, c, stream);
   }
 }
 
@@ -319,14 +326,16 @@ int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
-                            hipStream_t stream) {
+                            hipStream_t stream, const uint16_t* W2, int N1) {
   if (M < 1 || M > 64) return hipErrorInvalidValue;
+  if (W2 && (N1 <= 0 || N1 >= N || N1 % (16 * ntiles))) return hipErrorInvalidValue;
+  const GemmCall c{A, W, W2, part, out_bf16, M, N, K, K / ksplit, W2 ? N1 : N};
   if (a_packed) {
-    if (packed) launch_gemm_variant<true, true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
-    else launch_gemm_variant<false, true>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+    if (packed) launch_gemm_variant<true, true>(c, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, true>(c, ksplit, ntiles, stream);
   } else {
-    if (packed) launch_gemm_variant<true, false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
-    else launch_gemm_variant<false, false>(A, W, part, out_bf16, M, N, K, ksplit, ntiles, stream);
+    if (packed) launch_gemm_variant<true, false>(c, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, false>(c, ksplit, ntiles, stream);
   }
   return hipGetLastError();
 }
@@ -356,16 +365,20 @@ hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipS
 
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
                                  float eps, void* out, int out_f32, int out_tiles,
-                                 const AppendArgs* append, hipStream_t stream) {
+                                 const AppendArgs* append, hipStream_t stream, int part_stride) {
   if (out_tiles && (out_f32 || out_tiles * 16 < M || R % 32)) return hipErrorInvalidValue;
+  const int ps = part_stride > 0 ? part_stride : R;
+  if (ps < R) return hipErrorInvalidValue;
   if (append) {
-    const int extra = (append->B + 3) / 4 < 16 ? (append->B + 3) / 4 : 16;
+    const int count = append->kv_part ? append->kv_rows : append->B;
+    const int extra = (count + 3) / 4 < 16 ? (count + 3) / 4 : 16;
     hipLaunchKernelGGL(rmsnorm_reduce_kernel<true>, dim3(static_cast<unsigned>(M + extra)),
-                       dim3(256), 0, stream, part, ksplit, g, M, R, eps, out, out_f32, out_tiles,
-                       *append);
+                       dim3(256), 0, stream, part, ksplit, g, M, R, ps, eps, out, out_f32,
+                       out_tiles, *append);
   } else {
     hipLaunchKernelGGL(rmsnorm_reduce_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(256), 0,
-                       stream, part, ksplit, g, M, R, eps, out, out_f32, out_tiles, AppendArgs{});
+                       stream, part, ksplit, g, M, R, ps, eps, out, out_f32, out_tiles,
+                       AppendArgs{});
   }
   return hipGetLastError();
 }

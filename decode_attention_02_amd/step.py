@@ -81,10 +81,14 @@ class DecodeStep:
                                self.num_splits, self.chunk_tokens, out=self.out,
                                workspace=self.split_ws)
 
-    def __call__(self, k_new, v_new, pos, seq_lens, x=None, weights=None, q=None):
+    def __call__(self, k_new, v_new, pos, seq_lens, x=None, weights=None, q=None, w_kv=None):
         """q from x and weights=(w_qdown, g, w_qup) (or given), append, attend,
         as one mfa_decode_step call (the library shares launches between the
-        stages). Returns ``out``."""
+        stages). Returns ``out``.
+
+        With ``w_kv`` ([2d][hidden], W_k over W_v; needs x), the appended
+        token is the K/V projection of x; k_new / v_new are then optional
+        outputs receiving it ([B][d] in the activation dtype, or None)."""
         args = _lib.StepArgs()
         args.B, args.H, args.d = self.B, self.H, self.d
         args.dtype = api._DTYPES[self.act_dtype]
@@ -101,14 +105,29 @@ class DecodeStep:
             args.qproj_workspace = self.qproj_ws.data_ptr()
             args.qproj_workspace_bytes = self.qproj_ws.numel()
             q = self.q
-        for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (pos, "pos"),
-                     (seq_lens, "seq_lens")):
+        if w_kv is not None:
+            if x is None:
+                raise ValueError("the K/V projection needs x")
+            api._dev(w_kv, "w_kv")
+            args.w_kv = w_kv.data_ptr()
+            args.kv_in_dtype = args.dtype
+            for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+                if t is not None:
+                    api._dev(t, n)
+                    if t.dtype != self.act_dtype:
+                        raise ValueError(f"{n} must be {self.act_dtype} with the K/V projection")
+            args.k_new = k_new.data_ptr() if k_new is not None else None
+            args.v_new = v_new.data_ptr() if v_new is not None else None
+        else:
+            api._dev(k_new, "k_new")
+            api._dev(v_new, "v_new")
+            args.k_new, args.v_new = k_new.data_ptr(), v_new.data_ptr()
+            args.kv_in_dtype = api._DTYPES[k_new.dtype]
+        for t, n in ((q, "q"), (pos, "pos"), (seq_lens, "seq_lens")):
             api._dev(t, n)
         if pos.dtype != torch.int32 or seq_lens.dtype != torch.int32:
             raise ValueError("pos and seq_lens must be int32")
         args.q = q.data_ptr()
-        args.k_new, args.v_new = k_new.data_ptr(), v_new.data_ptr()
-        args.kv_in_dtype = api._DTYPES[k_new.dtype]
         args.pos = pos.data_ptr()
         args.cache = ctypes.pointer(self._desc)
         args.seq_lens = seq_lens.data_ptr()

@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define MFA_ABI_VERSION 1
+#define MFA_ABI_VERSION 2
 #define MFA_BLOCK_TOKENS 64
 
 typedef enum {
@@ -144,7 +144,9 @@ const char *mfa_status_str(int status);
  *          weights packed by mfa_pack_weight)
  * q_out    [B][H][d]            dtype
  * workspace: >= mfa_qproj_workspace_bytes(B, hidden, q_rank, H, d, dtype) bytes
- *          (fp32 split-K partials and the normalised latent n).
+ *          (fp32 split-K partials and the normalised latent n). The size also
+ *          covers mfa_decode_step with the K/V projection (w_kv set) for the
+ *          same arguments, d being the KV head dim.
  * dtype: MFA_BF16 (c kept in fp32; n and q rounded to bf16) or MFA_F32 (all
  * fp32). Limits: 1 <= B <= 256, q_rank <= 8192; bf16: hidden and q_rank
  * multiples of 256, H*d a multiple of 64; fp32: hidden and H*d multiples of 4,
@@ -267,6 +269,18 @@ mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
  *   k_new, v_new [B][d] of kv_in_dtype; pos [B] int32: as in mfa_kv_append
  *                with n_new == 1
  *   cache ... out_dtype: as in mfa_decode_attn
+ *   w_kv         optional K/V projection of the new token (the input side
+ *                of the attention instance's KV cache: "Step-3 is Large yet
+ *                Affordable" summary page, §7, attention instances own their
+ *                KV caches). NULL: k_new, v_new are inputs. Otherwise (x must
+ *                be set) w_kv is [2d][hidden] of dtype, W_k stacked over W_v
+ *                (torch Linear [out][in]; packed by mfa_pack_weight as one
+ *                2d x hidden matrix when weight_layout is packed), and
+ *                  k = x W_k^T,  v = x W_v^T   (fp32 accumulation)
+ *                rounded to dtype are appended at pos instead; k_new, v_new
+ *                are then optional outputs ([B][d] of dtype; NULL: not
+ *                written) and kv_in_dtype must equal dtype. The product
+ *                shares the down-projection's launch (x is read once).
  */
 typedef struct {
   int B, H, d, dtype;
@@ -289,6 +303,7 @@ typedef struct {
   size_t split_workspace_bytes;
   void *out;
   int out_dtype;
+  const void *w_kv;
 } mfa_step_args;
 
 mfa_status mfa_decode_step(const mfa_step_args *args, void *stream);

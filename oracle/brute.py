@@ -50,3 +50,14 @@ def query_projection(x: Sequence[Sequence[float]], w_qdown, g, w_qup, heads: int
         qf = matvec_t(w_qup, n)
         out.append([qf[h * head_dim:(h + 1) * head_dim] for h in range(heads)])
     return out
+
+
+def kv_projection(x: Sequence[Sequence[float]], w_kv, head_dim: int):
+    """Row by row: k = W_k x, v = W_v x, with W_k the first head_dim rows of
+    w_kv and W_v the next head_dim rows."""
+    ks, vs = [], []
+    for xb in x:
+        kv = matvec_t(w_kv, xb)
+        ks.append(kv[:head_dim])
+        vs.append(kv[head_dim:2 * head_dim])
+    return ks, vs

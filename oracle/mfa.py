@@ -73,6 +73,35 @@ def query_projection(x, w_qdown, g, w_qup, heads: int, head_dim: int,
     return q.reshape(x.shape[0], heads, head_dim)
 
 
+def kv_projection(x, w_kv, head_dim: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The new token's key and value: k = x W_k^T, v = x W_v^T.
+
+    x [B][Dm]; w_kv [2d][Dm] is W_k stacked over W_v (weights as [out][in]).
+    The attention instance computes them from the layer input and appends
+    them to the cache it owns (§7 Implementation and Results); the pages give
+    no positional rotation, so none is applied. Returns (k, v), each [B][d].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_kv, dtype=np.float64)
+    kv = x @ w.T                                              # [B][2d]
+    return kv[:, :head_dim], kv[:, head_dim:2 * head_dim]
+
+
+def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even of fp64 values to bfloat16 bit patterns.
+
+    bfloat16 keeps 8 significant bits and fp32's exponent range: each value
+    is rounded once, directly from fp64, to a multiple of 2^(e-8) (e its
+    binary exponent, 2^(e-1) <= |a| < 2^e; subnormal step 2^-133), ties to
+    even. Values must be finite and below the bf16 overflow threshold.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(a / step) * step                              # exact: fits 8 bits
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 # --------------------------------------------------------------------------
 # attention of H heads against one shared K/V head
 # --------------------------------------------------------------------------

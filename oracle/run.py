@@ -31,11 +31,32 @@ def query(inp: Dict, eps: float = DEFAULT_EPS) -> np.ndarray:
     return mfa.stored_to_f64(inp["q"], w.act_dtype).reshape(w.batch, w.heads, w.head_dim)
 
 
+def new_token(inp: Dict):
+    """Stored values (bf16 bits or fp32) of every sequence's new token, [B][d]
+    each: given (``k_new``, ``v_new``), or, with ``w_kv``, the K/V projection
+    of x rounded once to the activation dtype."""
+    if "w_kv" not in inp:
+        return inp["k_new"], inp["v_new"]
+    if "_projected_token" in inp:                 # computed once per input dict
+        return inp["_projected_token"]
+    w = inp["workload"]
+    a = w.act_dtype
+    k, v = mfa.kv_projection(mfa.stored_to_f64(inp["x"], a), mfa.stored_to_f64(inp["w_kv"], a),
+                             w.head_dim)
+    if a == "f32":
+        res = (k.astype(np.float32), v.astype(np.float32))
+    else:
+        res = (mfa.f64_to_bf16_bits(k), mfa.f64_to_bf16_bits(v))
+    inp["_projected_token"] = res
+    return res
+
+
 def sequence_tokens(inp: Dict, b: int):
     """Stored logical K and V rows (prefill + appended token) of sequence b."""
     o = inp["ctx_offsets"]
-    k = np.concatenate([inp["k_ctx"][o[b]:o[b + 1]], inp["k_new"][b:b + 1]])
-    v = np.concatenate([inp["v_ctx"][o[b]:o[b + 1]], inp["v_new"][b:b + 1]])
+    kn, vn = new_token(inp)
+    k = np.concatenate([inp["k_ctx"][o[b]:o[b + 1]], kn[b:b + 1]])
+    v = np.concatenate([inp["v_ctx"][o[b]:o[b + 1]], vn[b:b + 1]])
     return k, v
 
 

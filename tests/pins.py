@@ -18,6 +18,10 @@ What pins what:
 * rmsnorm / query projection -- output RMS equals 1 before the gain; scale
   invariance; constant input gives the gain; identity down-projection reduces
   to W_up x / rms(x); pure-Python brute force; head h owns columns h*d..h*d+d-1.
+* K/V projection -- block-identity weights give x's halves exactly; row
+  mapping of W_k / W_v; pure-Python brute force.
+* bf16 rounding -- anchor values including exact ties (to even) and values
+  next to them; torch's RNE cast of fp32 values; the half-ulp error bound.
 * e4m3 -- torch's float8_e4m3fn decode of all 256 codes; anchor values of the
   OCP format; round trip of every finite value; midpoints round to even;
   torch's RNE cast on random values.
@@ -50,6 +54,8 @@ def real_oracle():
         combine=mfa.combine,
         rmsnorm=mfa.rmsnorm,
         query_projection=mfa.query_projection,
+        kv_projection=mfa.kv_projection,
+        f64_to_bf16_bits=mfa.f64_to_bf16_bits,
         quantize_tokens=mfa.quantize_tokens,
         dequantize_tokens=mfa.dequantize_tokens,
         e4m3_decode=e4m3.decode,
@@ -247,6 +253,62 @@ def check_qproj(O):
     return fails
 
 
+# ---------------------------------------------------------------- K/V projection
+def check_kv_projection(O):
+    fails = []
+    rng = np.random.default_rng(11)
+    d = 3
+    # W_k = [I | 0], W_v = [0 | 2I] on Dm = 2d: k = x[:, :d], v = 2 x[:, d:]
+    x = rng.standard_normal((4, 2 * d))
+    w = np.zeros((2 * d, 2 * d))
+    w[:d, :d] = np.eye(d)
+    w[d:, d:] = 2.0 * np.eye(d)
+    k, v = O.kv_projection(x, w, d)
+    if not (np.array_equal(k, x[:, :d]) and np.array_equal(v, 2.0 * x[:, d:])):
+        fails.append("block-identity K/V projection closed form fails")
+    # row j of w_kv feeds k[:, j]; row d + j feeds v[:, j]
+    w = np.zeros((2 * d, 5)); w[1, 4] = 1.0; w[d + 2, 0] = -1.0
+    x = rng.standard_normal((2, 5))
+    k, v = O.kv_projection(x, w, d)
+    want_k = np.zeros((2, d)); want_k[:, 1] = x[:, 4]
+    want_v = np.zeros((2, d)); want_v[:, 2] = -x[:, 0]
+    if not (np.array_equal(k, want_k) and np.array_equal(v, want_v)):
+        fails.append("K/V projection row mapping is wrong")
+    # pure-Python brute force
+    x = rng.standard_normal((3, 7)); w = rng.standard_normal((2 * d, 7))
+    k, v = O.kv_projection(x, w, d)
+    bk, bv = O.brute.kv_projection(x.tolist(), w.tolist(), d)
+    if not (_close(k, np.array(bk), 1e-13) and _close(v, np.array(bv), 1e-13)):
+        fails.append("K/V projection differs from brute force")
+    return fails
+
+
+def check_bf16_round(O):
+    import torch
+    fails = []
+    anchors = {1.0: 0x3F80, -2.0: 0xC000, 0.0: 0x0000, 3.140625: 0x4049,
+               1.0 + 2.0 ** -8: 0x3F80,                    # tie -> even mantissa 0
+               1.0 + 3 * 2.0 ** -8: 0x3F82,                # tie -> even mantissa 2
+               1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,       # just above the tie
+               -(1.0 + 2.0 ** -8 - 2.0 ** -30): 0xBF80}    # just below the tie
+    got = O.f64_to_bf16_bits(np.array(list(anchors)))
+    for (val, want), g in zip(anchors.items(), got.tolist()):
+        if g != want:
+            fails.append(f"bf16 rounding of {val!r}: {g:#06x} != {want:#06x}")
+    # torch's round-to-nearest-even cast on fp32 values (exact in fp64)
+    rng = np.random.default_rng(12)
+    a32 = (rng.standard_normal(4096) * np.exp2(rng.integers(-20, 20, 4096))).astype(np.float32)
+    ref = torch.from_numpy(a32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if not np.array_equal(O.f64_to_bf16_bits(a32.astype(np.float64)), ref):
+        fails.append("bf16 rounding differs from torch's cast")
+    # error bound: half a unit in the 8th significant bit
+    a = rng.standard_normal(4096) * 1e3
+    r = (O.f64_to_bf16_bits(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if not np.all(np.abs(r - a) <= np.abs(a) * 2.0 ** -8):
+        fails.append("bf16 rounding error above half an ulp")
+    return fails
+
+
 # ---------------------------------------------------------------- e4m3
 def check_e4m3(O):
     import torch
@@ -378,8 +440,8 @@ def check_layout(O):
     return fails
 
 
-ALL_CHECKS = (check_attention, check_gather, check_combine, check_qproj, check_e4m3,
-              check_quantize, check_cost, check_layout)
+ALL_CHECKS = (check_attention, check_gather, check_combine, check_qproj, check_kv_projection,
+              check_bf16_round, check_e4m3, check_quantize, check_cost, check_layout)
 
 
 def run_all(O):

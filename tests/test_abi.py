@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mfa_abi_version() == 1
+    assert lib.mfa_abi_version() == _lib.ABI_VERSION == 2
     for s in range(8):
         assert lib.mfa_status_str(s)
     assert lib.mfa_status_str(99) == b"unknown status"
@@ -201,3 +201,17 @@ def test_decode_step_validation(lib):
     a.hidden = 7168
     a.qproj_workspace, a.qproj_workspace_bytes = None, 0
     assert ok() == WS
+    # K/V projection: needs x, an aligned weight, kv_in_dtype == dtype; k_new, v_new optional
+    a.qproj_workspace, a.qproj_workspace_bytes = P, 1 << 30
+    a.w_kv = PM
+    assert ok() == ALIGN
+    a.w_kv = P
+    a.kv_in_dtype = F32
+    assert ok() == DTYPE
+    a.kv_in_dtype = BF16
+    a.k_new = a.v_new = None
+    a.pos = None
+    assert ok() == NULL                                          # pos still required
+    a.pos = P
+    a.x = None
+    assert ok() == NULL                                          # projection without x

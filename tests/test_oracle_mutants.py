@@ -121,7 +121,35 @@ def _k_blocks_gc_swapped(rows, dt):
     return np.ascontiguousarray(x).reshape(x.shape[0], -1)
 
 
+def _kv_swapped(x, w, d):
+    k, v = mfa.kv_projection(x, w, d)
+    return v, k
+
+
+def _kv_rows_offset(x, w, d):
+    # the weight rows read one row off (W_k / W_v halves misaligned)
+    kv = np.asarray(x, float) @ np.roll(np.asarray(w, float), 1, axis=0).T
+    return kv[:, :d], kv[:, d:2 * d]
+
+
+def _bf16_truncate(a):
+    a32 = np.asarray(a, np.float64).astype(np.float32)
+    return (a32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_ties_away(a):
+    a = np.asarray(a, np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.sign(a) * np.floor(np.abs(a) / step + 0.5) * step
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 MUTANTS = {
+    "kv_projection_k_v_swapped": dict(kv_projection=_kv_swapped),
+    "kv_projection_rows_offset": dict(kv_projection=_kv_rows_offset),
+    "bf16_round_truncates": dict(f64_to_bf16_bits=_bf16_truncate),
+    "bf16_round_ties_away": dict(f64_to_bf16_bits=_bf16_ties_away),
     "attention_missing_scale": dict(softmax_attention=_attn_no_scale),
     "attention_softmax_over_heads": dict(softmax_attention=_attn_heads_axis),
     "attention_drops_last_token": dict(softmax_attention=_attn_drop_last),

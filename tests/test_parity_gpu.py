@@ -343,6 +343,78 @@ def test_fused_step_matches_staged(gpu_lib, idx, shrink):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("idx,shrink,packed", [
+    (2, dict(batch=6, hidden=1024, q_rank=512, context=300), False),
+    (2, dict(batch=6, hidden=1024, q_rank=512, context=300), True),
+    (2, dict(batch=70, hidden=512, q_rank=256, context=130), True),     # two row passes
+    (2, dict(batch=5, hidden=512, q_rank=256, context=200, kv_dtype="fp8", paged=True), True),
+    (5, dict(batch=3, context=300), True),
+    (1, {}, False),                                                     # fp32 path
+], ids=["bf16", "bf16-packed", "bf16-two-passes", "fp8-paged", "split", "f32"])
+def test_kv_projection_step(gpu_lib, idx, shrink, packed):
+    """The K/V projection fused into the step (w_kv): the new token equals
+    the oracle's x W_k^T, x W_v^T rounded to the activation dtype; the cache
+    holds exactly what mfa_kv_append writes from the step's k/v outputs; the
+    attention output matches the oracle step with the projected token."""
+    import decode_attention_02_amd as mfa
+    w = dataclasses.replace(W[idx], **shrink)
+    inp = workloads.make_inputs(idx, workload=w, seed=31, kv_proj=True)
+    say(f"kv projection: {w.name} {shrink} packed={packed}")
+    act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
+    res = {}
+    for mode in ("fused", "staged"):
+        T, cache, step = setup(inp, num_splits=3 if (w.context or 0) > 256 else None)
+        wts = (T["w_qdown"], T["g"], T["w_qup"])
+        wkv = T["w_kv"]
+        if packed:
+            step.packed_weights = True
+            wts = (mfa.pack_weight(wts[0]), wts[1], mfa.pack_weight(wts[2]))
+            wkv = mfa.pack_weight(wkv)
+        if mode == "fused":
+            k_out = torch.empty((w.batch, w.head_dim), dtype=act, device="cuda")
+            v_out = torch.empty_like(k_out)
+            out = step(k_out, v_out, T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts,
+                       w_kv=wkv)
+            torch.cuda.synchronize()
+            res["k"], res["v"] = k_out.clone(), v_out.clone()
+        else:
+            out = step.staged(res["k"], res["v"], T["prefill_lens"], T["seq_lens"], x=T["x"],
+                              weights=wts)
+            torch.cuda.synchronize()
+        rows = list(cache_rows(cache))
+        if cache.dtype == "fp8":
+            rows += [cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()]
+        res[mode] = (out.detach().cpu().clone(), rows)
+    # 1. the projected token against the oracle's exact projection
+    kx, vx = omfa.kv_projection(omfa.stored_to_f64(inp["x"], w.act_dtype),
+                                omfa.stored_to_f64(inp["w_kv"], w.act_dtype), w.head_dim)
+    for got, want, n in ((to_np(res["k"]), kx, "k"), (to_np(res["v"]), vx, "v")):
+        r = rel_l2(got, want)
+        if w.act_dtype == "f32":
+            say(f"projected {n}: rel_l2={r:.3e}")
+            assert r <= REL_L2_F32
+        else:
+            # one bf16 rounding of a value that differs from the exact one by
+            # the fp32 accumulation only: within one unit in the 8th bit
+            err = np.abs(got - want) / np.maximum(np.abs(want), 1e-30)
+            say(f"projected {n}: rel_l2={r:.3e} max rel={err.max():.3e}")
+            assert r <= REL_L2_BF16 and np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-6)
+    # 2. fused cache == append of the step's own k/v outputs (bit for bit);
+    # the outputs are not compared bit for bit: with the K/V columns the
+    # down-projection may split K differently, so q can differ in its last bits
+    for a, b in zip(res["fused"][1], res["staged"][1]):
+        assert np.array_equal(a, b)
+    # 3. attention output against the oracle step with the projected token
+    want = orun.decode_step(inp)["o"]
+    got = to_np(res["fused"][0])
+    if w.act_dtype == "f32":
+        r = rel_l2(got, want)
+        say(f"kv projection f32 step: rel_l2={r:.3e}")
+        assert r <= REL_L2_F32
+    else:
+        check_bf16(got, want, "kv projection step")
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

@@ -102,7 +102,7 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = None,
                 context: Optional[int] = None, workload: Optional[Workload] = None,
-                prefill_lens=None):
+                prefill_lens=None, kv_proj: bool = False):
     """Draw the inputs of one decode step of workload ``index``.
 
     ``batch`` / ``context`` shrink the workload (for tests that need a small
@@ -114,6 +114,10 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
     sequence-major) with ``ctx_offsets`` [B+1]; ``k_new, v_new`` [B][d];
     ``prefill_lens`` and ``seq_lens`` [B] int32; ``block_table`` [B][max_blocks]
     int32 or None; ``num_blocks``, ``max_blocks_per_seq``; plus the workload.
+    ``kv_proj`` (query-path workloads only) also draws ``w_kv`` [2d][hidden]
+    (W_k over W_v, N(0, 1/hidden)) after everything else, so the other
+    arrays are the same with and without it; the new token is then the K/V
+    projection of x and ``k_new`` / ``v_new`` are not its values.
     """
     w = workload if workload is not None else WORKLOADS[index]
     if batch is not None or context is not None:
@@ -185,6 +189,13 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
         out["block_table"] = None
         out["num_blocks"] = B * max_blocks
     out["max_blocks_per_seq"] = max_blocks
+
+    # 5. K/V projection weights (drawn last)
+    if kv_proj:
+        if not w.has_qproj:
+            raise ValueError("the K/V projection needs a query-path workload (x)")
+        out["w_kv"] = _store(rng.standard_normal((2 * d, w.hidden), dtype=np.float32)
+                             / np.float32(math.sqrt(w.hidden)), act)
     return out
 
 
@@ -207,6 +218,8 @@ def to_torch(inp, device="cuda"):
     if w.has_qproj:
         for k in ("x", "w_qdown", "w_qup"):
             out[k] = t(inp[k], w.act_dtype)
+        if "w_kv" in inp:
+            out["w_kv"] = t(inp["w_kv"], w.act_dtype)
         out["g"] = torch.from_numpy(inp["g"]).to(device)
     else:
         out["q"] = t(inp["q"], w.act_dtype)

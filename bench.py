@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-proj", action="store_true",
+                    help="compute the new token's K/V from x in the step (w_kv) instead of "
+                         "reading it (query-path workloads)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for HBM counters)")
@@ -137,7 +140,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.WORKLOADS[args.config]
-    inp = workloads.make_inputs(args.config)
+    if args.kv_proj and not w.has_qproj:
+        print("--kv-proj needs a workload with a query path (configs 1, 2, 5)", file=sys.stderr)
+        sys.exit(2)
+    inp = workloads.make_inputs(args.config, kv_proj=args.kv_proj)
     T = workloads.to_torch(inp, dev)
     act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     B = w.batch
@@ -147,6 +153,8 @@ def main():
     w_bytes = 0
     if w.has_qproj:
         w_bytes = (T["w_qdown"].numel() + T["w_qup"].numel()) * T["w_qup"].element_size()
+        if args.kv_proj:
+            w_bytes += T["w_kv"].numel() * T["w_kv"].element_size()
     rotate = args.rotate or max(2, min(8, -(-2 * 256 * 2 ** 20 // max(kv_bytes + w_bytes, 1))))
 
     sets = []
@@ -158,14 +166,16 @@ def main():
         packed = w.has_qproj and w.act_dtype == "bf16"
         step = DecodeStep(cache, B, w.heads, maxlen, hidden=w.hidden, q_rank=w.q_rank,
                           act_dtype=act, num_splits=ns, packed_weights=packed, device=dev)
-        wts = None
+        wts, wkv = None, None
         if w.has_qproj:
             # weights are static: packed once into operand order, like a load step
             if packed:
                 wts = (mfa.pack_weight(T["w_qdown"]), T["g"].clone(), mfa.pack_weight(T["w_qup"]))
+                wkv = mfa.pack_weight(T["w_kv"]) if args.kv_proj else None
             else:
                 wts = (T["w_qdown"].clone(), T["g"].clone(), T["w_qup"].clone())
-        sets.append((step, wts))
+                wkv = T["w_kv"].clone() if args.kv_proj else None
+        sets.append((step, wts, wkv))
     torch.cuda.synchronize()
 
     def attention(i, q):
@@ -180,9 +190,10 @@ def main():
     def one(i):
         """One decode step on buffer set i % rotate (DecodeStep: query path,
         KV append, attention, split combine)."""
-        step, wts = sets[i % rotate]
+        step, wts, wkv = sets[i % rotate]
         if w.has_qproj:
-            step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts)
+            step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts,
+                 w_kv=wkv)
         else:
             step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
 
@@ -257,7 +268,8 @@ def main():
                    "head_dim": w.head_dim, "kv_dtype": w.kv_dtype, "hidden": w.hidden,
                    "q_rank": w.q_rank, "paged": w.paged, "num_splits": step0.num_splits,
                    "chunk_tokens": step0.chunk_tokens, "rotate": rotate,
-                   "step": "qproj+kv_append+decode_attn+combine" if w.has_qproj
+                   "step": ("qproj+kv_proj+kv_append+decode_attn+combine" if args.kv_proj
+                            else "qproj+kv_append+decode_attn+combine") if w.has_qproj
                    else "kv_append+decode_attn+combine"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

@@ -35,12 +35,33 @@ __device__ __forceinline__ void append_token_wave(const AppendArgs& a, int b, in
     const size_t prow = static_cast<size_t>(b - a.kv_row0) * a.kv_stride + a.kv_col0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) { xk[e] = 0.f; xv[e] = 0.f; }
-    for (int ks = 0; ks < a.kv_ks; ++ks) {
-      const float* pr = a.kv_part + static_cast<size_t>(ks) * a.kv_rows * a.kv_stride + prow;
+    // slices in groups of 8 with all loads of a group in flight at once
+    for (int k0 = 0; k0 < a.kv_ks; k0 += 8) {
+      float tk[8][EPT], tv[8][EPT];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        xk[e] += pr[lane * EPT + e];
-        xv[e] += pr[d + lane * EPT + e];
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < a.kv_ks) {
+          const float* pr = a.kv_part + static_cast<size_t>(k0 + u) * a.kv_rows * a.kv_stride + prow;
+          if constexpr (EPT == 4) {   // 16-byte aligned: strides and column offsets are multiples of 4
+            const float4 k4 = *reinterpret_cast<const float4*>(pr + lane * 4);
+            const float4 v4 = *reinterpret_cast<const float4*>(pr + d + lane * 4);
+            tk[u][0] = k4.x; tk[u][1] = k4.y; tk[u][2] = k4.z; tk[u][3] = k4.w;
+            tv[u][0] = v4.x; tv[u][1] = v4.y; tv[u][2] = v4.z; tv[u][3] = v4.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+              tk[u][e] = pr[lane * EPT + e];
+              tv[u][e] = pr[d + lane * EPT + e];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < a.kv_ks) {
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) { xk[e] += tk[u][e]; xv[e] += tv[u][e]; }
+        }
       }
     }
 #pragma unroll

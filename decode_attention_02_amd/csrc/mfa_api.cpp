@@ -32,17 +32,33 @@ struct GemmPlan {
 };
 
 // Wide outputs (>= 512 tiles of 32 columns) run one K slice on 32-column
-// tiles; narrower ones use 64-column tiles and halve K until the grid reaches
-// 256 workgroups or a slice would drop below 16 k-steps of 32 (two per wave).
-GemmPlan plan_gemm(int N, int K) {
+// tiles; narrower ones use 64-column tiles (80 when that fills the 256
+// compute units better: the down-projection with the K/V columns, 2560
+// columns, is 32 x 8 workgroups of 80 columns instead of 40 x 8 of 64) and
+// halve K until the grid reaches 256 workgroups or a slice would drop below
+// 16 k-steps of 32 (two per wave).
+GemmPlan plan_gemm(int N, int K, int rows) {
   if (N % 32 == 0 && N / 32 >= 512) return GemmPlan{2, 1};
-  GemmPlan p{N % 64 == 0 ? 4 : 2, 1};
-  const int tiles = N / (16 * p.ntiles);
-  const int steps = K / 32;
-  while (static_cast<long long>(tiles) * p.ks < 256 && steps % (p.ks * 2) == 0 &&
-         steps / (p.ks * 2) >= 16)
-    p.ks *= 2;
-  return p;
+  auto split = [&](int ntiles) {
+    GemmPlan p{ntiles, 1};
+    const int tiles = N / (16 * ntiles);
+    const int steps = K / 32;
+    while (static_cast<long long>(tiles) * p.ks < 256 && steps % (p.ks * 2) == 0 &&
+           steps / (p.ks * 2) >= 16)
+      p.ks *= 2;
+    return p;
+  };
+  // fraction of the last round of 256 workgroups that is busy
+  auto fill = [&](const GemmPlan& p) {
+    const long long wg = static_cast<long long>(N / (16 * p.ntiles)) * p.ks;
+    return static_cast<double>(wg) / (256.0 * static_cast<double>((wg + 255) / 256));
+  };
+  GemmPlan best = split(N % 64 == 0 ? 4 : 2);
+  if (N % 80 == 0 && rows <= 32) {      // 80-column tiles hold at most 32 rows
+    const GemmPlan p5 = split(5);
+    if (fill(p5) > fill(best) + 1e-9) best = p5;
+  }
+  return best;
 }
 
 struct QprojPlan {
@@ -56,9 +72,9 @@ QprojPlan plan_qproj(int B, int hidden, int q_rank, int HD, int dtype, int kvc) 
   QprojPlan p{};
   p.rows = B < kRowsPerPass ? B : kRowsPerPass;
   if (dtype == MFA_BF16) {
-    p.down = plan_gemm(q_rank, hidden);
-    p.down_kv = plan_gemm(q_rank + kvc, hidden);
-    p.up = plan_gemm(HD, q_rank);
+    p.down = plan_gemm(q_rank, hidden, p.rows);
+    p.down_kv = plan_gemm(q_rank + kvc, hidden, p.rows);
+    p.up = plan_gemm(HD, q_rank, p.rows);
     p.off_part_down = 0;
     const size_t part_q = static_cast<size_t>(p.down.ks) * p.rows * q_rank * 4;
     const size_t part_kv = static_cast<size_t>(p.down_kv.ks) * p.rows * (q_rank + kvc) * 4;

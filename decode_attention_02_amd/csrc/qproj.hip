@@ -67,18 +67,20 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
   __amdgpu_buffer_rsrc_t wr[NT];
   int wofs;
   constexpr int kStepBytes = PACKED ? 1024 : 64;
-  const bool second = W2 != nullptr && n0 >= N1;
-  const uint16_t* Wt = second ? W2 : W;
-  const int nw = second ? n0 - N1 : n0;              // first row of this tile in Wt
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    // 16-row group nt of the tile: from W2 at and past column N1
+    const int col = n0 + nt * 16;
+    const bool second = W2 != nullptr && col >= N1;
+    const uint16_t* Wt = second ? W2 : W;
+    const int nw = second ? col - N1 : col;          // its first row in Wt
     const uint16_t* base;
     int bytes;
     if constexpr (PACKED) {
-      base = Wt + static_cast<size_t>((nw / 16 + nt) * (K / 32) + kbeg / 32) * 64 * 8;
+      base = Wt + static_cast<size_t>((nw / 16) * (K / 32) + kbeg / 32) * 64 * 8;
       bytes = nsteps * 1024;
     } else {
-      base = Wt + static_cast<size_t>(nw + nt * 16) * K + kbeg;
+      base = Wt + static_cast<size_t>(nw) * K + kbeg;
       bytes = (15 * K + kchunk) * 2;
     }
     wr[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
@@ -140,8 +142,23 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w][(mt * 16 + 4 * g + i) * kPad + nt * 16 + c] = acc[mt][nt][i];
   __syncthreads();
-  constexpr int kPer = TM * TN / (kGemmWaves * 64);  // outputs per thread (contiguous in n)
-  static_assert(kPer == 1 || kPer % 2 == 0, "one or pairs of outputs per thread");
+  constexpr int kOut = TM * TN;
+  if constexpr (kOut % (kGemmWaves * 64) != 0 || (kOut / (kGemmWaves * 64)) % 2 == 1) {
+    // tile sizes that do not split into pairs per thread: one output at a time
+    for (int e = tid; e < kOut; e += kGemmWaves * 64) {
+      const int m = e / TN, nl = e % TN;
+      if (m >= M) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][m * kPad + nl];
+      if (out_bf16)
+        __builtin_nontemporal_store(f32_to_bf16(sum), out_bf16 + static_cast<size_t>(m) * N + n0 + nl);
+      else
+        store_nt(part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl, sum);
+    }
+    return;
+  }
+  constexpr int kPer = kOut / (kGemmWaves * 64);     // outputs per thread (contiguous in n)
   const int e0 = tid * kPer;
   const int m = e0 / TN, nl = e0 % TN;
   if (m < M) {
@@ -193,10 +210,14 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
   if constexpr (APPEND) {
     if (m >= M) {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+      if (app.kv_part) {
+        // projected tokens: one sequence per workgroup (wave 0), so the K-slice
+        // partials of the rows are read by as many compute units as rows
+        if (w == 0) append_token(app, app.kv_row0 + (m - M), tid & 63);
+        return;
+      }
       const int per = (gridDim.x - M) * 4;
-      const int first = app.kv_part ? app.kv_row0 : 0;
-      const int count = app.kv_part ? app.kv_rows : app.B;
-      for (int i = (m - M) * 4 + w; i < count; i += per) append_token(app, first + i, tid & 63);
+      for (int b = (m - M) * 4 + w; b < app.B; b += per) append_token(app, b, tid & 63);
       return;
     }
   }
@@ -314,6 +335,11 @@ static void launch_gemm_variant(const GemmCall& c, int ksplit, int ntiles, hipSt
     if (M <= 16) launch_gemm_shape<1, 4, 4, PACKED, PA>(grid, c, stream);
     else if (M <= 32) launch_gemm_shape<2, 4, 4, PACKED, PA>(grid, c, stream);
     else launch_gemm_shape<4, 4, 3, PACKED, PA>(grid, c, stream);
+  } else if (ntiles == 5) {
+    dim3 grid(static_cast<unsigned>(c.N / 80), static_cast<unsigned>(ksplit));
+    // (64 rows x 80 columns would need more LDS than a CU has for the reduction)
+    if (M <= 16) launch_gemm_shape<1, 5, 4, PACKED, PA>(grid, c, stream);
+    else launch_gemm_shape<2, 5, 4, PACKED, PA>(grid, c, stream);
   } else {
     dim3 grid(static_cast<unsigned>(c.N / 32), static_cast<unsigned>(ksplit));
     if (M <= 16) launch_gemm_shape<1, 2, 8, PACKED, PA>(grid, c, stream);
@@ -328,7 +354,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, u
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
                             hipStream_t stream, const uint16_t* W2, int N1) {
   if (M < 1 || M > 64) return hipErrorInvalidValue;
-  if (W2 && (N1 <= 0 || N1 >= N || N1 % (16 * ntiles))) return hipErrorInvalidValue;
+  if (ntiles != 2 && ntiles != 4 && ntiles != 5) return hipErrorInvalidValue;
+  if (ntiles == 5 && M > 32) return hipErrorInvalidValue;
+  if (N % (16 * ntiles)) return hipErrorInvalidValue;
+  if (W2 && (N1 <= 0 || N1 >= N || N1 % 16)) return hipErrorInvalidValue;
   const GemmCall c{A, W, W2, part, out_bf16, M, N, K, K / ksplit, W2 ? N1 : N};
   if (a_packed) {
     if (packed) launch_gemm_variant<true, true>(c, ksplit, ntiles, stream);
@@ -370,8 +399,10 @@ hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, 
   const int ps = part_stride > 0 ? part_stride : R;
   if (ps < R) return hipErrorInvalidValue;
   if (append) {
-    const int count = append->kv_part ? append->kv_rows : append->B;
-    const int extra = (count + 3) / 4 < 16 ? (count + 3) / 4 : 16;
+    // given tokens: one wave per sequence, at most 16 workgroups; projected
+    // tokens (<= 64 rows per pass): one workgroup per sequence
+    const int extra = append->kv_part ? append->kv_rows
+                                      : ((append->B + 3) / 4 < 16 ? (append->B + 3) / 4 : 16);
     hipLaunchKernelGGL(rmsnorm_reduce_kernel<true>, dim3(static_cast<unsigned>(M + extra)),
                        dim3(256), 0, stream, part, ksplit, g, M, R, ps, eps, out, out_f32,
                        out_tiles, *append);

@@ -348,9 +348,10 @@ def test_fused_step_matches_staged(gpu_lib, idx, shrink):
     (2, dict(batch=6, hidden=1024, q_rank=512, context=300), True),
     (2, dict(batch=70, hidden=512, q_rank=256, context=130), True),     # two row passes
     (2, dict(batch=5, hidden=512, q_rank=256, context=200, kv_dtype="fp8", paged=True), True),
-    (5, dict(batch=3, context=300), True),
+    (5, dict(batch=3, context=300), True),                              # 80-column tiles, 16 rows
+    (2, dict(batch=24, context=130), True),                             # 80-column tiles, 32 rows
     (1, {}, False),                                                     # fp32 path
-], ids=["bf16", "bf16-packed", "bf16-two-passes", "fp8-paged", "split", "f32"])
+], ids=["bf16", "bf16-packed", "bf16-two-passes", "fp8-paged", "split", "full-width", "f32"])
 def test_kv_projection_step(gpu_lib, idx, shrink, packed):
     """The K/V projection fused into the step (w_kv): the new token equals
     the oracle's x W_k^T, x W_v^T rounded to the activation dtype; the cache

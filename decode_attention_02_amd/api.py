@@ -197,6 +197,42 @@ def decode_attn(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq
     return out if (num_splits == 1 or combine) else None
 
 
+def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq_len: int,
+                      sm_scale: Optional[float] = None, num_splits: int = 1,
+                      chunk_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None,
+                      combine: bool = True) -> Optional[torch.Tensor]:
+    """Attention of q [B][q_len][H][d] (the last q_len tokens of every sequence,
+    causal among themselves) over the cache (mfa_decode_attn_multi); out is
+    [B][q_len][H][d]. Splits and ``combine`` as in ``decode_attn``, over the
+    B * q_len rows."""
+    lib = _lib.load()
+    B, T, H, d = q.shape
+    _dev(q, "q")
+    _dev(seq_lens, "seq_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if chunk_tokens is None:
+        per = -(-max(max_seq_len, 1) // num_splits)
+        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+    if out_dtype is None:
+        out_dtype = q.dtype
+    if out is None and (num_splits == 1 or combine):
+        out = torch.empty((B, T, H, d), dtype=out_dtype, device=q.device)
+    if num_splits > 1 and workspace is None:
+        workspace = torch.empty(split_workspace_bytes(B * T, H, d, num_splits), dtype=torch.uint8,
+                                device=q.device)
+    desc = cache.desc()
+    check("mfa_decode_attn_multi", lib.mfa_decode_attn_multi(
+        _ptr(q), _DTYPES[q.dtype], B, T, H, ctypes.byref(desc), _ptr(seq_lens), int(max_seq_len),
+        float(sm_scale), int(num_splits), int(chunk_tokens), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0,
+        _ptr(out) if (num_splits == 1 or combine) else None, _DTYPES[out_dtype],
+        _stream(q.device)))
+    return out if (num_splits == 1 or combine) else None
+
+
 def combine_splits(workspace: torch.Tensor, batch: int, heads: int, head_dim: int, num_splits: int,
                    out: Optional[torch.Tensor] = None,
                    out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:

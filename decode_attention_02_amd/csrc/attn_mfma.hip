@@ -123,10 +123,14 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int hg = id % kHS;
   const int split = (id / kHS) % a.num_splits;
-  const int b = id / kHS / a.num_splits;
+  const int b = id / kHS / a.num_splits;                                // virtual row (q, partials, out)
   const int h0 = hg * kHW;                                              // first head
+  const int ql = a.q_len > 0 ? a.q_len : 1;
+  const int bs = b / ql;                                                // its sequence (cache, lengths)
+  const int jq = b - bs * ql;                                           // its query token
 
-  int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[b];
+  // query token jq sees the sequence up to and including itself
+  int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[bs] - (ql - 1 - jq);
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int t0 = split * a.chunk_tokens;
   const int t1 = min(t0 + a.chunk_tokens, L);
@@ -179,11 +183,11 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // join the vector-memory counter the K/V ring waits on.
   using cint = const __attribute__((address_space(4))) int;
   cint* bt_row = a.block_table
-                     ? (cint*)a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
+                     ? (cint*)a.block_table + static_cast<size_t>(bs) * a.max_blocks_per_seq
                      : nullptr;
   auto phys = [&](int n) __attribute__((always_inline)) -> size_t {   // physical id of the workgroup's n-th block
     const int j = blk0 + n;
-    int pid = bt_row ? bt_row[j] : b * a.max_blocks_per_seq + j;
+    int pid = bt_row ? bt_row[j] : bs * a.max_blocks_per_seq + j;
     pid = pid < 0 ? 0 : (pid >= a.num_blocks ? a.num_blocks - 1 : pid);
     return static_cast<size_t>(pid);
   };

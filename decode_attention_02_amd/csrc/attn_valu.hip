@@ -30,8 +30,11 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
   const int HD = H * D;
   const int tid = threadIdx.x;
   const int split = blockIdx.x % a.num_splits;
-  const int b = blockIdx.x / a.num_splits;
-  int L = a.seq_lens[b];
+  const int b = blockIdx.x / a.num_splits;          // virtual row (q, partials, out)
+  const int ql = a.q_len > 0 ? a.q_len : 1;
+  const int bs = b / ql;                            // its sequence (cache, lengths)
+  const int jq = b - bs * ql;                       // its query token: sees the sequence up to itself
+  int L = a.seq_lens[bs] - (ql - 1 - jq);
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int t0 = split * a.chunk_tokens;
   const int t1 = min(t0 + a.chunk_tokens, L);
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
   float o[kMaxPerThread];
 #pragma unroll
   for (int r = 0; r < kMaxPerThread; ++r) o[r] = 0.f;
-  const int* bt_row = a.block_table ? a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq
+  const int* bt_row = a.block_table ? a.block_table + static_cast<size_t>(bs) * a.max_blocks_per_seq
                                     : nullptr;
   float kr[kPer], vr[kPer];
   auto load_tile = [&](int tt) {               // element i = tid + 256 r: token i / D, dim i % D
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
       float kv = 0.f, vv = 0.f;
       if (t < n) {
         const int tok = tt + t;
-        int id = bt_row ? bt_row[tok >> 6] : b * a.max_blocks_per_seq + (tok >> 6);
+        int id = bt_row ? bt_row[tok >> 6] : bs * a.max_blocks_per_seq + (tok >> 6);
         id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
         const int off = tok & 63;
         if (a.kv_f32) {

@@ -33,8 +33,15 @@ struct AttnArgs {
   float* part_ml;             // [B][S][H][2]
   void* out;                  // [B][H][d] when num_splits == 1
   int out_f32;
+  // Query tokens per sequence (>= 1). Rows of q, the partials and out are
+  // virtual rows r = b * q_len + j (query token j of sequence b); row r reads
+  // sequence b's cache (block table row b, seq_lens[b]) and attends to its
+  // first seq_lens[b] - (q_len - 1 - j) tokens: causal among the new tokens,
+  // which are the last q_len of the sequence.
+  int q_len;
 };
 
+// B: virtual rows (sequences x q_len).
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
 

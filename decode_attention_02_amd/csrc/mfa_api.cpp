@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int kBlock = MFA_BLOCK_TOKENS;
+constexpr int kMaxQueryTokens = MFA_MAX_QUERY_TOKENS;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -409,10 +410,12 @@ struct AttnCall {
   void* out;
 };
 
+// q_len query tokens per sequence: the rows of q, the partials and out are
+// the B * q_len virtual rows (sequence, query token).
 mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
                         const int32_t* seq_lens, int max_seq_len, float sm_scale, int num_splits,
                         int chunk_tokens, void* workspace, size_t workspace_bytes, void* out,
-                        int out_dtype, AttnCall* c) {
+                        int out_dtype, AttnCall* c, int q_len = 1) {
   if (!q || !seq_lens) return MFA_ERR_NULL;
   const mfa_status cs = check_cache(cache);
   if (cs != MFA_OK) return cs;
@@ -421,6 +424,9 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
     return MFA_ERR_ALIGN;
   const int d = cache->head_dim;
   if (B < 1 || H < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
+  if (q_len < 1 || q_len > kMaxQueryTokens) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(B) * q_len > 0x7fffffffll / 64) return MFA_ERR_SHAPE;
+  const int Bv = B * q_len;                       // virtual rows
   if (static_cast<long long>(max_seq_len) > static_cast<long long>(cache->max_blocks_per_seq) * kBlock)
     return MFA_ERR_SHAPE;
   if (!cache->block_table &&
@@ -428,7 +434,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
     return MFA_ERR_SHAPE;
   if (num_splits < 1 || chunk_tokens < kBlock || chunk_tokens % kBlock) return MFA_ERR_SHAPE;
   if (static_cast<long long>(num_splits) * chunk_tokens < max_seq_len) return MFA_ERR_SHAPE;
-  if (static_cast<long long>(B) * num_splits > 0x7fffffffll) return MFA_ERR_SHAPE;
+  if (static_cast<long long>(Bv) * num_splits > 0x7fffffffll / 64) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return MFA_ERR_SHAPE;
   c->mfma = mfma_shape(H, d, cache->dtype);
@@ -443,7 +449,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
     if (!out) return MFA_ERR_NULL;
   } else {
     if (!workspace) return MFA_ERR_WORKSPACE;
-    if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
+    if (workspace_bytes < mfa_split_workspace_bytes(Bv, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   }
 
   mfa::AttnArgs& a = c->a;
@@ -466,7 +472,8 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.kv_f32 = cache->dtype == MFA_F32;
   a.sm_scale = sm_scale;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  const size_t rows = static_cast<size_t>(B) * num_splits * H;
+  a.q_len = q_len;
+  const size_t rows = static_cast<size_t>(Bv) * num_splits * H;
   if (num_splits > 1) {
     a.part_o = workspace;
     a.part_bf16 = out_dtype == MFA_BF16;
@@ -475,7 +482,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.out = out;
   a.out_f32 = out_dtype == MFA_F32;
   c->fp8 = cache->dtype == MFA_FP8_E4M3;
-  c->B = B;
+  c->B = Bv;
   c->H = H;
   c->d = d;
   c->num_splits = num_splits;
@@ -507,6 +514,19 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
                                      num_splits, chunk_tokens, workspace, workspace_bytes, out,
                                      out_dtype, &c);
+  if (st != MFA_OK) return st;
+  return launch_attn(c, as_stream(stream));
+}
+
+mfa_status mfa_decode_attn_multi(const void* q, int q_dtype, int B, int q_len, int H,
+                                 const mfa_kv_cache* cache, const int32_t* seq_lens,
+                                 int max_seq_len, float sm_scale, int num_splits, int chunk_tokens,
+                                 void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                                 void* stream) {
+  AttnCall c;
+  const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
+                                     num_splits, chunk_tokens, workspace, workspace_bytes, out,
+                                     out_dtype, &c, q_len);
   if (st != MFA_OK) return st;
   return launch_attn(c, as_stream(stream));
 }

@@ -88,6 +88,8 @@ extern "C" {
 
 #define MFA_ABI_VERSION 2
 #define MFA_BLOCK_TOKENS 64
+/* Most query tokens per sequence in mfa_decode_attn_multi. */
+#define MFA_MAX_QUERY_TOKENS 16
 
 typedef enum {
   MFA_OK = 0,
@@ -236,6 +238,32 @@ mfa_status mfa_decode_attn(const void *q, int q_dtype, int B, int H,
                            int chunk_tokens, void *workspace,
                            size_t workspace_bytes, void *out, int out_dtype,
                            void *stream);
+
+/*
+ * Multi-token decode attention: q_len new tokens per sequence (several
+ * tokens decoded in one step, as in multi-token prediction: "Step-3 is Large
+ * yet Affordable" summary page, §5, where more query tokens per KV read
+ * raise the attention's arithmetic intensity). The q_len new tokens are the
+ * last q_len of each sequence (appended before the call, e.g. by
+ * mfa_kv_append with n_new = q_len); query token j (0-based) of sequence b
+ * attends to the sequence's first seq_lens[b] - (q_len - 1 - j) tokens, so
+ * the new tokens see each other causally.
+ *   q        [B][q_len][H][d] of q_dtype
+ *   out      [B][q_len][H][d] of out_dtype
+ *   q_len    1 .. MFA_MAX_QUERY_TOKENS; q_len == 1 is mfa_decode_attn
+ * Every other argument is as in mfa_decode_attn, with the split partials and
+ * the combine over the B * q_len rows (sequence, query token): the workspace
+ * is mfa_split_workspace_bytes(B * q_len, H, d, num_splits) bytes and a
+ * separate mfa_combine takes B * q_len as its batch. The query tokens of a
+ * sequence run on one XCD side by side, so its KV blocks are read from HBM
+ * about once and from that XCD's L2 q_len times.
+ */
+mfa_status mfa_decode_attn_multi(const void *q, int q_dtype, int B, int q_len, int H,
+                                 const mfa_kv_cache *cache, const int32_t *seq_lens,
+                                 int max_seq_len, float sm_scale, int num_splits,
+                                 int chunk_tokens, void *workspace,
+                                 size_t workspace_bytes, void *out, int out_dtype,
+                                 void *stream);
 
 /*
  * Split combine: merges the num_splits partials (layout as in

@@ -169,6 +169,33 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     return np.stack(out)
 
 
+def decode_attention_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                           block_table: Optional[np.ndarray], max_blocks_per_seq: int,
+                           seq_lens: Sequence[int], sm_scale: float,
+                           seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Several new tokens per sequence, attending causally.
+
+    q [B][T][H][d]: the queries of the last T tokens of every sequence (the
+    tokens decoded together in one step, as multi-token prediction does, §5
+    of the summary page). Query j (0-based) of sequence b sees the sequence's
+    first seq_lens[b] - (T - 1 - j) tokens: everything before the new tokens
+    plus new tokens 0..j. Returns o [len(seqs)][T][H][d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T = q.shape[1]
+    if seqs is None:
+        seqs = range(q.shape[0])
+    out = []
+    for b in seqs:
+        per_token = []
+        for j in range(T):
+            n = max(int(seq_lens[b]) - (T - 1 - j), 0)
+            rows = physical_rows(b, n, block_table, max_blocks_per_seq)
+            per_token.append(softmax_attention(q[b, j], k_cache[rows], v_cache[rows], sm_scale))
+        out.append(np.stack(per_token))
+    return np.stack(out)
+
+
 # --------------------------------------------------------------------------
 # split-KV partials and their log-sum-exp combine
 # --------------------------------------------------------------------------

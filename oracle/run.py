@@ -135,3 +135,19 @@ def expected_cache_rows(inp: Dict, seqs: Sequence[int]):
         res["k_scale"] = ks
         res["v_scale"] = vs
     return res, owned
+
+
+def decode_step_multi(inp: Dict, seqs: Optional[Sequence[int]] = None,
+                      sm_scale: Optional[float] = None) -> np.ndarray:
+    """Multi-token decode: the queries ``q_multi`` [B][T][H][d] of the last T
+    tokens of every sequence (the cache after the step's append), causal
+    among themselves. Returns o [len(seqs)][T][H][d] in fp64."""
+    w = inp["workload"]
+    if seqs is None:
+        seqs = list(range(w.batch))
+    if sm_scale is None:
+        sm_scale = mfa.default_sm_scale(w.head_dim)
+    q = mfa.stored_to_f64(inp["q_multi"], w.act_dtype)
+    kc, vc = physical_cache(inp, seqs)
+    return mfa.decode_attention_multi(q, kc, vc, inp["block_table"], inp["max_blocks_per_seq"],
+                                      inp["seq_lens"], sm_scale, seqs=seqs)

@@ -18,6 +18,9 @@ What pins what:
 * rmsnorm / query projection -- output RMS equals 1 before the gain; scale
   invariance; constant input gives the gain; identity down-projection reduces
   to W_up x / rms(x); pure-Python brute force; head h owns columns h*d..h*d+d-1.
+* multi-token decode -- each query token equals single-token decode at its
+  causal length; a later new token is invisible to earlier queries and
+  visible to its own; pure-Python brute force.
 * K/V projection -- block-identity weights give x's halves exactly; row
   mapping of W_k / W_v; pure-Python brute force.
 * bf16 rounding -- anchor values including exact ties (to even) and values
@@ -49,6 +52,7 @@ def real_oracle():
         softmax_attention=mfa.softmax_attention,
         physical_rows=mfa.physical_rows,
         decode_attention=mfa.decode_attention,
+        decode_attention_multi=mfa.decode_attention_multi,
         scatter_tokens=mfa.scatter_tokens,
         split_partials=mfa.split_partials,
         combine=mfa.combine,
@@ -253,6 +257,50 @@ def check_qproj(O):
     return fails
 
 
+# ---------------------------------------------------------------- multi-token decode
+def check_multi_token(O):
+    fails = []
+    rng = np.random.default_rng(13)
+    H, d, T, mb = 2, 3, 3, 2
+    lens = [5, 70, 2]                        # pre-existing tokens + the T new ones
+    nb = 3 * mb
+    kc = rng.standard_normal((nb * 64, d)); vc = rng.standard_normal((nb * 64, d))
+    bt = np.arange(nb, dtype=np.int32).reshape(3, mb)[:, ::-1].copy()   # permuted blocks
+    q = rng.standard_normal((3, T, H, d))
+    got = O.decode_attention_multi(q, kc, vc, bt, mb, lens, 0.5)
+    # one query token at a time is single-token decode with the causal length
+    for j in range(T):
+        lj = [max(L - (T - 1 - j), 0) for L in lens]
+        want = O.decode_attention(q[:, j], kc, vc, bt, mb, lj, 0.5)
+        if not _close(got[:, j], want, 1e-13):
+            fails.append(f"query token {j} differs from single-token decode at its length")
+    # causality: changing the last new token changes only the last query's output
+    last = [O.physical_rows(b, lens[b], bt, mb)[-1] for b in range(3)]
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[last] += 5.0; vc2[last] -= 3.0
+    got2 = O.decode_attention_multi(q, kc2, vc2, bt, mb, lens, 0.5)
+    if not _close(got2[:, :T - 1], got[:, :T - 1], 1e-13):
+        fails.append("earlier query tokens see a later new token")
+    if _close(got2[:, T - 1], got[:, T - 1], 1e-6):
+        fails.append("the last query token does not see itself")
+    # brute force on logical rows
+    for b in range(3):
+        rows = O.physical_rows(b, lens[b], bt, mb)
+        for j in range(T):
+            n = lens[b] - (T - 1 - j)
+            if n <= 0:                       # fewer tokens than queries: nothing to attend
+                if np.any(got[b, j] != 0.0):
+                    fails.append(f"query token {j} of a too-short sequence is not zero")
+                continue
+            for h in range(H):
+                want = O.brute.attention(q[b, j, h:h + 1].tolist(), kc[rows[:n]].tolist(),
+                                         vc[rows[:n]].tolist(), 0.5)
+                if not _close(got[b, j, h], np.array(want)[0], 1e-12):
+                    fails.append(f"brute force differs at b={b} j={j} h={h}")
+                    return fails
+    return fails
+
+
 # ---------------------------------------------------------------- K/V projection
 def check_kv_projection(O):
     fails = []
@@ -440,7 +488,8 @@ def check_layout(O):
     return fails
 
 
-ALL_CHECKS = (check_attention, check_gather, check_combine, check_qproj, check_kv_projection,
+ALL_CHECKS = (check_attention, check_gather, check_combine, check_multi_token, check_qproj,
+              check_kv_projection,
               check_bf16_round, check_e4m3, check_quantize, check_cost, check_layout)
 
 

@@ -121,6 +121,21 @@ def _k_blocks_gc_swapped(rows, dt):
     return np.ascontiguousarray(x).reshape(x.shape[0], -1)
 
 
+def _multi_not_causal(q, kc, vc, bt, mb, lens, sc, seqs=None):
+    # every query token sees all seq_lens[b] tokens
+    T = np.asarray(q).shape[1]
+    return np.stack([mfa.decode_attention(np.asarray(q)[:, j], kc, vc, bt, mb, lens, sc, seqs)
+                     for j in range(T)], axis=1)
+
+
+def _multi_off_by_one(q, kc, vc, bt, mb, lens, sc, seqs=None):
+    # query j sees one token fewer than it should
+    T = np.asarray(q).shape[1]
+    return np.stack([mfa.decode_attention(np.asarray(q)[:, j], kc, vc, bt, mb,
+                                          [max(L - (T - j), 0) for L in lens], sc, seqs)
+                     for j in range(T)], axis=1)
+
+
 def _kv_swapped(x, w, d):
     k, v = mfa.kv_projection(x, w, d)
     return v, k
@@ -146,6 +161,8 @@ def _bf16_ties_away(a):
 
 
 MUTANTS = {
+    "multi_token_not_causal": dict(decode_attention_multi=_multi_not_causal),
+    "multi_token_off_by_one": dict(decode_attention_multi=_multi_off_by_one),
     "kv_projection_k_v_swapped": dict(kv_projection=_kv_swapped),
     "kv_projection_rows_offset": dict(kv_projection=_kv_rows_offset),
     "bf16_round_truncates": dict(f64_to_bf16_bits=_bf16_truncate),

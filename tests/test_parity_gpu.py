@@ -416,6 +416,61 @@ def test_kv_projection_step(gpu_lib, idx, shrink, packed):
         check_bf16(got, want, "kv projection step")
 
 
+MULTI = [
+    ("bf16-paged", 3, dict(), [3, 62, 63, 64, 65, 200, 777]),
+    ("fp8-paged", 4, dict(), [2, 64, 129, 513]),
+    ("bf16-contig", 3, dict(paged=False), [130, 5, 64]),
+    ("f32-valu", 3, dict(paged=False, kv_dtype="f32", act_dtype="f32", heads=4, head_dim=64),
+     [7, 100, 64]),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("name,base,over,lens", MULTI, ids=[m[0] for m in MULTI])
+def test_multi_token_decode(gpu_lib, name, base, over, lens, T, splits):
+    """T new tokens per sequence attending causally (mfa_decode_attn_multi)
+    against the oracle; sequences shorter than T included (their early
+    queries see nothing or only part of the new tokens)."""
+    import decode_attention_02_amd as mfa
+    w = small(base, batch=len(lens), **over)
+    inp = workloads.make_inputs(base, workload=w, seed=41, prefill_lens=lens, q_len=T)
+    say(f"multi-token {name} T={T} splits={splits}")
+    T_, cache, step = setup(inp)
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    chunk = -(-(-(-maxlen // splits)) // 64) * 64 if splits > 1 else None
+    out = mfa.decode_attn_multi(T_["q_multi"], cache, T_["seq_lens"], maxlen,
+                                num_splits=splits, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    want = orun.decode_step_multi(inp)
+    got = to_np(out)
+    if w.act_dtype == "f32":
+        r = rel_l2(got, want)
+        say(f"multi-token f32: rel_l2={r:.3e}")
+        assert r <= REL_L2_F32
+    else:
+        check_bf16(got, want, f"multi-token {name} T={T}")
+
+
+def test_multi_token_one_is_single_token(gpu_lib):
+    """q_len = 1 through mfa_decode_attn_multi is bit-identical to mfa_decode_attn."""
+    import decode_attention_02_amd as mfa
+    w = small(3, batch=5)
+    inp = workloads.make_inputs(3, workload=w, seed=42, prefill_lens=[1, 63, 64, 300, 129])
+    T_, cache, step = setup(inp)
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    for splits in (1, 2):
+        chunk = -(-(-(-maxlen // splits)) // 64) * 64
+        a = mfa.decode_attn(T_["q"], cache, T_["seq_lens"], maxlen, num_splits=splits,
+                            chunk_tokens=chunk)
+        b = mfa.decode_attn_multi(T_["q"].unsqueeze(1), cache, T_["seq_lens"], maxlen,
+                                  num_splits=splits, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.squeeze(1).view(torch.int16))
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

@@ -102,7 +102,7 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = None,
                 context: Optional[int] = None, workload: Optional[Workload] = None,
-                prefill_lens=None, kv_proj: bool = False):
+                prefill_lens=None, kv_proj: bool = False, q_len: int = 1):
     """Draw the inputs of one decode step of workload ``index``.
 
     ``batch`` / ``context`` shrink the workload (for tests that need a small
@@ -118,6 +118,9 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
     (W_k over W_v, N(0, 1/hidden)) after everything else, so the other
     arrays are the same with and without it; the new token is then the K/V
     projection of x and ``k_new`` / ``v_new`` are not its values.
+    ``q_len`` > 1 (workloads that draw q) also draws ``q_multi``
+    [B][q_len][H][d], the queries of the last q_len tokens of every sequence
+    (multi-token decode), after everything else.
     """
     w = workload if workload is not None else WORKLOADS[index]
     if batch is not None or context is not None:
@@ -196,6 +199,12 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
             raise ValueError("the K/V projection needs a query-path workload (x)")
         out["w_kv"] = _store(rng.standard_normal((2 * d, w.hidden), dtype=np.float32)
                              / np.float32(math.sqrt(w.hidden)), act)
+
+    # 6. queries of several new tokens per sequence (drawn last)
+    if q_len > 1:
+        if w.has_qproj:
+            raise ValueError("multi-token queries are drawn for workloads without a query path")
+        out["q_multi"] = _store(rng.standard_normal((B, q_len, H, d), dtype=np.float32), act)
     return out
 
 
@@ -223,6 +232,8 @@ def to_torch(inp, device="cuda"):
         out["g"] = torch.from_numpy(inp["g"]).to(device)
     else:
         out["q"] = t(inp["q"], w.act_dtype)
+        if "q_multi" in inp:
+            out["q_multi"] = t(inp["q_multi"], w.act_dtype)
     for k in ("k_ctx", "v_ctx", "k_new", "v_new"):
         out[k] = t(inp[k], kvin)
     out["ctx_offsets"] = inp["ctx_offsets"]

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new tokens per sequence decoded together (multi-token decode, "
+                         "workloads without a query path)")
     ap.add_argument("--kv-proj", action="store_true",
                     help="compute the new token's K/V from x in the step (w_kv) instead of "
                          "reading it (query-path workloads)")
@@ -91,14 +94,19 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
         threads = len(os.sched_getaffinity(0))
     w = inp["workload"]
     runs, total = 0, 0.0
+    multi = "q_multi" in inp
+    tq = inp["q_multi"].shape[1] if multi else 1
     while total < min_seconds and runs < 50:
         t0 = time.perf_counter()
-        orun.decode_step(inp)
+        if multi:
+            orun.decode_step_multi(inp)
+        else:
+            orun.decode_step(inp)
         total += time.perf_counter() - t0
         runs += 1
     dt = total / runs
     toks = int(inp["seq_lens"].sum())
-    return {"value": w.batch / dt, "unit": "decode tokens/s", "cores": int(threads),
+    return {"value": w.batch * tq / dt, "unit": "decode tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
                       f"tokens), fp64 numpy, mean of {runs} runs ({dt:.2f} s each)"}
@@ -143,7 +151,11 @@ def main():
     if args.kv_proj and not w.has_qproj:
         print("--kv-proj needs a workload with a query path (configs 1, 2, 5)", file=sys.stderr)
         sys.exit(2)
-    inp = workloads.make_inputs(args.config, kv_proj=args.kv_proj)
+    TQ = args.q_len
+    if TQ > 1 and w.has_qproj:
+        print("--q-len > 1 needs a workload whose queries are drawn (configs 3, 4)", file=sys.stderr)
+        sys.exit(2)
+    inp = workloads.make_inputs(args.config, kv_proj=args.kv_proj, q_len=TQ)
     T = workloads.to_torch(inp, dev)
     act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     B = w.batch
@@ -178,7 +190,33 @@ def main():
         sets.append((step, wts, wkv))
     torch.cuda.synchronize()
 
+    if TQ > 1:
+        # multi-token decode: the step appends TQ tokens per sequence (the last TQ
+        # positions) and attends with the TQ queries of each, causal among them
+        ns_m, ch_m = mfa.decode_plan(B * TQ, w.heads, w.head_dim, maxlen, w.kv_dtype)
+        if args.splits:
+            ns_m = args.splits
+            ch_m = -(-(-(-maxlen // ns_m)) // 64) * 64
+        k_m = T["k_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
+        v_m = T["v_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
+        pos_m = (T["seq_lens"] - TQ).to(torch.int32)
+        multi = []
+        for r in range(rotate):
+            nb = mfa.split_workspace_bytes(B * TQ, w.heads, w.head_dim, ns_m)
+            multi.append((torch.empty(max(nb, 16), dtype=torch.uint8, device=dev),
+                          torch.empty((B, TQ, w.heads, w.head_dim), dtype=act, device=dev)))
+
+    def attention_multi(i, combine):
+        step = sets[i % rotate][0]
+        ws, out = multi[i % rotate]
+        mfa.decode_attn_multi(T["q_multi"], step.cache, T["seq_lens"], maxlen, step.sm_scale,
+                              ns_m, ch_m, out=out if combine else None, workspace=ws,
+                              combine=combine)
+
     def attention(i, q):
+        if TQ > 1:
+            attention_multi(i, combine=ns_m == 1)
+            return
         step = sets[i % rotate][0]
         if step.num_splits > 1:
             mfa.decode_attn(q, step.cache, T["seq_lens"], step.max_seq_len, step.sm_scale,
@@ -191,6 +229,10 @@ def main():
         """One decode step on buffer set i % rotate (DecodeStep: query path,
         KV append, attention, split combine)."""
         step, wts, wkv = sets[i % rotate]
+        if TQ > 1:
+            mfa.kv_append(step.cache, k_m, v_m, pos_m)
+            attention_multi(i, combine=True)
+            return
         if w.has_qproj:
             step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], x=T["x"], weights=wts,
                  w_kv=wkv)
@@ -253,7 +295,7 @@ def main():
     traffic = counters_for(w.name, kernel_source_sig())
     rec = {
         "metric": "MFA decode-attention tokens/s and achieved KV HBM GB/s (% of peak), 1xMI355X",
-        "value": B / (ms * 1e-3),
+        "value": B * TQ / (ms * 1e-3),
         "unit": "decode tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -266,11 +308,14 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V, N(0,1/fan_in) weights, random-init)",
         "config": {"workload": w.name, "batch": B, "context": maxlen, "heads": w.heads,
                    "head_dim": w.head_dim, "kv_dtype": w.kv_dtype, "hidden": w.hidden,
-                   "q_rank": w.q_rank, "paged": w.paged, "num_splits": step0.num_splits,
-                   "chunk_tokens": step0.chunk_tokens, "rotate": rotate,
+                   "q_rank": w.q_rank, "paged": w.paged,
+                   "num_splits": ns_m if TQ > 1 else step0.num_splits,
+                   "chunk_tokens": ch_m if TQ > 1 else step0.chunk_tokens, "rotate": rotate,
+                   "q_len": TQ,
                    "step": ("qproj+kv_proj+kv_append+decode_attn+combine" if args.kv_proj
                             else "qproj+kv_append+decode_attn+combine") if w.has_qproj
-                   else "kv_append+decode_attn+combine"},
+                   else ("kv_append(q_len)+decode_attn_multi+combine" if TQ > 1
+                         else "kv_append+decode_attn+combine")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (traffic / (attn_avg * 1e-3) / 1e9) if traffic else None,

@@ -17,16 +17,17 @@
 //   * QK waves 0..3: wave w holds K rows 16w..16w+15 of each block and
 //     computes S^T[token][head] = K . Q^T on the 16x16x32 matrix cores (the
 //     16 tokens are the row side, the 64 heads sharing the KV head four
-//     16-column tiles of Q, staged once in LDS in operand order); then the
-//     online softmax: per-head block max across the four QK waves through
-//     LDS, p = exp2(s * c - m) as one fma and one exp2, lane-partial row
-//     sums, P^T (bf16) into LDS;
-//   * PV waves 4..7: wave 4+j holds the V^T rows (features) 64j..64j+63 of
-//     each block and accumulates O^T[feature][head] += V^T . P^T.
+//     16-column tiles of Q, staged once in LDS in operand order), writes the
+//     logits to LDS and its per-head maximum over its 16 tokens;
+//   * PV waves 4..7: wave 4+j runs the online softmax for the 16 tokens QK
+//     wave j scored (block max from the four per-wave maxima, p = exp2(s * c
+//     - m) as one fma and one exp2, lane-partial row sums, P^T (bf16) into
+//     LDS), and holds the V^T rows (features) 64j..64j+63 of each block to
+//     accumulate O^T[feature][head] += V^T . P^T.
 // Each wave holds only its own role's operands in a register ring of RK
 // (QK) or RV (PV) blocks, filled with buffer loads. The stages are skewed
-// across iterations separated by one barrier each: iteration i computes the
-// softmax of block i-1 and S of block i, and the P.V product of block i-2.
+// across iterations separated by one barrier each: iteration i computes S
+// of block i, the P.V product of block i-2 and the softmax of block i-1.
 // Every iteration issues the same number of loads (past the walk through
 // empty buffer resources, which read nothing), so the compiler's wait before
 // a ring slot is consumed leaves the younger slots in flight.
@@ -38,6 +39,8 @@
 // registers as is. FP8 codes are widened to bf16 in registers (exact);
 // per-token K scales multiply the logits, V scales multiply P before its
 // bf16 rounding.
+// Several query tokens per sequence (multi-token decode) are virtual rows:
+// row r = sequence b, query token j walks b's cache up to its own position.
 #include <type_traits>
 
 #include "device_common.h"

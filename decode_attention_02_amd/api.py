@@ -233,6 +233,31 @@ def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, m
     return out if (num_splits == 1 or combine) else None
 
 
+def out_proj(o: torch.Tensor, w_o: torch.Tensor, packed: bool = False, want_y: bool = True,
+             want_fp8: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Attention output projection y = o W_o^T (bf16) and its per-token FP8
+    pack (mfa_out_proj). o [B][HD] (or [B][H][d]); w_o [hidden][HD].
+    Returns (y or None, codes uint8 [B][hidden] or None, scales [B] or None)."""
+    lib = _lib.load()
+    o2 = o.reshape(o.shape[0], -1)
+    _dev(o2, "o")
+    _dev(w_o, "w_o")
+    B, HD = o2.shape
+    hidden = w_o.shape[0]
+    dt = _DTYPES[o2.dtype]
+    if workspace is None:
+        nb = lib.mfa_out_proj_workspace_bytes(B, HD, hidden, dt)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=o.device)
+    y = torch.empty((B, hidden), dtype=o2.dtype, device=o.device) if want_y else None
+    codes = torch.empty((B, hidden), dtype=torch.uint8, device=o.device) if want_fp8 else None
+    scales = torch.empty(B, dtype=torch.float32, device=o.device) if want_fp8 else None
+    check("mfa_out_proj", lib.mfa_out_proj(
+        _ptr(o2), _ptr(w_o), MFA_WEIGHTS_PACKED if packed else MFA_WEIGHTS_ROWMAJOR, B, HD,
+        hidden, dt, _ptr(workspace), workspace.numel(), _ptr(y), _ptr(codes), _ptr(scales),
+        _stream(o.device)))
+    return y, codes, scales
+
+
 def combine_splits(workspace: torch.Tensor, batch: int, heads: int, head_dim: int, num_splits: int,
                    out: Optional[torch.Tensor] = None,
                    out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:

@@ -108,6 +108,11 @@ hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipS
 hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, int M, int R,
                                  float eps, void* out, int out_f32, int out_tiles,
                                  const AppendArgs* append, hipStream_t stream, int part_stride = 0);
+// y[m][n] = bf16(sum over ksplit partials) (y nullable); with codes set,
+// also the per-row FP8 pack of the bf16 row: scales[m] = amax / 448 (1 when
+// 0), codes = RNE e4m3(y / scale). N % 8 == 0, N <= 8192.
+hipError_t launch_outproj_pack(const float* part, int ksplit, int M, int N, uint16_t* y,
+                               uint8_t* codes, float* scales, hipStream_t stream);
 // out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
 hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
                               int out_f32, hipStream_t stream);

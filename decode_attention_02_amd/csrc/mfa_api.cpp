@@ -162,6 +162,66 @@ size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, in
   return plan_qproj(B, hidden, q_rank, H * d, dtype, 2 * d).total;
 }
 
+// ---- attention output projection ----------------------------------------
+namespace {
+struct OutProjPlan {
+  int rows;
+  GemmPlan g;
+  size_t total;
+};
+OutProjPlan plan_out_proj(int B, int HD, int hidden) {
+  OutProjPlan p{};
+  p.rows = B < kRowsPerPass ? B : kRowsPerPass;
+  p.g = plan_gemm(hidden, HD, p.rows);
+  p.total = round_up(static_cast<size_t>(p.g.ks) * p.rows * hidden * 4, 256);
+  return p;
+}
+mfa_status check_out_proj_shape(int B, int HD, int hidden, int dtype) {
+  if (dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  if (B < 1 || B > 256 || HD < 256 || hidden < 64) return MFA_ERR_SHAPE;
+  if (HD % 256 || hidden % 64 || hidden > 8192) return MFA_ERR_SHAPE;
+  return MFA_OK;
+}
+}  // namespace
+
+size_t mfa_out_proj_workspace_bytes(int B, int HD, int hidden, int dtype) {
+  if (check_out_proj_shape(B, HD, hidden, dtype) != MFA_OK) return 0;
+  return plan_out_proj(B, HD, hidden).total;
+}
+
+mfa_status mfa_out_proj(const void* o, const void* w_o, int weight_layout, int B, int HD,
+                        int hidden, int dtype, void* workspace, size_t workspace_bytes, void* y,
+                        void* codes, float* scales, void* stream) {
+  if (!o || !w_o) return MFA_ERR_NULL;
+  if (!y && !codes) return MFA_ERR_NULL;                 // nothing to write
+  if ((codes == nullptr) != (scales == nullptr)) return MFA_ERR_NULL;
+  const mfa_status sh = check_out_proj_shape(B, HD, hidden, dtype);
+  if (sh != MFA_OK) return sh;
+  if (weight_layout != MFA_WEIGHTS_ROWMAJOR && weight_layout != MFA_WEIGHTS_PACKED)
+    return MFA_ERR_SHAPE;
+  if (!aligned16(o) || !aligned16(w_o) || (y && !aligned16(y)) || (codes && !aligned16(codes)) ||
+      (scales && !aligned4(scales)) || (workspace && !aligned16(workspace)))
+    return MFA_ERR_ALIGN;
+  const OutProjPlan p = plan_out_proj(B, HD, hidden);
+  if (!workspace || workspace_bytes < p.total) return MFA_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  float* part = static_cast<float*>(workspace);
+  for (int r0 = 0; r0 < B; r0 += p.rows) {
+    const int M = (B - r0) < p.rows ? (B - r0) : p.rows;
+    const uint16_t* oa = static_cast<const uint16_t*>(o) + static_cast<size_t>(r0) * HD;
+    hipError_t e = mfa::launch_gemm_bf16(oa, static_cast<const uint16_t*>(w_o), part, nullptr, M,
+                                         hidden, HD, p.g.ks, p.g.ntiles,
+                                         weight_layout == MFA_WEIGHTS_PACKED, false, st);
+    if (e != hipSuccess) return MFA_ERR_HIP;
+    e = mfa::launch_outproj_pack(
+        part, p.g.ks, M, hidden, y ? static_cast<uint16_t*>(y) + static_cast<size_t>(r0) * hidden : nullptr,
+        codes ? static_cast<uint8_t*>(codes) + static_cast<size_t>(r0) * hidden : nullptr,
+        scales ? scales + r0 : nullptr, st);
+    if (e != hipSuccess) return MFA_ERR_HIP;
+  }
+  return MFA_OK;
+}
+
 mfa_status mfa_pack_weight(const void* w, void* packed, int N, int K, int dtype, void* stream) {
   if (!w || !packed) return MFA_ERR_NULL;
   if (dtype != MFA_BF16) return MFA_ERR_DTYPE;

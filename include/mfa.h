@@ -278,6 +278,30 @@ mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
                        void *stream);
 
 /*
+ * Attention output projection and the FP8 hand-off to the FFN side
+ * ("Step-3 is Large yet Affordable" summary page, §7: attention instances
+ * send FP8 tokens with their scales to the FFN instances; 128 tokens of
+ * hidden 7168 are 896 KiB of codes):
+ *   y = o W_o^T                 (fp32 accumulation, rounded to bf16)
+ *   scales[b] = max_j |y[b][j]| / 448  (1 when the row is zero; one correctly
+ *               rounded fp32 division),  codes[b][j] = RNE e4m3(y[b][j] / scales[b])
+ * o        [B][HD] bf16 (the attention output, heads concatenated)
+ * w_o      [hidden][HD] bf16 (torch Linear [out][in]), or packed by
+ *          mfa_pack_weight when weight_layout is MFA_WEIGHTS_PACKED
+ * y        [B][hidden] bf16, or NULL (not written)
+ * codes    [B][hidden] OCP e4m3 bytes and scales [B] fp32: both or neither
+ *          (at least one of y and codes must be given)
+ * workspace >= mfa_out_proj_workspace_bytes(B, HD, hidden, dtype) bytes
+ *          (fp32 split-K partials)
+ * dtype    MFA_BF16. Limits: 1 <= B <= 256; HD a multiple of 256; hidden a
+ *          multiple of 64, at most 8192.
+ */
+size_t mfa_out_proj_workspace_bytes(int B, int HD, int hidden, int dtype);
+mfa_status mfa_out_proj(const void *o, const void *w_o, int weight_layout, int B, int HD,
+                        int hidden, int dtype, void *workspace, size_t workspace_bytes,
+                        void *y, void *codes, float *scales, void *stream);
+
+/*
  * One whole decode step on one stream, equal to
  *   mfa_qproj (when x != NULL) -> mfa_kv_append (one token per sequence)
  *   -> mfa_decode_attn (with out: attention and split combine)

@@ -61,3 +61,8 @@ def kv_projection(x: Sequence[Sequence[float]], w_kv, head_dim: int):
         ks.append(kv[:head_dim])
         vs.append(kv[head_dim:2 * head_dim])
     return ks, vs
+
+
+def output_projection(o: Sequence[Sequence[float]], w_o):
+    """Row by row: y = W_o o, o being one row of concatenated head outputs."""
+    return [matvec_t(w_o, ob) for ob in o]

@@ -45,3 +45,10 @@ def qproj_weight_bytes(hidden: int, q_rank: int, heads: int, head_dim: int,
 
 def qproj_flop(batch: int, hidden: int, q_rank: int, heads: int, head_dim: int) -> int:
     return 2 * batch * (hidden * q_rank + q_rank * heads * head_dim)
+
+
+def hidden_payload_bytes(tokens: int, hidden: int, elem_bytes: int, scale_bytes: int = 0) -> int:
+    """Bytes of hidden states sent one way between attention and FFN
+    instances: tokens x hidden elements, plus a per-token scale if any (the
+    StepMesh page's traffic model: FP8 from attention to FFN, BF16 back)."""
+    return tokens * (hidden * elem_bytes + scale_bytes)

@@ -87,6 +87,32 @@ def kv_projection(x, w_kv, head_dim: int) -> Tuple[np.ndarray, np.ndarray]:
     return kv[:, :head_dim], kv[:, head_dim:2 * head_dim]
 
 
+def output_projection(o, w_o) -> np.ndarray:
+    """Attention output projection y = o W_o^T.
+
+    o [B][H][d] or [B][H*d] (heads concatenated, head h in columns
+    h*d .. h*d+d-1); w_o [Dm][H*d] as [out][in]. Returns y [B][Dm]. The
+    attention instance hands y on to the FFN instances (§7 Implementation and
+    Results); the pages give no bias, so none is added.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    o = o.reshape(o.shape[0], -1)
+    return o @ np.asarray(w_o, dtype=np.float64).T
+
+
+def a2f_pack(y_bf16_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """FP8 hand-off of bf16 hidden states from attention to FFN.
+
+    §7 (Implementation and Results) of the summary page has attention send
+    FP8 tokens with their scales to the FFN side; the StepMesh page's traffic
+    model counts one byte per hidden element. Reading taken here: the bf16
+    row is quantised per token exactly as the FP8 KV cache is (one fp32 scale
+    amax/448 per row, RNE e4m3 codes of the correctly rounded fp32
+    quotient). Returns (codes uint8 [B][Dm], scales float32 [B]).
+    """
+    return quantize_tokens(bf16_bits_to_f64(np.asarray(y_bf16_bits, dtype=np.uint16)))
+
+
 def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even of fp64 values to bfloat16 bit patterns.
 

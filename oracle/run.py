@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 Takes the dict made by ``workloads.make_inputs`` and computes, in fp64:
 the query (projection or given), the cache contents after the step's append
 (prefilled tokens plus the new token at position prefill_len), and the
-attention output for the requested sequences. FP8 caches are quantised with
-this package's own codec.
+attention output for the requested sequences, and the output projection with
+its FP8 pack. FP8 caches are quantised with this package's own codec.
 """
 from __future__ import annotations
 
@@ -151,3 +151,17 @@ def decode_step_multi(inp: Dict, seqs: Optional[Sequence[int]] = None,
     kc, vc = physical_cache(inp, seqs)
     return mfa.decode_attention_multi(q, kc, vc, inp["block_table"], inp["max_blocks_per_seq"],
                                       inp["seq_lens"], sm_scale, seqs=seqs)
+
+
+def output_projection(inp: Dict, o: Optional[np.ndarray] = None) -> Dict:
+    """The output projection of the drawn attention output ``o_attn`` (or of
+    ``o`` [B][H][d] / [B][H*d] in fp64, e.g. this module's decode_step output)
+    through the drawn ``w_o``: y in fp64, its bf16 rounding, and the FP8
+    attention-to-FFN pack of that rounding."""
+    w = inp["workload"]
+    if o is None:
+        o = mfa.stored_to_f64(inp["o_attn"], w.act_dtype)
+    y = mfa.output_projection(o, mfa.stored_to_f64(inp["w_o"], w.act_dtype))
+    bits = mfa.f64_to_bf16_bits(y)
+    codes, scales = mfa.a2f_pack(bits)
+    return {"y": y, "y_bits": bits, "codes": codes, "scales": scales}

@@ -23,6 +23,11 @@ What pins what:
   visible to its own; pure-Python brute force.
 * K/V projection -- block-identity weights give x's halves exactly; row
   mapping of W_k / W_v; pure-Python brute force.
+* output projection -- identity weight returns o; head h reaches only its
+  own column block; [B][H][d] and [B][H*d] agree; pure-Python brute force.
+* A2F pack -- hand-worked rows (scale 1 and scale 2, negative amax, zero
+  row) coded bit for bit; the amax element codes to +-448; error within half
+  an e4m3 step times the scale; the page's 896 KiB / 1.75 MiB payloads.
 * bf16 rounding -- anchor values including exact ties (to even) and values
   next to them; torch's RNE cast of fp32 values; the half-ulp error bound.
 * e4m3 -- torch's float8_e4m3fn decode of all 256 codes; anchor values of the
@@ -59,6 +64,9 @@ def real_oracle():
         rmsnorm=mfa.rmsnorm,
         query_projection=mfa.query_projection,
         kv_projection=mfa.kv_projection,
+        output_projection=mfa.output_projection,
+        a2f_pack=mfa.a2f_pack,
+        hidden_payload_bytes=cost.hidden_payload_bytes,
         f64_to_bf16_bits=mfa.f64_to_bf16_bits,
         quantize_tokens=mfa.quantize_tokens,
         dequantize_tokens=mfa.dequantize_tokens,
@@ -331,6 +339,76 @@ def check_kv_projection(O):
     return fails
 
 
+# ---------------------------------------------------------------- output projection
+def check_output_projection(O):
+    fails = []
+    rng = np.random.default_rng(21)
+    H, d = 3, 4
+    o = rng.standard_normal((2, H, d))
+    # identity weight (Dm = H*d): y is o with heads concatenated
+    if not np.array_equal(O.output_projection(o, np.eye(H * d)), o.reshape(2, H * d)):
+        fails.append("identity output projection does not return o")
+    # only head 1's block of W_o set: y depends on head 1 alone
+    w = np.zeros((5, H * d)); w[:, d:2 * d] = rng.standard_normal((5, d))
+    o2 = o.copy(); o2[:, 0] += 7.0; o2[:, 2] -= 3.0
+    y1, y2 = O.output_projection(o, w), O.output_projection(o2, w)
+    if not (np.array_equal(y1, y2) and _close(y1, o[:, 1] @ w[:, d:2 * d].T, 1e-14)):
+        fails.append("head h does not map to columns h*d .. h*d+d-1 of W_o")
+    w = rng.standard_normal((5, H * d))
+    if not np.array_equal(O.output_projection(o, w), O.output_projection(o.reshape(2, -1), w)):
+        fails.append("[B][H][d] and [B][H*d] inputs differ")
+    want = O.brute.output_projection(o.reshape(2, -1).tolist(), w.tolist())
+    if not _close(O.output_projection(o, w), np.array(want), 1e-13):
+        fails.append("output projection differs from brute force")
+    return fails
+
+
+def _bf16_bits(vals):
+    """bf16 bit patterns of values that bf16 holds exactly (checked)."""
+    a = np.asarray(vals, dtype=np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), a)
+    return bits
+
+
+def check_a2f_pack(O):
+    fails = []
+    # worked rows: 448 -> s = 1, codes are the values' own e4m3 codes
+    # (448 = 0x7E, -224 = -1.75*2^7 -> 0xF6, 1 -> 0x38, 0.5 -> 0x30, 0 -> 0x00);
+    # amax 896 (negative) -> s = 2; a zero row -> s = 1, all codes 0
+    rows = _bf16_bits([[448.0, -224.0, 1.0, 0.0, 0.5, 0.0, 0.0, 0.0],
+                       [-896.0, 1.0, 2.0, 448.0, -0.0, 0.0, 0.0, 0.0],
+                       [0.0] * 8])
+    codes, s = O.a2f_pack(rows)
+    want = [[0x7E, 0xF6, 0x38, 0x00, 0x30, 0, 0, 0],
+            [0xFE, 0x30, 0x38, 0x76, 0x80, 0, 0, 0],
+            [0] * 8]
+    if not (np.array_equal(codes, np.array(want, dtype=np.uint8))
+            and np.array_equal(s, np.array([1.0, 2.0, 1.0], dtype=np.float32))):
+        fails.append(f"worked A2F rows: codes {codes.tolist()}, scales {s.tolist()}")
+    # random rows: amax element codes to +-448, error within half a step
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((16, 512)) * rng.uniform(1e-3, 40, size=(16, 1))
+    bits = O.f64_to_bf16_bits(y)
+    yb = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, s = O.a2f_pack(bits)
+    j = np.argmax(np.abs(yb), axis=1)
+    if not np.all((codes[np.arange(16), j] & 0x7F) == 0x7E):
+        fails.append("amax element of an A2F row not coded as 448")
+    deq = O.dequantize_tokens(codes, s)
+    r = np.abs(deq / s[:, None].astype(np.float64))
+    step = np.where(r < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(r, 2.0 ** -6))) - 3))
+    if not np.all(np.abs(deq - yb) / s[:, None] <= step / 2 * (1 + 1e-6) + 1e-30):
+        fails.append("A2F pack error beyond half a step of the bf16 values")
+    with open(os.path.join(GOLDEN, "page_figures.json")) as f:
+        figs = {e["id"]: e["value"] for e in json.load(f)["figures"]}
+    if O.hidden_payload_bytes(128, 7168, 1) != figs["a2f_bytes_batch128"]:
+        fails.append("FP8 attention-to-FFN payload != page figure")
+    if O.hidden_payload_bytes(128, 7168, 2) != figs["f2a_bytes_batch128"]:
+        fails.append("BF16 FFN-to-attention payload != page figure")
+    return fails
+
+
 def check_bf16_round(O):
     import torch
     fails = []
@@ -489,7 +567,7 @@ def check_layout(O):
 
 
 ALL_CHECKS = (check_attention, check_gather, check_combine, check_multi_token, check_qproj,
-              check_kv_projection,
+              check_kv_projection, check_output_projection, check_a2f_pack,
               check_bf16_round, check_e4m3, check_quantize, check_cost, check_layout)
 
 

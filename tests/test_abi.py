@@ -133,6 +133,34 @@ def test_pack_weight_validation(lib):
     assert lib.mfa_pack_weight(PM, P, 64, 64, BF16, None) == ALIGN
 
 
+def test_out_proj_validation_and_workspace(lib):
+    def op(**kw):
+        return lib.mfa_out_proj(kw.get("o", P), kw.get("w", P), kw.get("lay", 0), kw.get("B", 128),
+                                kw.get("HD", 16384), kw.get("hid", 7168), kw.get("dt", BF16),
+                                kw.get("ws", P), kw.get("wsb", 1 << 30), kw.get("y", P),
+                                kw.get("codes", P), kw.get("sc", P), None)
+    assert op(o=None) == NULL
+    assert op(y=None, codes=None, sc=None) == NULL               # nothing to write
+    assert op(codes=None) == NULL                                # codes and scales go together
+    assert op(sc=None) == NULL
+    assert op(B=0) == SHAPE
+    assert op(B=257) == SHAPE
+    assert op(HD=1000) == SHAPE
+    assert op(hid=7000) == SHAPE
+    assert op(hid=8256) == SHAPE                                 # above 8192
+    assert op(dt=F32) == DTYPE
+    assert op(lay=2) == SHAPE
+    assert op(o=PM) == ALIGN
+    assert op(codes=PM) == ALIGN
+    assert op(sc=P + 2) == ALIGN
+    assert op(ws=None) == WS
+    need = lib.mfa_out_proj_workspace_bytes(128, 16384, 7168, BF16)
+    assert need > 0 and need % 256 == 0
+    assert op(wsb=need - 1) == WS
+    assert lib.mfa_out_proj_workspace_bytes(128, 16384, 7000, BF16) == 0
+    assert lib.mfa_out_proj_workspace_bytes(128, 16384, 7168, F32) == 0
+
+
 def test_plan_and_split_workspace(lib):
     ns, ch = ctypes.c_int(), ctypes.c_int()
     for B, L in ((32, 4096), (128, 8193), (16, 32768), (4, 65536), (1, 1), (2, 0)):

@@ -141,6 +141,42 @@ def _kv_swapped(x, w, d):
     return v, k
 
 
+def _oproj_heads_reversed(o, w):
+    o = np.asarray(o, float)
+    if o.ndim == 3:
+        o = o[:, ::-1]
+    return mfa.output_projection(o, w)
+
+
+def _oproj_weight_not_transposed(o, w):
+    o = np.asarray(o, float).reshape(len(o), -1)
+    w = np.asarray(w, float)
+    return o @ w if w.shape[0] == o.shape[1] else o @ w.T[:, ::-1]
+
+
+def _a2f_signed_max(bits):
+    y = mfa.bf16_bits_to_f64(bits)
+    amax = np.max(y, axis=1)                   # forgets the absolute value
+    s = np.where(amax == 0, 1.0, amax / 448.0).astype(np.float32)
+    return e4m3.encode_rne((y / s[:, None]).astype(np.float32)), s
+
+
+def _a2f_e4m3_max_240(bits):
+    y = mfa.bf16_bits_to_f64(bits)
+    amax = np.max(np.abs(y), axis=1)
+    s = np.where(amax == 0, 1.0, amax / 240.0).astype(np.float32)
+    return e4m3.encode_rne((y / s[:, None]).astype(np.float32)), s
+
+
+def _a2f_no_scale(bits):
+    y = mfa.bf16_bits_to_f64(bits)
+    return e4m3.encode_rne(y), np.ones(len(y), np.float32)
+
+
+def _payload_with_scales(tokens, hidden, elem_bytes, scale_bytes=0):
+    return tokens * (hidden * elem_bytes + 4)
+
+
 def _kv_rows_offset(x, w, d):
     # the weight rows read one row off (W_k / W_v halves misaligned)
     kv = np.asarray(x, float) @ np.roll(np.asarray(w, float), 1, axis=0).T
@@ -165,6 +201,12 @@ MUTANTS = {
     "multi_token_off_by_one": dict(decode_attention_multi=_multi_off_by_one),
     "kv_projection_k_v_swapped": dict(kv_projection=_kv_swapped),
     "kv_projection_rows_offset": dict(kv_projection=_kv_rows_offset),
+    "output_projection_heads_reversed": dict(output_projection=_oproj_heads_reversed),
+    "output_projection_weight_not_transposed": dict(output_projection=_oproj_weight_not_transposed),
+    "a2f_pack_signed_max": dict(a2f_pack=_a2f_signed_max),
+    "a2f_pack_e4m3_max_240": dict(a2f_pack=_a2f_e4m3_max_240),
+    "a2f_pack_no_scale": dict(a2f_pack=_a2f_no_scale),
+    "a2f_payload_counts_scales": dict(hidden_payload_bytes=_payload_with_scales),
     "bf16_round_truncates": dict(f64_to_bf16_bits=_bf16_truncate),
     "bf16_round_ties_away": dict(f64_to_bf16_bits=_bf16_ties_away),
     "attention_missing_scale": dict(softmax_attention=_attn_no_scale),

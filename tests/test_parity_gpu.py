@@ -471,6 +471,107 @@ def test_multi_token_one_is_single_token(gpu_lib):
         assert torch.equal(a.view(torch.int16), b.squeeze(1).view(torch.int16))
 
 
+# ---------------------------------------------------------------- output projection
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_a2f(y, codes, scales, want, what):
+    """y within the bf16 bars of the fp64 projection. The FP8 pack is an
+    integer decision on the bf16 row: where the library's bf16 y equals the
+    oracle's rounding, codes are bit-exact; a row's scale equals the
+    oracle's when its amax element rounds alike; the rest is checked for
+    validity (adjacent codes, scale within one bf16 step, dequantised values
+    within the bars)."""
+    check_bf16(to_np(y), want["y"], f"{what} y")
+    yb = bf16_bits(y)
+    cg, sg = codes.cpu().numpy(), scales.cpu().numpy()
+    oc, os_ = want["codes"], want["scales"]
+    same_bits = yb == want["y_bits"]
+    same_scale = sg == os_
+    say(f"{what}: y bits equal {same_bits.mean():.5f}, scales equal {same_scale.mean():.3f}")
+    assert same_bits.mean() > 0.99 and same_scale.mean() >= 0.9
+    m = same_scale[:, None] & same_bits
+    assert np.array_equal(cg[m], oc[m]), f"{what}: codes differ where y and scale agree"
+    dc = np.abs((cg & 0x7F).astype(np.int32) - (oc & 0x7F).astype(np.int32))
+    assert np.all(dc[~m] <= 1), f"{what}: codes more than one step apart"
+    assert np.all(np.abs(sg / os_ - 1) <= 2.0 ** -7)
+    deq = omfa.dequantize_tokens(cg, sg)
+    r = rel_l2(deq, want["y"])
+    say(f"{what}: dequantised pack rel_l2={r:.3e}")
+    assert r <= 0.04                    # e4m3 keeps 3 mantissa bits: rms error ~2^-6
+
+
+OUTPROJ = [
+    # (B, heads*head_dim via heads, hidden, packed)
+    (1, 4, 512, False),
+    (5, 64, 7168, False),
+    (64, 4, 1024, True),
+    (70, 64, 2048, False),
+    (128, 64, 7168, True),
+    (128, 64, 7168, False),
+]
+
+
+@pytest.mark.parametrize("B,heads,hidden,packed", OUTPROJ)
+def test_out_proj(gpu_lib, B, heads, hidden, packed):
+    """y = o W_o^T and its per-token FP8 pack (mfa_out_proj) against the
+    oracle; 128 tokens of Step-3's shape is the page's A2F payload (the last
+    two cases). B = 70 and 128 take two passes of at most 64 rows."""
+    import decode_attention_02_amd as mfa
+    w = small(2, batch=B, heads=heads, hidden=hidden, context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=51, out_proj=True)
+    T = workloads.to_torch(inp)
+    say(f"out_proj B={B} HD={heads * 256} hidden={hidden} packed={packed}")
+    wo = mfa.pack_weight(T["w_o"]) if packed else T["w_o"]
+    y, codes, scales = mfa.out_proj(T["o_attn"], wo, packed=packed)
+    torch.cuda.synchronize()
+    want = orun.output_projection(inp)
+    check_a2f(y, codes, scales, want, f"out_proj B={B}")
+    # y alone and the pack alone give the same bytes as both together
+    y2, _, _ = mfa.out_proj(T["o_attn"], wo, packed=packed, want_fp8=False)
+    _, c3, s3 = mfa.out_proj(T["o_attn"], wo, packed=packed, want_y=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(codes, c3) and torch.equal(scales, s3)
+
+
+def test_out_proj_zero_rows(gpu_lib):
+    """A zero attention output row projects to zeros, packs with scale 1 and
+    all-zero codes, next to non-zero rows."""
+    import decode_attention_02_amd as mfa
+    w = small(2, batch=6, heads=4, hidden=512, context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=52, out_proj=True)
+    inp["o_attn"][[0, 4]] = 0
+    T = workloads.to_torch(inp)
+    say("out_proj zero rows")
+    y, codes, scales = mfa.out_proj(T["o_attn"], T["w_o"])
+    torch.cuda.synchronize()
+    sc = scales.cpu().numpy()
+    assert sc[0] == 1.0 and sc[4] == 1.0
+    assert not codes[[0, 4]].any() and not y[[0, 4]].float().abs().sum()
+    check_a2f(y, codes, scales, orun.output_projection(inp), "out_proj zero rows")
+
+
+def test_step_then_out_proj(gpu_lib):
+    """The decode step's attention output fed to the output projection
+    against the oracle's chained fp64 result (errors of both stages add)."""
+    import decode_attention_02_amd as mfa
+    w = small(3, batch=6)
+    inp = workloads.make_inputs(3, workload=w, seed=53, prefill_lens=[0, 63, 64, 200, 700, 129],
+                                out_proj=True)
+    say("step then out_proj")
+    T, cache, step = setup(inp)
+    _, o = run(T, step)
+    y, codes, scales = mfa.out_proj(o, T["w_o"])
+    torch.cuda.synchronize()
+    res = orun.decode_step(inp)
+    want = orun.output_projection(inp, res["o"])
+    check_bf16(to_np(y), want["y"], "step -> out_proj y")
+    deq = omfa.dequantize_tokens(codes.cpu().numpy(), scales.cpu().numpy())
+    assert rel_l2(deq, want["y"]) <= 0.04
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_tiny_f32(gpu_lib):
     inp = workloads.make_inputs(1)

@@ -37,6 +37,9 @@ from typing import Optional
 import numpy as np
 
 BLOCK_TOKENS = 64
+# Step-3's hidden width, for workloads that draw q directly: 128 tokens of it
+# are 896 KiB in FP8 on the StepMesh page's attention-to-FFN traffic model.
+STEP3_HIDDEN = 7168
 
 
 @dataclasses.dataclass(frozen=True)
@@ -102,7 +105,8 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = None,
                 context: Optional[int] = None, workload: Optional[Workload] = None,
-                prefill_lens=None, kv_proj: bool = False, q_len: int = 1):
+                prefill_lens=None, kv_proj: bool = False, q_len: int = 1,
+                out_proj: bool = False):
     """Draw the inputs of one decode step of workload ``index``.
 
     ``batch`` / ``context`` shrink the workload (for tests that need a small
@@ -121,6 +125,9 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
     ``q_len`` > 1 (workloads that draw q) also draws ``q_multi``
     [B][q_len][H][d], the queries of the last q_len tokens of every sequence
     (multi-token decode), after everything else.
+    ``out_proj`` also draws, after all of the above, ``o_attn`` [B][H*d]
+    (an attention output, N(0, 1)) and ``w_o`` [hidden][H*d] (N(0, 1/(H*d))),
+    hidden being the workload's (Step-3's 7168 when it has no query path).
     """
     w = workload if workload is not None else WORKLOADS[index]
     if batch is not None or context is not None:
@@ -205,6 +212,13 @@ def make_inputs(index: int, seed: Optional[int] = None, batch: Optional[int] = N
         if w.has_qproj:
             raise ValueError("multi-token queries are drawn for workloads without a query path")
         out["q_multi"] = _store(rng.standard_normal((B, q_len, H, d), dtype=np.float32), act)
+
+    # 7. attention output and the output projection weight (drawn last)
+    if out_proj:
+        hid = w.hidden if w.has_qproj else STEP3_HIDDEN
+        out["o_attn"] = _store(rng.standard_normal((B, H * d), dtype=np.float32), act)
+        out["w_o"] = _store(rng.standard_normal((hid, H * d), dtype=np.float32)
+                            / np.float32(math.sqrt(H * d)), act)
     return out
 
 
@@ -234,6 +248,9 @@ def to_torch(inp, device="cuda"):
         out["q"] = t(inp["q"], w.act_dtype)
         if "q_multi" in inp:
             out["q_multi"] = t(inp["q_multi"], w.act_dtype)
+    for k in ("o_attn", "w_o"):
+        if k in inp:
+            out[k] = t(inp[k], w.act_dtype)
     for k in ("k_ctx", "v_ctx", "k_new", "v_new"):
         out[k] = t(inp[k], kvin)
     out["ctx_offsets"] = inp["ctx_offsets"]

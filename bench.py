@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--kv-proj", action="store_true",
                     help="compute the new token's K/V from x in the step (w_kv) instead of "
                          "reading it (query-path workloads)")
+    ap.add_argument("--out-proj", action="store_true",
+                    help="the step also projects the attention output (W_o, hidden 7168 for "
+                         "workloads without a query path) and packs it to FP8 (mfa_out_proj)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for HBM counters)")
@@ -83,7 +86,8 @@ def kernel_source_sig() -> str:
 
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """fp64 oracle on the same inputs: the whole batch (query path, cache
-    fill, attention of every sequence), repeated until ``min_seconds`` of
+    fill, attention of every sequence, and the output projection with its FP8
+    pack when the inputs hold W_o), repeated until ``min_seconds`` of
     host time have passed. Returns the record."""
     import numpy as np  # noqa: F401
     from oracle import run as orun
@@ -101,7 +105,9 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
         if multi:
             orun.decode_step_multi(inp)
         else:
-            orun.decode_step(inp)
+            res = orun.decode_step(inp)
+            if "w_o" in inp:
+                orun.output_projection(inp, res["o"])
         total += time.perf_counter() - t0
         runs += 1
     dt = total / runs
@@ -109,7 +115,8 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
     return {"value": w.batch * tq / dt, "unit": "decode tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
-                      f"tokens), fp64 numpy, mean of {runs} runs ({dt:.2f} s each)"}
+                      f"tokens{', with output projection' if 'w_o' in inp else ''}), fp64 numpy, "
+                      f"mean of {runs} runs ({dt:.2f} s each)"}
 
 
 def copy_calibration(mib: int) -> None:
@@ -155,7 +162,11 @@ def main():
     if TQ > 1 and w.has_qproj:
         print("--q-len > 1 needs a workload whose queries are drawn (configs 3, 4)", file=sys.stderr)
         sys.exit(2)
-    inp = workloads.make_inputs(args.config, kv_proj=args.kv_proj, q_len=TQ)
+    if args.out_proj and (TQ > 1 or w.act_dtype != "bf16"):
+        print("--out-proj needs a single-token bf16 workload (configs 2..5)", file=sys.stderr)
+        sys.exit(2)
+    inp = workloads.make_inputs(args.config, kv_proj=args.kv_proj, q_len=TQ,
+                                out_proj=args.out_proj)
     T = workloads.to_torch(inp, dev)
     act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     B = w.batch
@@ -167,6 +178,12 @@ def main():
         w_bytes = (T["w_qdown"].numel() + T["w_qup"].numel()) * T["w_qup"].element_size()
         if args.kv_proj:
             w_bytes += T["w_kv"].numel() * T["w_kv"].element_size()
+    if args.out_proj:
+        hid = T["w_o"].shape[0]
+        HDo = T["w_o"].shape[1]
+        w_bytes += T["w_o"].numel() * 2
+        # algorithmic bytes of one output projection: W_o, o, y, FP8 codes, scales
+        op_bytes = hid * HDo * 2 + B * HDo * 2 + B * hid * 2 + B * hid + B * 4
     rotate = args.rotate or max(2, min(8, -(-2 * 256 * 2 ** 20 // max(kv_bytes + w_bytes, 1))))
 
     sets = []
@@ -189,6 +206,21 @@ def main():
                 wkv = T["w_kv"].clone() if args.kv_proj else None
         sets.append((step, wts, wkv))
     torch.cuda.synchronize()
+    ops = []
+    if args.out_proj:
+        nb = mfa.load().mfa_out_proj_workspace_bytes(B, HDo, hid, 1)
+        for r in range(rotate):
+            ops.append((mfa.pack_weight(T["w_o"]),
+                        torch.empty(max(nb, 16), dtype=torch.uint8, device=dev),
+                        (torch.empty((B, hid), dtype=torch.bfloat16, device=dev),
+                         torch.empty((B, hid), dtype=torch.uint8, device=dev),
+                         torch.empty(B, dtype=torch.float32, device=dev))))
+        torch.cuda.synchronize()
+
+    def project(i):
+        step = sets[i % rotate][0]
+        wo, ws, outs = ops[i % rotate]
+        mfa.out_proj(step.out, wo, packed=True, workspace=ws, out=outs)
 
     if TQ > 1:
         # multi-token decode: the step appends TQ tokens per sequence (the last TQ
@@ -238,6 +270,8 @@ def main():
                  w_kv=wkv)
         else:
             step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+        if args.out_proj:
+            project(i)
 
     q_fixed = [sets[r][0].q if w.has_qproj else T["q"] for r in range(rotate)]
 
@@ -260,6 +294,8 @@ def main():
         g_warm = capture(lambda: [one(i) for i in range(args.warmup)])
         g_steps = capture(lambda: [one(i) for i in range(args.steps)])
         g_attn = capture(lambda: [attention(i, q_fixed[i % rotate]) for i in range(args.steps)])
+        if args.out_proj:
+            g_op = capture(lambda: [project(i) for i in range(args.steps)])
     # warmup
     if use_graph:
         g_warm.replay()
@@ -290,6 +326,24 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     attn_avg = a0.elapsed_time(a1) / args.steps
+    op_rec = None
+    if args.out_proj:
+        # timed region 3: K output projections back to back
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        if use_graph:
+            g_op.replay()
+        else:
+            for i in range(args.steps):
+                project(i)
+        p1.record()
+        torch.cuda.synchronize()
+        op_avg = p0.elapsed_time(p1) / args.steps
+        op_ach = op_bytes / (op_avg * 1e-3) / 1e9
+        op_rec = {"bound": "hbm", "achieved": op_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": op_ach / HBM_PEAK_GBS, "kernels": "gemm_skinny_kernel+outproj_pack_kernel",
+                  "call_avg_us": op_avg * 1e3, "algorithmic_bytes_per_call": op_bytes,
+                  "hidden": hid, "tokens": B}
     achieved = kv_bytes / (attn_avg * 1e-3) / 1e9
     step0 = sets[0][0]
     traffic = counters_for(w.name, kernel_source_sig())
@@ -312,10 +366,11 @@ def main():
                    "num_splits": ns_m if TQ > 1 else step0.num_splits,
                    "chunk_tokens": ch_m if TQ > 1 else step0.chunk_tokens, "rotate": rotate,
                    "q_len": TQ,
-                   "step": ("qproj+kv_proj+kv_append+decode_attn+combine" if args.kv_proj
-                            else "qproj+kv_append+decode_attn+combine") if w.has_qproj
-                   else ("kv_append(q_len)+decode_attn_multi+combine" if TQ > 1
-                         else "kv_append+decode_attn+combine")},
+                   "step": (("qproj+kv_proj+kv_append+decode_attn+combine" if args.kv_proj
+                             else "qproj+kv_append+decode_attn+combine") if w.has_qproj
+                            else ("kv_append(q_len)+decode_attn_multi+combine" if TQ > 1
+                                  else "kv_append+decode_attn+combine"))
+                   + ("+out_proj+fp8_pack" if args.out_proj else "")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (traffic / (attn_avg * 1e-3) / 1e9) if traffic else None,
@@ -327,6 +382,8 @@ def main():
                      "algorithmic_bytes_per_launch": kv_bytes},
         "step_kv_plus_weights_GBps": (kv_bytes + w_bytes) / (ms * 1e-3) / 1e9,
     }
+    if op_rec is not None:
+        rec["out_proj_roofline"] = op_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(rec), flush=True)

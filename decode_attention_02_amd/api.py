@@ -234,9 +234,11 @@ def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, m
 
 
 def out_proj(o: torch.Tensor, w_o: torch.Tensor, packed: bool = False, want_y: bool = True,
-             want_fp8: bool = True, workspace: Optional[torch.Tensor] = None):
+             want_fp8: bool = True, workspace: Optional[torch.Tensor] = None,
+             out: Optional[tuple] = None):
     """Attention output projection y = o W_o^T (bf16) and its per-token FP8
     pack (mfa_out_proj). o [B][HD] (or [B][H][d]); w_o [hidden][HD].
+    ``out`` = (y, codes, scales) preallocated (entries may be None).
     Returns (y or None, codes uint8 [B][hidden] or None, scales [B] or None)."""
     lib = _lib.load()
     o2 = o.reshape(o.shape[0], -1)
@@ -248,9 +250,19 @@ def out_proj(o: torch.Tensor, w_o: torch.Tensor, packed: bool = False, want_y: b
     if workspace is None:
         nb = lib.mfa_out_proj_workspace_bytes(B, HD, hidden, dt)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=o.device)
-    y = torch.empty((B, hidden), dtype=o2.dtype, device=o.device) if want_y else None
-    codes = torch.empty((B, hidden), dtype=torch.uint8, device=o.device) if want_fp8 else None
-    scales = torch.empty(B, dtype=torch.float32, device=o.device) if want_fp8 else None
+    if out is not None:
+        y, codes, scales = out
+        for t, name in ((y, "y"), (codes, "codes"), (scales, "scales")):
+            if t is not None:
+                _dev(t, name)
+    else:
+        y = torch.empty((B, hidden), dtype=o2.dtype, device=o.device) if want_y else None
+        codes = torch.empty((B, hidden), dtype=torch.uint8, device=o.device) if want_fp8 else None
+        scales = torch.empty(B, dtype=torch.float32, device=o.device) if want_fp8 else None
+    if y is not None and y.numel() != B * hidden:
+        raise ValueError("y must hold B x hidden values")
+    if codes is not None and (codes.numel() != B * hidden or scales is None or scales.numel() != B):
+        raise ValueError("codes must hold B x hidden bytes and scales B floats")
     check("mfa_out_proj", lib.mfa_out_proj(
         _ptr(o2), _ptr(w_o), MFA_WEIGHTS_PACKED if packed else MFA_WEIGHTS_ROWMAJOR, B, HD,
         hidden, dt, _ptr(workspace), workspace.numel(), _ptr(y), _ptr(codes), _ptr(scales),

@@ -84,7 +84,7 @@ struct AppendArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 
 // Query path.
-// bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 64. With ksplit > 1 writes fp32
+// bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 128. With ksplit > 1 writes fp32
 // partials part[ks][M][N] (K slice ks); with ksplit == 1 and out_bf16 set,
 // writes bf16 C directly. ntiles (2, 4, or 5 with M <= 32) = 16-column tiles
 // per workgroup.
@@ -93,10 +93,12 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // 16-row tiles per 32-wide k-step.
 int gemm_row_tiles(int M);
 // W2 (nullable): columns N1 .. N-1 come from W2 (its rows 0 .. N-N1-1)
-// instead of W; N1 % 16 == 0.
+// instead of W; N1 % 16 == 0. stream_w: non-temporal weight loads (row-major
+// A only).
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
-                            hipStream_t stream, const uint16_t* W2 = nullptr, int N1 = 0);
+                            hipStream_t stream, const uint16_t* W2 = nullptr, int N1 = 0,
+                            bool stream_w = false);
 // Row-major bf16 W [N][K] -> operand-order packed weight (N % 16 == 0, K % 32 == 0).
 hipError_t launch_pack_weight(const uint16_t* W, uint16_t* P, int N, int K, hipStream_t stream);
 // n[m][j] = bf16(c / sqrt(mean c^2 + eps) * g), c = sum over ksplit partials.

@@ -25,7 +25,8 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 mfa_status from_hip(hipError_t e) { return e == hipSuccess ? MFA_OK : MFA_ERR_HIP; }
 
 // ---- query path planning -------------------------------------------------
-constexpr int kRowsPerPass = 64;     // matrix-core GEMM handles <= 64 rows per pass
+constexpr int kRowsPerPass = 64;     // rows per pass of the query path
+constexpr int kOutProjRows = 128;    // rows per pass of the output projection (GEMM limit)
 
 struct GemmPlan {
   int ntiles;        // 16-column tiles per workgroup (2 or 4)
@@ -171,7 +172,7 @@ struct OutProjPlan {
 };
 OutProjPlan plan_out_proj(int B, int HD, int hidden) {
   OutProjPlan p{};
-  p.rows = B < kRowsPerPass ? B : kRowsPerPass;
+  p.rows = B < kOutProjRows ? B : kOutProjRows;
   p.g = plan_gemm(hidden, HD, p.rows);
   p.total = round_up(static_cast<size_t>(p.g.ks) * p.rows * hidden * 4, 256);
   return p;
@@ -211,7 +212,8 @@ mfa_status mfa_out_proj(const void* o, const void* w_o, int weight_layout, int B
     const uint16_t* oa = static_cast<const uint16_t*>(o) + static_cast<size_t>(r0) * HD;
     hipError_t e = mfa::launch_gemm_bf16(oa, static_cast<const uint16_t*>(w_o), part, nullptr, M,
                                          hidden, HD, p.g.ks, p.g.ntiles,
-                                         weight_layout == MFA_WEIGHTS_PACKED, false, st);
+                                         weight_layout == MFA_WEIGHTS_PACKED, false, st, nullptr,
+                                         0, true);
     if (e != hipSuccess) return MFA_ERR_HIP;
     e = mfa::launch_outproj_pack(
         part, p.g.ks, M, hidden, y ? static_cast<uint16_t*>(y) + static_cast<size_t>(r0) * hidden : nullptr,

@@ -20,7 +20,7 @@
 namespace mfa {
 
 // Skinny bf16 product on the matrix cores: part[ks][m][n] = sum over the K
-// slice ks of A[m][k] * W[n][k] for m < M <= 64.
+// slice ks of A[m][k] * W[n][k] for m < M <= 128.
 //
 // A workgroup of 8 waves owns NT*16 output columns and one K slice; the
 // waves take interleaved 32-wide k-steps of that slice, so every wave
@@ -42,17 +42,68 @@ namespace mfa {
 // (they feed only output rows that are not written).
 constexpr int kGemmWaves = 8;
 
+// Sum the waves' accumulators for rows r0 .. r0+TM-1 of the tile (red[w]
+// holds them at row r - r0) and write rows below M: fp32 partials of slice
+// ks, or bf16 when out_bf16 is set.
+template <int TM, int TN, int kPad>
+__device__ __forceinline__ void gemm_store_rows(const float (*red)[TM * kPad], int tid, int r0,
+                                                int M, int N, int n0, int ks,
+                                                float* __restrict__ part,
+                                                uint16_t* __restrict__ out_bf16) {
+  constexpr int kOut = TM * TN;
+  if constexpr (kOut % (kGemmWaves * 64) != 0 || (kOut / (kGemmWaves * 64)) % 2 == 1) {
+    // tile sizes that do not split into pairs per thread: one output at a time
+    for (int e = tid; e < kOut; e += kGemmWaves * 64) {
+      const int ml = e / TN, nl = e % TN, m = r0 + ml;
+      if (m >= M) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][ml * kPad + nl];
+      if (out_bf16)
+        __builtin_nontemporal_store(f32_to_bf16(sum), out_bf16 + static_cast<size_t>(m) * N + n0 + nl);
+      else
+        store_nt(part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl, sum);
+    }
+  } else {
+    constexpr int kPer = kOut / (kGemmWaves * 64);   // outputs per thread (contiguous in n)
+    const int e0 = tid * kPer;
+    const int ml = e0 / TN, nl = e0 % TN, m = r0 + ml;
+    if (m >= M) return;
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = ml * kPad + nl + j;
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][o];
+      v[j] = sum;
+    }
+    if (out_bf16) {
+      uint16_t* dst = out_bf16 + static_cast<size_t>(m) * N + n0 + nl;
+#pragma unroll
+      for (int j = 0; j < kPer; j += 2) store_nt(dst + j, pack_bf16x2(v[j], v[j + 1]));
+    } else {
+      float* dst = part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl;
+#pragma unroll
+      for (int j = 0; j < kPer; j += 2) store_nt(dst + j, make_float2(v[j], v[j + 1]));
+    }
+  }
+}
+
+// NTW marks the weight loads non-temporal: a weight that is read once per
+// call streams through L2 without pushing out the activations and partials.
 // Columns N1 .. N-1 may come from a second weight matrix W2 (rows 0 ..
 // N-N1-1 of it; null W2: all from W), so two products that share A run as
 // one launch (the down-projection and the K/V projection share x).
-template <int MT, int NT, int PD, bool PACKED, bool PA>
+template <int MT, int NT, int PD, bool PACKED, bool PA, bool NTW>
 __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float* __restrict__ part,
     uint16_t* __restrict__ out_bf16, int M, int N, int K, int kchunk,
     const uint16_t* __restrict__ W2, int N1) {
-  constexpr int TM = MT * 16, TN = NT * 16;
+  constexpr int TN = NT * 16;
+  constexpr int RG = MT < 4 ? MT : 4;                // row tiles per LDS reduction round
   constexpr int kPad = TN + 4;                       // padded LDS row (floats)
-  __shared__ __attribute__((aligned(16))) float red[kGemmWaves][TM * kPad];
+  __shared__ __attribute__((aligned(16))) float red[kGemmWaves][RG * 16 * kPad];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -106,7 +157,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       wb[slot][nt] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr[nt], wofs + kk * kStepBytes, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr[nt], wofs + kk * kStepBytes, 0, NTW ? 2 : 0));
     if constexpr (PA) {
       const uint16_t* au = A + static_cast<size_t>((kbeg / 32 + kk) * MT) * 64 * 8 + lane * 8;
 #pragma unroll
@@ -134,60 +185,19 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_skinny_kernel(
     }
   }
 
-  // accumulator lane holds C[mt*16 + 4g + i][nt*16 + c]; sum the waves
+  // accumulator lane holds C[mt*16 + 4g + i][nt*16 + c]; the waves' sums
+  // meet in LDS, RG row tiles at a time
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mg = 0; mg < MT; mg += RG) {
+    if (mg) __syncthreads();                         // previous group's reads are done
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int mt = 0; mt < RG; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[w][(mt * 16 + 4 * g + i) * kPad + nt * 16 + c] = acc[mt][nt][i];
-  __syncthreads();
-  constexpr int kOut = TM * TN;
-  if constexpr (kOut % (kGemmWaves * 64) != 0 || (kOut / (kGemmWaves * 64)) % 2 == 1) {
-    // tile sizes that do not split into pairs per thread: one output at a time
-    for (int e = tid; e < kOut; e += kGemmWaves * 64) {
-      const int m = e / TN, nl = e % TN;
-      if (m >= M) continue;
-      float sum = 0.f;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][m * kPad + nl];
-      if (out_bf16)
-        __builtin_nontemporal_store(f32_to_bf16(sum), out_bf16 + static_cast<size_t>(m) * N + n0 + nl);
-      else
-        store_nt(part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl, sum);
-    }
-    return;
-  }
-  constexpr int kPer = kOut / (kGemmWaves * 64);     // outputs per thread (contiguous in n)
-  const int e0 = tid * kPer;
-  const int m = e0 / TN, nl = e0 % TN;
-  if (m < M) {
-    float v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int o = m * kPad + nl + j;
-      float sum = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kGemmWaves; ++ww) sum += red[ww][o];
-      v[j] = sum;
-    }
-    if (out_bf16) {
-      uint16_t* dst = out_bf16 + static_cast<size_t>(m) * N + n0 + nl;
-      if constexpr (kPer == 1) {
-        __builtin_nontemporal_store(f32_to_bf16(v[0]), dst);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kPer; j += 2) store_nt(dst + j, pack_bf16x2(v[j], v[j + 1]));
-      }
-    } else {
-      float* dst = part + (static_cast<size_t>(ks) * M + m) * N + n0 + nl;
-      if constexpr (kPer == 1) {
-        store_nt(dst, v[0]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kPer; j += 2) store_nt(dst + j, make_float2(v[j], v[j + 1]));
-      }
-    }
+        for (int i = 0; i < 4; ++i) red[w][(mt * 16 + 4 * g + i) * kPad + nt * 16 + c] = acc[mg + mt][nt][i];
+    __syncthreads();
+    gemm_store_rows<RG * 16, TN, kPad>(red, tid, mg * 16, M, N, n0, ks, part, out_bf16);
   }
 }
 
@@ -404,50 +414,56 @@ struct GemmCall {
   int M, N, K, kchunk, N1;
 };
 
-template <int MT, int NT, int PD, bool PACKED, bool PA>
+template <int MT, int NT, int PD, bool PACKED, bool PA, bool NTW>
 static void launch_gemm_shape(dim3 grid, const GemmCall& c, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED, PA>), grid, dim3(kGemmWaves * 64), 0,
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, PD, PACKED, PA, NTW>), grid, dim3(kGemmWaves * 64), 0,
                      stream, c.A, c.W, c.part, c.out_bf16, c.M, c.N, c.K, c.kchunk, c.W2, c.N1);
 }
 
-template <bool PACKED, bool PA>
+template <bool PACKED, bool PA, bool NTW>
 static void launch_gemm_variant(const GemmCall& c, int ksplit, int ntiles, hipStream_t stream) {
   const int M = c.M;
   if (ntiles == 4) {
     dim3 grid(static_cast<unsigned>(c.N / 64), static_cast<unsigned>(ksplit));
-    if (M <= 16) launch_gemm_shape<1, 4, 4, PACKED, PA>(grid, c, stream);
-    else if (M <= 32) launch_gemm_shape<2, 4, 4, PACKED, PA>(grid, c, stream);
-    else launch_gemm_shape<4, 4, 3, PACKED, PA>(grid, c, stream);
+    if (M <= 16) launch_gemm_shape<1, 4, 4, PACKED, PA, NTW>(grid, c, stream);
+    else if (M <= 32) launch_gemm_shape<2, 4, 4, PACKED, PA, NTW>(grid, c, stream);
+    else if (M <= 64) launch_gemm_shape<4, 4, 3, PACKED, PA, NTW>(grid, c, stream);
+    else launch_gemm_shape<8, 4, 2, PACKED, PA, NTW>(grid, c, stream);
   } else if (ntiles == 5) {
     dim3 grid(static_cast<unsigned>(c.N / 80), static_cast<unsigned>(ksplit));
     // (64 rows x 80 columns would need more LDS than a CU has for the reduction)
-    if (M <= 16) launch_gemm_shape<1, 5, 4, PACKED, PA>(grid, c, stream);
-    else launch_gemm_shape<2, 5, 4, PACKED, PA>(grid, c, stream);
+    if (M <= 16) launch_gemm_shape<1, 5, 4, PACKED, PA, NTW>(grid, c, stream);
+    else launch_gemm_shape<2, 5, 4, PACKED, PA, NTW>(grid, c, stream);
   } else {
     dim3 grid(static_cast<unsigned>(c.N / 32), static_cast<unsigned>(ksplit));
-    if (M <= 16) launch_gemm_shape<1, 2, 8, PACKED, PA>(grid, c, stream);
-    else if (M <= 32) launch_gemm_shape<2, 2, 6, PACKED, PA>(grid, c, stream);
-    else launch_gemm_shape<4, 2, 4, PACKED, PA>(grid, c, stream);
+    if (M <= 16) launch_gemm_shape<1, 2, 8, PACKED, PA, NTW>(grid, c, stream);
+    else if (M <= 32) launch_gemm_shape<2, 2, 6, PACKED, PA, NTW>(grid, c, stream);
+    else if (M <= 64) launch_gemm_shape<4, 2, 4, PACKED, PA, NTW>(grid, c, stream);
+    else launch_gemm_shape<8, 2, 4, PACKED, PA, NTW>(grid, c, stream);
   }
 }
 
-int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+int gemm_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8)); }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, uint16_t* out_bf16,
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
-                            hipStream_t stream, const uint16_t* W2, int N1) {
-  if (M < 1 || M > 64) return hipErrorInvalidValue;
+                            hipStream_t stream, const uint16_t* W2, int N1, bool stream_w) {
+  if (M < 1 || M > 128) return hipErrorInvalidValue;
   if (ntiles != 2 && ntiles != 4 && ntiles != 5) return hipErrorInvalidValue;
   if (ntiles == 5 && M > 32) return hipErrorInvalidValue;
   if (N % (16 * ntiles)) return hipErrorInvalidValue;
   if (W2 && (N1 <= 0 || N1 >= N || N1 % 16)) return hipErrorInvalidValue;
   const GemmCall c{A, W, W2, part, out_bf16, M, N, K, K / ksplit, W2 ? N1 : N};
+  if (a_packed && stream_w) return hipErrorInvalidValue;   // not instantiated
   if (a_packed) {
-    if (packed) launch_gemm_variant<true, true>(c, ksplit, ntiles, stream);
-    else launch_gemm_variant<false, true>(c, ksplit, ntiles, stream);
+    if (packed) launch_gemm_variant<true, true, false>(c, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, true, false>(c, ksplit, ntiles, stream);
+  } else if (stream_w) {
+    if (packed) launch_gemm_variant<true, false, true>(c, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, false, true>(c, ksplit, ntiles, stream);
   } else {
-    if (packed) launch_gemm_variant<true, false>(c, ksplit, ntiles, stream);
-    else launch_gemm_variant<false, false>(c, ksplit, ntiles, stream);
+    if (packed) launch_gemm_variant<true, false, false>(c, ksplit, ntiles, stream);
+    else launch_gemm_variant<false, false, false>(c, ksplit, ntiles, stream);
   }
   return hipGetLastError();
 }

@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--out-proj", action="store_true",
                     help="the step also projects the attention output (W_o, hidden 7168 for "
                          "workloads without a query path) and packs it to FP8 (mfa_out_proj)")
+    ap.add_argument("--fp8-queries", action="store_true",
+                    help="FP8-cache workloads: queries quantized per head and Q.K^T on the FP8 "
+                         "matrix cores (mfa_decode_attn_q8)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for HBM counters)")
@@ -84,7 +87,7 @@ def kernel_source_sig() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0):
+def cpu_baseline(inp, min_seconds: float = 10.0, fp8_queries: bool = False):
     """fp64 oracle on the same inputs: the whole batch (query path, cache
     fill, attention of every sequence, and the output projection with its FP8
     pack when the inputs hold W_o), repeated until ``min_seconds`` of
@@ -103,9 +106,9 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
     while total < min_seconds and runs < 50:
         t0 = time.perf_counter()
         if multi:
-            orun.decode_step_multi(inp)
+            orun.decode_step_multi(inp, fp8_queries=fp8_queries)
         else:
-            res = orun.decode_step(inp)
+            res = orun.decode_step(inp, fp8_queries=fp8_queries)
             if "w_o" in inp:
                 orun.output_projection(inp, res["o"])
         total += time.perf_counter() - t0
@@ -162,6 +165,10 @@ def main():
     if TQ > 1 and w.has_qproj:
         print("--q-len > 1 needs a workload whose queries are drawn (configs 3, 4)", file=sys.stderr)
         sys.exit(2)
+    if args.fp8_queries and (w.kv_dtype != "fp8" or w.has_qproj):
+        print("--fp8-queries needs an FP8-cache workload (config 4)", file=sys.stderr)
+        sys.exit(2)
+    MULTI = TQ > 1 or args.fp8_queries          # append + mfa_decode_attn_multi / _q8 per step
     if args.out_proj and (TQ > 1 or w.act_dtype != "bf16"):
         print("--out-proj needs a single-token bf16 workload (configs 2..5)", file=sys.stderr)
         sys.exit(2)
@@ -222,9 +229,10 @@ def main():
         wo, ws, outs = ops[i % rotate]
         mfa.out_proj(step.out, wo, packed=True, workspace=ws, out=outs)
 
-    if TQ > 1:
+    if MULTI:
         # multi-token decode: the step appends TQ tokens per sequence (the last TQ
         # positions) and attends with the TQ queries of each, causal among them
+        # (TQ = 1 with FP8 queries: the single-token step through the same call)
         ns_m, ch_m = mfa.decode_plan(B * TQ, w.heads, w.head_dim, maxlen, w.kv_dtype)
         if args.splits:
             ns_m = args.splits
@@ -232,6 +240,7 @@ def main():
         k_m = T["k_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
         v_m = T["v_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
         pos_m = (T["seq_lens"] - TQ).to(torch.int32)
+        q_m = T["q_multi"] if TQ > 1 else T["q"].unsqueeze(1)
         multi = []
         for r in range(rotate):
             nb = mfa.split_workspace_bytes(B * TQ, w.heads, w.head_dim, ns_m)
@@ -241,12 +250,12 @@ def main():
     def attention_multi(i, combine):
         step = sets[i % rotate][0]
         ws, out = multi[i % rotate]
-        mfa.decode_attn_multi(T["q_multi"], step.cache, T["seq_lens"], maxlen, step.sm_scale,
+        mfa.decode_attn_multi(q_m, step.cache, T["seq_lens"], maxlen, step.sm_scale,
                               ns_m, ch_m, out=out if combine else None, workspace=ws,
-                              combine=combine)
+                              combine=combine, fp8_queries=args.fp8_queries)
 
     def attention(i, q):
-        if TQ > 1:
+        if MULTI:
             attention_multi(i, combine=ns_m == 1)
             return
         step = sets[i % rotate][0]
@@ -261,7 +270,7 @@ def main():
         """One decode step on buffer set i % rotate (DecodeStep: query path,
         KV append, attention, split combine)."""
         step, wts, wkv = sets[i % rotate]
-        if TQ > 1:
+        if MULTI:
             mfa.kv_append(step.cache, k_m, v_m, pos_m)
             attention_multi(i, combine=True)
             return
@@ -358,17 +367,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else ("fp8-kv/bf16" if w.kv_dtype == "fp8" else "f32"),
+        "dtype": "bf16" if w.kv_dtype == "bf16" else (
+            ("fp8-qk/bf16-pv" if args.fp8_queries else "fp8-kv/bf16") if w.kv_dtype == "fp8"
+            else "f32"),
         "data": "synthetic (seeded N(0,1) K/V, N(0,1/fan_in) weights, random-init)",
         "config": {"workload": w.name, "batch": B, "context": maxlen, "heads": w.heads,
                    "head_dim": w.head_dim, "kv_dtype": w.kv_dtype, "hidden": w.hidden,
                    "q_rank": w.q_rank, "paged": w.paged,
-                   "num_splits": ns_m if TQ > 1 else step0.num_splits,
-                   "chunk_tokens": ch_m if TQ > 1 else step0.chunk_tokens, "rotate": rotate,
-                   "q_len": TQ,
+                   "num_splits": ns_m if MULTI else step0.num_splits,
+                   "chunk_tokens": ch_m if MULTI else step0.chunk_tokens, "rotate": rotate,
+                   "q_len": TQ, "fp8_queries": bool(args.fp8_queries),
                    "step": (("qproj+kv_proj+kv_append+decode_attn+combine" if args.kv_proj
                              else "qproj+kv_append+decode_attn+combine") if w.has_qproj
-                            else ("kv_append(q_len)+decode_attn_multi+combine" if TQ > 1
+                            else ("kv_append(q_len)+decode_attn_q8+combine" if args.fp8_queries
+                                  else "kv_append(q_len)+decode_attn_multi+combine" if TQ > 1
                                   else "kv_append+decode_attn+combine"))
                    + ("+out_proj+fp8_pack" if args.out_proj else "")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -385,7 +397,7 @@ def main():
     if op_rec is not None:
         rec["out_proj_roofline"] = op_rec
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp)
+        rec["cpu_baseline"] = cpu_baseline(inp, fp8_queries=args.fp8_queries)
     print(json.dumps(rec), flush=True)
 
 

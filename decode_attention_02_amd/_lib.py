@@ -79,6 +79,8 @@ SIGNATURES = {
     "mfa_decode_attn": (_i, [_p, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p, _i, _p]),
     "mfa_decode_attn_multi": (_i, [_p, _i, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p,
                                    _i, _p]),
+    "mfa_decode_attn_q8": (_i, [_p, _i, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p,
+                                _i, _p]),
     "mfa_combine": (_i, [_p, _sz, _i, _i, _i, _i, _p, _i, _p]),
     "mfa_out_proj_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_out_proj": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _sz, _p, _p, _p, _p]),

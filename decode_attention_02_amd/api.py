@@ -202,11 +202,12 @@ def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, m
                       chunk_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
                       out_dtype: Optional[torch.dtype] = None,
-                      combine: bool = True) -> Optional[torch.Tensor]:
+                      combine: bool = True, fp8_queries: bool = False) -> Optional[torch.Tensor]:
     """Attention of q [B][q_len][H][d] (the last q_len tokens of every sequence,
     causal among themselves) over the cache (mfa_decode_attn_multi); out is
     [B][q_len][H][d]. Splits and ``combine`` as in ``decode_attn``, over the
-    B * q_len rows."""
+    B * q_len rows. ``fp8_queries`` (FP8 caches): q quantized per (row, head)
+    and Q.K^T on the FP8 matrix cores (mfa_decode_attn_q8)."""
     lib = _lib.load()
     B, T, H, d = q.shape
     _dev(q, "q")
@@ -224,7 +225,9 @@ def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, m
         workspace = torch.empty(split_workspace_bytes(B * T, H, d, num_splits), dtype=torch.uint8,
                                 device=q.device)
     desc = cache.desc()
-    check("mfa_decode_attn_multi", lib.mfa_decode_attn_multi(
+    fn, name = ((lib.mfa_decode_attn_q8, "mfa_decode_attn_q8") if fp8_queries
+                else (lib.mfa_decode_attn_multi, "mfa_decode_attn_multi"))
+    check(name, fn(
         _ptr(q), _DTYPES[q.dtype], B, T, H, ctypes.byref(desc), _ptr(seq_lens), int(max_seq_len),
         float(sm_scale), int(num_splits), int(chunk_tokens), _ptr(workspace),
         workspace.numel() if workspace is not None else 0,

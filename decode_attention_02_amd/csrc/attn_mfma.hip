@@ -41,6 +41,11 @@
 // bf16 rounding.
 // Several query tokens per sequence (multi-token decode) are virtual rows:
 // row r = sequence b, query token j walks b's cache up to its own position.
+// FP8 queries (Q8, FP8 caches): the QK waves quantize each head's q row to
+// e4m3 with one scale amax/448 (the cache's own per-token codec) while
+// staging it, and multiply the raw K codes from the ring on the 16x16x128
+// FP8 matrix cores (two products per 16x16 tile, no K conversion); the
+// logits are scaled by the K and q scales. The PV side is unchanged.
 #include <type_traits>
 
 #include "device_common.h"
@@ -99,12 +104,17 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
 // HT: 16-head tiles per workgroup (4: all 64 heads; 2: half of them, two
 // workgroups per (sequence, split) reading the same K/V blocks).
-template <bool FP8, int RK, int RV, int HT>
+template <bool FP8, int RK, int RV, int HT, bool Q8 = false>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
+  static_assert(!Q8 || FP8, "FP8 queries run against FP8 caches");
   using C = Cfg<FP8>;
   constexpr int kHW = 16 * HT;                                          // heads of this workgroup
   constexpr int kHS = kH / kHW;                                         // workgroups per split
-  __shared__ __attribute__((aligned(16))) uint4 q_lds[HT * 8 * 64];     // HT x 8 KB, operand order
+  // Q in operand order: bf16 HT x 8 KB; Q8 codes HT x 4 KB, block (ht, k2),
+  // lane (gg, cc), two uint4: codes of q[h0+16ht+cc][128k2 + 16gg .. +16]
+  // and [128k2 + 64 + 16gg .. +16] (the K ring's unit pair for k2)
+  __shared__ __attribute__((aligned(16))) uint4 q_lds[HT * (Q8 ? 4 : 8) * 64];
+  __shared__ float qs_lds[Q8 ? kHW : 1];                                 // Q8: q scale per head
   __shared__ __attribute__((aligned(16))) uint4 p_lds[2][HT * 2 * 64];  // 2 x HT x 2 KB, operand order
   __shared__ __attribute__((aligned(16))) f32x4_t s_lds[2][4 * HT * 64]; // logits by (QK wave, tile, lane)
   __shared__ __attribute__((aligned(16))) float red[2][kHW * 4];        // block max [head][QK wave]
@@ -149,13 +159,60 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // iterations later.
   constexpr int kQLoads = 2 * HT;                                       // 16-byte loads per QK thread
   static_assert(kQLoads == 4 || kQLoads == 8, "Q staging covers two or four head tiles");
+  // Q8 staging: kTPH adjacent threads share a head, each with kDPT
+  // consecutive dims (so a head's amax is a reduction over kTPH lanes)
+  constexpr int kTPH = 256 / kHW;
+  constexpr int kDPT = kD / kTPH;
+  static_assert(kDPT == 8 * kQLoads, "Q8 staging: one 16-byte load per 8 dims");
   auto q_src = [&](int r) __attribute__((always_inline)) -> const uint4* {
+    if constexpr (Q8) {
+      return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
+                                            (h0 + tid / kTPH) * kD + (tid % kTPH) * kDPT + 8 * r);
+    }
     const int idx = tid + 256 * r;
     const int ln = idx & 63, blk = idx >> 6;
     const int ht = blk >> 3, s = blk & 7;
     const int gg = ln >> 4, cc = ln & 15;
     return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
                                           (h0 + ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
+  };
+  // Q8: this thread's kDPT bf16 values of head h0 + tid/kTPH -> e4m3 codes
+  // in operand order, scale = amax/448 of the head's row (1 when 0), code =
+  // RNE e4m3 of the correctly rounded quotient
+  auto stage_q8 = [&](const uint4 (&qv)[8]) __attribute__((always_inline)) {
+    const int hl = tid / kTPH, j = tid % kTPH;
+    float x[kDPT];
+#pragma unroll
+    for (int r = 0; r < kQLoads; ++r) {
+      const uint32_t u[4] = {qv[r].x, qv[r].y, qv[r].z, qv[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * r + 2 * e] = __uint_as_float(u[e] << 16);
+        x[8 * r + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < kDPT; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int off = 1; off < kTPH; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int p = 0; p < kDPT / 16; ++p) {        // pieces of 16 codes
+      uint32_t wd[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v |= encode_e4m3_rne(x[16 * p + 4 * q4 + e] / sc) << (8 * e);
+        wd[q4] = v;
+      }
+      const int d0 = j * kDPT + 16 * p;
+      const int k2 = d0 >> 7, half = (d0 >> 6) & 1, gp = (d0 >> 4) & 3;
+      q_lds[((((hl >> 4) * 2 + k2) * 64) + gp * 16 + (hl & 15)) * 2 + half] =
+          make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    if (j == 0) qs_lds[hl] = sc;
   };
   // prologue of either role: the QK waves load Q, then ring blocks 0 .. R-1,
   // then stage Q; the PV waves fill their ring after the Q barrier
@@ -170,9 +227,14 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
       __builtin_amdgcn_sched_barrier(0);
-      q_lds[tid] = q0; q_lds[tid + 256] = q1; q_lds[tid + 512] = q2; q_lds[tid + 768] = q3;
-      if constexpr (kQLoads == 8) {
-        q_lds[tid + 1024] = q4; q_lds[tid + 1280] = q5; q_lds[tid + 1536] = q6; q_lds[tid + 1792] = q7;
+      if constexpr (Q8) {
+        const uint4 qv[8] = {q0, q1, q2, q3, q4, q5, q6, q7};
+        stage_q8(qv);
+      } else {
+        q_lds[tid] = q0; q_lds[tid + 256] = q1; q_lds[tid + 512] = q2; q_lds[tid + 768] = q3;
+        if constexpr (kQLoads == 8) {
+          q_lds[tid + 1024] = q4; q_lds[tid + 1280] = q5; q_lds[tid + 1536] = q6; q_lds[tid + 1792] = q7;
+        }
       }
     }
   };
@@ -237,6 +299,27 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       f32x4_t s_acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
+        // two 128-deep k-steps: the K unit pair (2k2, 2k2+1) as codes
+        static_for<0, 2>([&](auto kc) {
+          constexpr int k2 = decltype(kc)::value;
+          const uint4 u0 = ring[slot][2 * k2], u1 = ring[slot][2 * k2 + 1];
+          const i32x8_t kop = {static_cast<int>(u0.x), static_cast<int>(u0.y),
+                               static_cast<int>(u0.z), static_cast<int>(u0.w),
+                               static_cast<int>(u1.x), static_cast<int>(u1.y),
+                               static_cast<int>(u1.z), static_cast<int>(u1.w)};
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const int qi = ((ht * 2 + k2) * 64 + lane) * 2;
+            const uint4 qa = q_lds[qi], qb = q_lds[qi + 1];
+            const i32x8_t qop = {static_cast<int>(qa.x), static_cast<int>(qa.y),
+                                 static_cast<int>(qa.z), static_cast<int>(qa.w),
+                                 static_cast<int>(qb.x), static_cast<int>(qb.y),
+                                 static_cast<int>(qb.z), static_cast<int>(qb.w)};
+            s_acc[ht] = mfma_16x16x128_e4m3(kop, qop, s_acc[ht]);
+          }
+        });
+      }
       // bf16: the Q operands of k-step s+1 are read from LDS while step s
       // multiplies (FP8: its operand conversions fill the gaps instead)
       constexpr bool kQdb = !FP8;
@@ -245,7 +328,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) qop[0][ht] = as_bf16x8(q_lds[(ht * 8) * 64 + lane]);
       }
-      static_for<0, 8>([&](auto sc) {
+      if constexpr (!Q8) static_for<0, 8>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         if constexpr (kQdb && s + 1 < 8) {
 #pragma unroll
@@ -271,9 +354,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
                              __uint_as_float(k4.w)};
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int ht = 0; ht < HT; ++ht) {
+          // Q8: and the q scale of head h0 + 16ht + c
+          const float qsc = Q8 ? qs_lds[Q8 ? 16 * ht + c : 0] : 1.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s_acc[ht][e] *= ks[e];
+          for (int e = 0; e < 4; ++e) s_acc[ht][e] *= Q8 ? ks[e] * qsc : ks[e];
+        }
         vs_lds[par][ww * 4 + g] = ring[slot][5];   // same value from the 16 lanes of a row
       }
       const int lim = tokens_in(n);
@@ -576,7 +662,10 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
   const long long pairs = static_cast<long long>(B) * a.num_splits;
   const bool half = pairs * 2 <= 256 && pairs % 8 == 0;
   const dim3 grid(static_cast<unsigned>(pairs * (half ? 2 : 1))), block(512);
-  if (fp8) {
+  if (fp8 && a.fp8_queries) {
+    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4, true>), grid, block, 0, stream, a);
+  } else if (fp8) {
     if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4>), grid, block, 0, stream, a);
   } else {

@@ -39,6 +39,19 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// 16x16x128 OCP-e4m3 matrix-core product (the f8f6f4 family, both operands
+// e4m3, unit block scales: E8M0 exponent 127): acc[m][n] += sum_k A[m][k] *
+// B[k][n] into the fp32 accumulator. Lane l holds 32 codes of row l%16 of A
+// and of column l%16 of B; both operands give k the same (lane group, byte)
+// positions, so pairing the bytes of the two operands the same way gives
+// the dot product whatever the order of k within them.
+__device__ __forceinline__ f32x4_t mfma_16x16x128_e4m3(const i32x8_t& a, const i32x8_t& b,
+                                                       const f32x4_t& acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
 // Non-temporal stores for results the next kernel reads: they leave the
 // L2 write-back path early, so less dirty data is left for the write-back
 // at the end of the kernel (measured: ~1.5 us less between back-to-back

@@ -39,6 +39,9 @@ struct AttnArgs {
   // first seq_lens[b] - (q_len - 1 - j) tokens: causal among the new tokens,
   // which are the last q_len of the sequence.
   int q_len;
+  // Matrix-core kernel, FP8 cache: quantize each (row, head) of q to e4m3
+  // (scale amax/448) and run Q.K^T on the FP8 matrix cores.
+  int fp8_queries;
 };
 
 // B: virtual rows (sequences x q_len).

@@ -477,7 +477,7 @@ struct AttnCall {
 mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_cache* cache,
                         const int32_t* seq_lens, int max_seq_len, float sm_scale, int num_splits,
                         int chunk_tokens, void* workspace, size_t workspace_bytes, void* out,
-                        int out_dtype, AttnCall* c, int q_len = 1) {
+                        int out_dtype, AttnCall* c, int q_len = 1, bool fp8_queries = false) {
   if (!q || !seq_lens) return MFA_ERR_NULL;
   const mfa_status cs = check_cache(cache);
   if (cs != MFA_OK) return cs;
@@ -500,6 +500,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return MFA_ERR_SHAPE;
   c->mfma = mfma_shape(H, d, cache->dtype);
+  if (fp8_queries && !(c->mfma && cache->dtype == MFA_FP8_E4M3)) return MFA_ERR_UNSUPPORTED;
   if (c->mfma) {
     if (q_dtype != MFA_BF16) return MFA_ERR_DTYPE;
   } else if (valu_shape(H, d, cache->dtype)) {
@@ -535,6 +536,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.sm_scale = sm_scale;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.q_len = q_len;
+  a.fp8_queries = fp8_queries ? 1 : 0;
   const size_t rows = static_cast<size_t>(Bv) * num_splits * H;
   if (num_splits > 1) {
     a.part_o = workspace;
@@ -589,6 +591,18 @@ mfa_status mfa_decode_attn_multi(const void* q, int q_dtype, int B, int q_len, i
   const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
                                      num_splits, chunk_tokens, workspace, workspace_bytes, out,
                                      out_dtype, &c, q_len);
+  if (st != MFA_OK) return st;
+  return launch_attn(c, as_stream(stream));
+}
+
+mfa_status mfa_decode_attn_q8(const void* q, int q_dtype, int B, int q_len, int H,
+                              const mfa_kv_cache* cache, const int32_t* seq_lens, int max_seq_len,
+                              float sm_scale, int num_splits, int chunk_tokens, void* workspace,
+                              size_t workspace_bytes, void* out, int out_dtype, void* stream) {
+  AttnCall c;
+  const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
+                                     num_splits, chunk_tokens, workspace, workspace_bytes, out,
+                                     out_dtype, &c, q_len, true);
   if (st != MFA_OK) return st;
   return launch_attn(c, as_stream(stream));
 }

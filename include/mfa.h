@@ -266,6 +266,27 @@ mfa_status mfa_decode_attn_multi(const void *q, int q_dtype, int B, int q_len, i
                                  void *stream);
 
 /*
+ * FP8-query decode attention (FP8 caches, H = 64, d = 256): as
+ * mfa_decode_attn_multi (q_len = 1 is single-token decode), with Q.K^T on
+ * the FP8 matrix cores. The page runs attention in FP8 ("Step-3 is Large yet
+ * Affordable" summary page, §7; §5: an 8-bit KV cache). Each (row, head)
+ * of the bf16 q is quantized inside the call with the cache's own codec:
+ *   s = max_i |q_i| / 448 (1 when 0; one correctly rounded fp32 division),
+ *   code_i = RNE e4m3(q_i / s),
+ * and the logits are (codes . K codes) * s * k_scale * sm_scale. Softmax,
+ * P.V (bf16 P, V widened to bf16), the split partials and the combine are
+ * those of mfa_decode_attn. The result therefore equals attention with q
+ * replaced by its e4m3 dequantisation, up to fp32 rounding.
+ * Errors: MFA_ERR_UNSUPPORTED unless the cache is MFA_FP8_E4M3 and H = 64,
+ * d = 256; q_dtype must be MFA_BF16; everything else as mfa_decode_attn_multi.
+ */
+mfa_status mfa_decode_attn_q8(const void *q, int q_dtype, int B, int q_len, int H,
+                              const mfa_kv_cache *cache, const int32_t *seq_lens,
+                              int max_seq_len, float sm_scale, int num_splits,
+                              int chunk_tokens, void *workspace, size_t workspace_bytes,
+                              void *out, int out_dtype, void *stream);
+
+/*
  * Split combine: merges the num_splits partials (layout as in
  * mfa_split_workspace_bytes) of every (sequence, head) by log-sum-exp:
  *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.

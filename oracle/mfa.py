@@ -291,6 +291,24 @@ def quantize_tokens(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return e4m3.encode_rne(y), s
 
 
+def quantize_queries(q: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """FP8 queries: each (token, head) row of q [..][H][d] quantised on its
+    own with the KV cache's per-token codec (``quantize_tokens``). Reading
+    taken here of the summary page's FP8 attention (§7): one scale per head
+    row, so a head's logits keep its own range. Returns (codes [..][H][d],
+    scales float32 [..][H])."""
+    q = np.asarray(q, dtype=np.float64)
+    codes, s = quantize_tokens(q.reshape(-1, q.shape[-1]))
+    return codes.reshape(q.shape), s.reshape(q.shape[:-1])
+
+
+def dequantize_queries(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """decode(code) * scale of every (token, head) row, exact in fp64."""
+    d = codes.shape[-1]
+    return dequantize_tokens(codes.reshape(-1, d), np.asarray(scales).reshape(-1)).reshape(
+        codes.shape)
+
+
 def dequantize_tokens(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """decode(code) * scale, exact in fp64."""
     return e4m3.decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]

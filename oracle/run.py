@@ -90,14 +90,19 @@ def physical_cache(inp: Dict, seqs: Sequence[int]):
 
 
 def decode_step(inp: Dict, seqs: Optional[Sequence[int]] = None,
-                sm_scale: Optional[float] = None, eps: float = DEFAULT_EPS) -> Dict:
-    """q for all sequences and the attention output for ``seqs``."""
+                sm_scale: Optional[float] = None, eps: float = DEFAULT_EPS,
+                fp8_queries: bool = False) -> Dict:
+    """q for all sequences and the attention output for ``seqs``; with
+    ``fp8_queries`` the attention uses q's per-(token, head) e4m3
+    dequantisation."""
     w = inp["workload"]
     if seqs is None:
         seqs = list(range(w.batch))
     if sm_scale is None:
         sm_scale = mfa.default_sm_scale(w.head_dim)
     q = query(inp, eps)
+    if fp8_queries:
+        q = mfa.dequantize_queries(*mfa.quantize_queries(q))
     kc, vc = physical_cache(inp, seqs)
     o = mfa.decode_attention(q, kc, vc, inp["block_table"], inp["max_blocks_per_seq"],
                              inp["seq_lens"], sm_scale, seqs=seqs)
@@ -138,16 +143,19 @@ def expected_cache_rows(inp: Dict, seqs: Sequence[int]):
 
 
 def decode_step_multi(inp: Dict, seqs: Optional[Sequence[int]] = None,
-                      sm_scale: Optional[float] = None) -> np.ndarray:
+                      sm_scale: Optional[float] = None, fp8_queries: bool = False) -> np.ndarray:
     """Multi-token decode: the queries ``q_multi`` [B][T][H][d] of the last T
     tokens of every sequence (the cache after the step's append), causal
-    among themselves. Returns o [len(seqs)][T][H][d] in fp64."""
+    among themselves (``fp8_queries``: their e4m3 dequantisation). Returns
+    o [len(seqs)][T][H][d] in fp64."""
     w = inp["workload"]
     if seqs is None:
         seqs = list(range(w.batch))
     if sm_scale is None:
         sm_scale = mfa.default_sm_scale(w.head_dim)
     q = mfa.stored_to_f64(inp["q_multi"], w.act_dtype)
+    if fp8_queries:
+        q = mfa.dequantize_queries(*mfa.quantize_queries(q))
     kc, vc = physical_cache(inp, seqs)
     return mfa.decode_attention_multi(q, kc, vc, inp["block_table"], inp["max_blocks_per_seq"],
                                       inp["seq_lens"], sm_scale, seqs=seqs)

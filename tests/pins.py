@@ -35,6 +35,10 @@ What pins what:
   torch's RNE cast on random values.
 * quantisation -- the amax element encodes to +-448; error within half an
   e4m3 step times the scale; zero rows; sign kept.
+* FP8 queries -- every (token, head) row on its own: scaling one head moves
+  only that head's scale and leaves its codes; rows already on the e4m3 grid
+  with amax 448 round-trip exactly; attention with such queries equals
+  attention with the originals; the amax element of each head codes to 448.
 * cost -- the page's intensity 128 at 8-bit KV and effective rank 16,384.
 * block layout -- hand-worked element positions of the documented storage
   order, a bijection, and the inverse undoing the forward map.
@@ -70,6 +74,8 @@ def real_oracle():
         f64_to_bf16_bits=mfa.f64_to_bf16_bits,
         quantize_tokens=mfa.quantize_tokens,
         dequantize_tokens=mfa.dequantize_tokens,
+        quantize_queries=mfa.quantize_queries,
+        dequantize_queries=mfa.dequantize_queries,
         e4m3_decode=e4m3.decode,
         e4m3_encode=e4m3.encode_rne,
         arithmetic_intensity=cost.arithmetic_intensity,
@@ -504,6 +510,49 @@ def check_quantize(O):
     return fails
 
 
+def check_fp8_queries(O):
+    fails = []
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((3, 2, 4, 64)).astype(np.float32).astype(np.float64)   # [B][T][H][d]
+    codes, s = O.quantize_queries(q)
+    if codes.shape != q.shape or s.shape != q.shape[:-1]:
+        fails.append("query codes / scales shape")
+        return fails
+    j = np.argmax(np.abs(q), axis=-1)
+    if not np.all((np.take_along_axis(codes, j[..., None], -1) & 0x7F) == 0x7E):
+        fails.append("amax element of a query head not coded as 448")
+    # error within half a step of the e4m3 grid, times the head's scale
+    deq = O.dequantize_queries(codes, s)
+    r = np.abs(deq / s[..., None].astype(np.float64))
+    step = np.where(r < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(r, 2.0 ** -6))) - 3))
+    if not np.all(np.abs(deq - q) / s[..., None] <= step / 2 * (1 + 1e-6) + 1e-30):
+        fails.append("query quantisation error beyond half a step")
+    # one head scaled by 2^5: its scale moves by 2^5, its codes and every other head stay
+    q2 = q.copy(); q2[1, 0, 2] *= 32.0
+    c2, s2 = O.quantize_queries(q2)
+    other = np.ones(s.shape, bool); other[1, 0, 2] = False
+    if not (np.array_equal(c2, codes) and np.array_equal(s2[other], s[other])
+            and s2[1, 0, 2] == np.float32(32.0) * s[1, 0, 2]):
+        fails.append("query heads are not quantised independently")
+    # rows already on the e4m3 grid with amax 448 (scale 1) round-trip exactly
+    grid_codes = rng.integers(0, 0x7E, size=(2, 4, 64)).astype(np.uint8)
+    grid_codes[..., 5] = 0x7E
+    grid_codes |= (rng.integers(0, 2, size=grid_codes.shape) * 0x80).astype(np.uint8)
+    qg = O.e4m3_decode(grid_codes)
+    c3, s3 = O.quantize_queries(qg)
+    if not (np.array_equal(s3, np.ones(s3.shape, np.float32))
+            and np.array_equal(O.dequantize_queries(c3, s3), qg)):
+        fails.append("queries on the e4m3 grid do not round-trip")
+    # attention with such queries equals attention with the originals
+    k = rng.standard_normal((40, 64)); v = rng.standard_normal((40, 64))
+    qd = O.dequantize_queries(c3, s3)
+    a1 = O.softmax_attention(qd[0], k, v, 0.01)
+    a2 = O.softmax_attention(qg[0], k, v, 0.01)
+    if not np.array_equal(a1, a2):
+        fails.append("FP8-query attention differs on exactly representable queries")
+    return fails
+
+
 def check_cost(O):
     fails = []
     with open(os.path.join(GOLDEN, "page_figures.json")) as f:
@@ -568,7 +617,8 @@ def check_layout(O):
 
 ALL_CHECKS = (check_attention, check_gather, check_combine, check_multi_token, check_qproj,
               check_kv_projection, check_output_projection, check_a2f_pack,
-              check_bf16_round, check_e4m3, check_quantize, check_cost, check_layout)
+              check_bf16_round, check_e4m3, check_quantize, check_fp8_queries, check_cost,
+              check_layout)
 
 
 def run_all(O):

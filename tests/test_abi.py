@@ -88,6 +88,20 @@ def test_decode_attn_validation(lib):
         assert _attn(lib, c, scale=bad) == SHAPE                 # scale must be positive, finite
 
 
+def test_decode_attn_q8_validation(lib):
+    def q8(cache, **kw):
+        return lib.mfa_decode_attn_q8(kw.get("q", P), kw.get("qdt", BF16), 4, kw.get("ql", 1), 64,
+                                      ctypes.byref(cache), P, 512, 0.0625, 1, 512, None, 0, P,
+                                      BF16, None)
+    fp8 = _cache(dtype=FP8, k_scale=P, v_scale=P)
+    assert q8(_cache()) == UNSUP                                   # bf16 cache
+    assert q8(fp8, qdt=F32) == DTYPE
+    assert q8(fp8, ql=0) == SHAPE
+    assert q8(fp8, ql=17) == SHAPE
+    assert q8(fp8, q=None) == NULL
+    assert q8(fp8, q=PM) == ALIGN
+
+
 def test_kv_append_validation(lib):
     c = _cache()
     ap = lambda **kw: lib.mfa_kv_append(kw.get("k", P), kw.get("v", P), kw.get("dt", BF16),

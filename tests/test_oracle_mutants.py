@@ -177,6 +177,26 @@ def _payload_with_scales(tokens, hidden, elem_bytes, scale_bytes=0):
     return tokens * (hidden * elem_bytes + 4)
 
 
+def _qq_one_scale_per_token(q):
+    q = np.asarray(q, float)
+    flat = q.reshape(-1, q.shape[-2] * q.shape[-1])          # all heads of a token together
+    c, sc = mfa.quantize_tokens(flat)
+    return c.reshape(q.shape), np.repeat(sc, q.shape[-2]).reshape(q.shape[:-1])
+
+
+def _qq_truncates(q):
+    q = np.asarray(q, float)
+    d = q.shape[-1]
+    rows = q.reshape(-1, d).astype(np.float32)
+    amax = np.max(np.abs(rows), axis=1)
+    sc = np.where(amax == 0, 1.0, amax / 448.0).astype(np.float32)
+    y = rows / sc[:, None]
+    vals = e4m3.DECODE_TABLE[:0x7F]
+    idx = np.searchsorted(vals, np.abs(y), side="right") - 1     # round toward zero
+    c = idx.astype(np.uint8) | np.where(np.signbit(y), 0x80, 0).astype(np.uint8)
+    return c.reshape(q.shape), sc.reshape(q.shape[:-1])
+
+
 def _kv_rows_offset(x, w, d):
     # the weight rows read one row off (W_k / W_v halves misaligned)
     kv = np.asarray(x, float) @ np.roll(np.asarray(w, float), 1, axis=0).T
@@ -207,6 +227,8 @@ MUTANTS = {
     "a2f_pack_e4m3_max_240": dict(a2f_pack=_a2f_e4m3_max_240),
     "a2f_pack_no_scale": dict(a2f_pack=_a2f_no_scale),
     "a2f_payload_counts_scales": dict(hidden_payload_bytes=_payload_with_scales),
+    "fp8_queries_one_scale_per_token": dict(quantize_queries=_qq_one_scale_per_token),
+    "fp8_queries_truncate": dict(quantize_queries=_qq_truncates),
     "bf16_round_truncates": dict(f64_to_bf16_bits=_bf16_truncate),
     "bf16_round_ties_away": dict(f64_to_bf16_bits=_bf16_ties_away),
     "attention_missing_scale": dict(softmax_attention=_attn_no_scale),

@@ -471,6 +471,62 @@ def test_multi_token_one_is_single_token(gpu_lib):
         assert torch.equal(a.view(torch.int16), b.squeeze(1).view(torch.int16))
 
 
+# ---------------------------------------------------------------- FP8 queries
+# FP8 caches; 5 and 3 sequences run one workgroup per split, 8 sequences (and
+# 4 x q_len 2) the two-head-group launch; q_len 1, 2 and 4; 1 and 3 splits.
+Q8_CASES = [
+    ("paged", dict(), [0, 63, 64, 190, 513], 1),
+    ("contig", dict(paged=False), [255, 70, 3], 1),
+    ("paged-8", dict(), [0, 1, 63, 64, 65, 190, 513, 1000], 1),
+    ("paged-T2", dict(), [2, 64, 129, 513], 2),
+    ("contig-T4", dict(paged=False), [3, 64, 300], 4),
+]
+
+
+def run_q8(inp, T, splits, cache, T_):
+    import decode_attention_02_amd as mfa
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    chunk = -(-(-(-maxlen // splits)) // 64) * 64 if splits > 1 else None
+    q = T_["q_multi"] if T > 1 else T_["q"].unsqueeze(1)
+    return mfa.decode_attn_multi(q, cache, T_["seq_lens"], maxlen, num_splits=splits,
+                                 chunk_tokens=chunk, fp8_queries=True)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("name,over,lens,T", Q8_CASES, ids=[c[0] for c in Q8_CASES])
+def test_fp8_queries(gpu_lib, name, over, lens, T, splits):
+    """mfa_decode_attn_q8 against the oracle with the same per-(row, head)
+    e4m3 queries; the output is also closer to that reading than to
+    attention with the unquantised queries (the quantisation really runs)."""
+    w = small(4, batch=len(lens), **over)
+    inp = workloads.make_inputs(4, workload=w, seed=61, prefill_lens=lens, q_len=T)
+    say(f"fp8 queries {name} T={T} splits={splits}")
+    T_, cache, step = setup(inp)
+    out = run_q8(inp, T, splits, cache, T_)
+    torch.cuda.synchronize()
+    got = to_np(out) if T > 1 else to_np(out)[:, 0]
+    if T > 1:
+        want, plain = (orun.decode_step_multi(inp, fp8_queries=True),
+                       orun.decode_step_multi(inp))
+    else:
+        want, plain = (orun.decode_step(inp, fp8_queries=True)["o"], orun.decode_step(inp)["o"])
+    check_bf16(got, want, f"fp8 queries {name}")
+    rq, rp = rel_l2(got, want), rel_l2(got, plain)
+    say(f"fp8 queries {name}: rel_l2 vs e4m3-q oracle {rq:.3e}, vs bf16-q oracle {rp:.3e}")
+    assert rq < rp
+
+
+def test_fp8_queries_rejects_bf16_cache(gpu_lib):
+    import decode_attention_02_amd as mfa
+    from decode_attention_02_amd._lib import MfaError
+    w = small(3, batch=2)
+    inp = workloads.make_inputs(3, workload=w, seed=62, prefill_lens=[10, 70])
+    T_, cache, step = setup(inp)
+    with pytest.raises(MfaError, match="UNSUPPORTED"):
+        mfa.decode_attn_multi(T_["q"].unsqueeze(1), cache, T_["seq_lens"], 71, fp8_queries=True)
+
+
 # ---------------------------------------------------------------- output projection
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
@@ -622,6 +678,23 @@ def test_full_fp8_32k_sampled(gpu_lib):
         assert np.array_equal(kg[rows], exp["k"][rows])
         assert np.array_equal(vg[rows], exp["v"][rows])
         assert np.array_equal(ks[rows].view(np.uint32), exp["k_scale"][rows].view(np.uint32))
+
+
+def test_full_fp8_32k_fp8_queries_sampled(gpu_lib):
+    """FP8 queries at full size (16 sequences of 32K, the library's split
+    plan), sampled sequences against the oracle."""
+    import decode_attention_02_amd as mfa
+    inp = workloads.make_inputs(4)
+    say("full fp8 32k, fp8 queries")
+    T, cache, step = setup(inp)
+    mfa.kv_append(cache, T["k_new"], T["v_new"], T["prefill_lens"])
+    out = mfa.decode_attn_multi(T["q"].unsqueeze(1), cache, T["seq_lens"], step.max_seq_len,
+                                num_splits=step.num_splits, chunk_tokens=step.chunk_tokens,
+                                fp8_queries=True)
+    torch.cuda.synchronize()
+    seqs = [0, 7, 15]
+    want = orun.decode_step(inp, seqs=seqs, fp8_queries=True)
+    check_bf16(to_np(out)[seqs, 0], want["o"], "fp8 32k fp8-queries sampled")
 
 
 def test_full_split32_64k(gpu_lib):

@@ -301,81 +301,76 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
 // the attention-to-FFN hand-off ("Step-3 is Large yet Affordable" summary
 // page, §7: FP8 tokens with their scales go from attention to FFN):
 // amax over the row, scale = amax / 448 (1 when amax = 0), code = RNE e4m3
-// of the correctly rounded quotient. One workgroup per row; a thread owns 8
-// consecutive columns per 2048.
-__global__ __launch_bounds__(256) void outproj_pack_kernel(const float* __restrict__ part,
-                                                           int ksplit, int M, int N,
-                                                           uint16_t* __restrict__ y,
-                                                           uint8_t* __restrict__ codes,
-                                                           float* __restrict__ scales) {
-  constexpr int kMaxChunks = 4;        // N <= 8192
-  __shared__ float wmax[4];
+// of the correctly rounded quotient. One 1024-thread workgroup per row, 8
+// consecutive columns per thread, so every load of the row is issued at once.
+constexpr int kPackThreads = 1024;
+__global__ __launch_bounds__(kPackThreads) void outproj_pack_kernel(const float* __restrict__ part,
+                                                                    int ksplit, int M, int N,
+                                                                    uint16_t* __restrict__ y,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    float* __restrict__ scales) {
+  __shared__ float wmax[kPackThreads / 64];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
-  float yv[kMaxChunks][8];
+  const int j0 = tid * 8;
+  float yv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) yv[j] = 0.f;
   float amax = 0.f;
+  if (j0 < N) {
+    for (int k0 = 0; k0 < ksplit; k0 += 8) {         // slices in slice order, 8 in flight
+      float4 a[8], b[8];
 #pragma unroll
-  for (int ch = 0; ch < kMaxChunks; ++ch) {
-    const int j0 = ch * 2048 + tid * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) yv[ch][j] = 0.f;
-    if (j0 < N) {
-      for (int k0 = 0; k0 < ksplit; k0 += 8) {       // slices in slice order, 8 in flight
-        float4 a[8], b[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (k0 + u < ksplit) {
-            const float* p = part + (static_cast<size_t>(k0 + u) * M + m) * N + j0;
-            a[u] = *reinterpret_cast<const float4*>(p);
-            b[u] = *reinterpret_cast<const float4*>(p + 4);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (k0 + u < ksplit) {
-            yv[ch][0] += a[u].x; yv[ch][1] += a[u].y; yv[ch][2] += a[u].z; yv[ch][3] += a[u].w;
-            yv[ch][4] += b[u].x; yv[ch][5] += b[u].y; yv[ch][6] += b[u].z; yv[ch][7] += b[u].w;
-          }
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < ksplit) {
+          const float* p = part + (static_cast<size_t>(k0 + u) * M + m) * N + j0;
+          a[u] = *reinterpret_cast<const float4*>(p);
+          b[u] = *reinterpret_cast<const float4*>(p + 4);
         }
       }
-      uint32_t bits[4];
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        bits[j / 2] = pack_bf16x2(yv[ch][j], yv[ch][j + 1]);
-        yv[ch][j] = __uint_as_float(bits[j / 2] << 16);               // the bf16 values
-        yv[ch][j + 1] = __uint_as_float(bits[j / 2] & 0xffff0000u);
-        amax = fmaxf(amax, fmaxf(fabsf(yv[ch][j]), fabsf(yv[ch][j + 1])));
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < ksplit) {
+          yv[0] += a[u].x; yv[1] += a[u].y; yv[2] += a[u].z; yv[3] += a[u].w;
+          yv[4] += b[u].x; yv[5] += b[u].y; yv[6] += b[u].z; yv[7] += b[u].w;
+        }
       }
-      if (y) store_nt(y + static_cast<size_t>(m) * N + j0, make_uint4(bits[0], bits[1], bits[2], bits[3]));
     }
+    uint32_t bits[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      bits[j / 2] = pack_bf16x2(yv[j], yv[j + 1]);
+      yv[j] = __uint_as_float(bits[j / 2] << 16);                     // the bf16 values
+      yv[j + 1] = __uint_as_float(bits[j / 2] & 0xffff0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(yv[j]), fabsf(yv[j + 1])));
+    }
+    if (y) store_nt(y + static_cast<size_t>(m) * N + j0, make_uint4(bits[0], bits[1], bits[2], bits[3]));
   }
   if (!codes) return;                  // uniform: no pack asked for
   amax = wave_max(amax);
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kPackThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
   const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (j0 < N) {
+    uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-  for (int ch = 0; ch < kMaxChunks; ++ch) {
-    const int j0 = ch * 2048 + tid * 8;
-    if (j0 < N) {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w0 |= encode_e4m3_rne(yv[ch][j] / sc) << (8 * j);
-        w1 |= encode_e4m3_rne(yv[ch][4 + j] / sc) << (8 * j);
-      }
-      store_nt(codes + static_cast<size_t>(m) * N + j0, make_uint2(w0, w1));
+    for (int j = 0; j < 4; ++j) {
+      w0 |= encode_e4m3_rne(yv[j] / sc) << (8 * j);
+      w1 |= encode_e4m3_rne(yv[4 + j] / sc) << (8 * j);
     }
+    store_nt(codes + static_cast<size_t>(m) * N + j0, make_uint2(w0, w1));
   }
   if (tid == 0) scales[m] = sc;
 }
 
 hipError_t launch_outproj_pack(const float* part, int ksplit, int M, int N, uint16_t* y,
                                uint8_t* codes, float* scales, hipStream_t stream) {
-  if (N % 8 || N > 8192 || M < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(outproj_pack_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream,
-                     part, ksplit, M, N, y, codes, scales);
+  if (N % 8 || N > 8 * kPackThreads || M < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(outproj_pack_kernel, dim3(static_cast<unsigned>(M)), dim3(kPackThreads), 0,
+                     stream, part, ksplit, M, N, y, codes, scales);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
             f"libmfa.so not found at {path}: build it first "
-            "(python -m decode_attention_02_amd.build or __graft_entry__.build())")
+            "(python -m decode_attention_02_amd.build)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

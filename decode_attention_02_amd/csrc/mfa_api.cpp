@@ -316,7 +316,7 @@ mfa_status launch_qproj(const QprojCall& c, const mfa::AppendArgs* append, hipSt
       e = mfa::launch_gemm_bf16(reinterpret_cast<const uint16_t*>(xa),
                                 static_cast<const uint16_t*>(c.w_qdown), pd, nullptr, M, N,
                                 c.hidden, dp.ks, dp.ntiles, c.packed, false, st,
-                                static_cast<const uint16_t*>(c.w_kv), c.q_rank);
+                                static_cast<const uint16_t*>(c.w_kv), c.q_rank, true);
       if (e != hipSuccess) return MFA_ERR_HIP;
       if (proj) {
         ap.kv_part = pd;
@@ -436,21 +436,13 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, i
                            int* chunk_tokens) {
   if (!num_splits || !chunk_tokens) return MFA_ERR_NULL;
   if (B < 1 || H < 1 || d < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
+  (void)kv_dtype;
   const int blocks = (max_seq_len + kBlock - 1) / kBlock;
   // One 8-wave attention workgroup per compute unit of an MI355X (256 CUs):
   // split each sequence so that the grid covers the chip once, with splits
   // of whole 128-token tiles (two cache blocks).
   constexpr int kTargetWorkgroups = 256;
-  int target = kTargetWorkgroups;
-  // bf16 caches at up to 64 sequences: half as many (sequence, split) pairs,
-  // which the launch then runs as two head groups each (the second group's
-  // block reads hit L2), so every workgroup walks twice as many blocks and
-  // the combine merges half as many partials (measured at 32 x 4K: 28.8 us
-  // against 29.5 us for the attention, 60.8 against 62.4 us for the step).
-  // Not for FP8, whose per-block conversions would then run twice (16 x 32K:
-  // 63.4 against 56.7 us).
-  if (kv_dtype == MFA_BF16 && H == 64 && d == 256 && B <= 64) target = kTargetWorkgroups / 2;
-  int splits = target / B;
+  int splits = kTargetWorkgroups / B;
   if (splits < 1) splits = 1;
   if (splits > blocks / 2) splits = blocks / 2 > 0 ? blocks / 2 : 1;
   int per = blocks > 0 ? (blocks + splits - 1) / splits : 2;

@@ -91,7 +91,10 @@ __device__ __forceinline__ void gemm_store_rows(const float (*red)[TM * kPad], i
 }
 
 // NTW marks the weight loads non-temporal: a weight that is read once per
-// call streams through L2 without pushing out the activations and partials.
+// call streams through L2 without pushing out the activations and partials
+// (measured: the down-projection's 29 MB this way saves 2.5 us per decode
+// step, the up-projection's 67 MB costs 1 us, the output projection's 235 MB
+// saves 3-5 %).
 // Columns N1 .. N-1 may come from a second weight matrix W2 (rows 0 ..
 // N-N1-1 of it; null W2: all from W), so two products that share A run as
 // one launch (the down-projection and the K/V projection share x).

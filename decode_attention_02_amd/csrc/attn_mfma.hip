@@ -260,8 +260,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   };
   auto tokens_in = [&](int n) __attribute__((always_inline)) { return t1 - (blk0 + n) * kBlockTokens; };   // valid tokens of block n (>= 1)
 
+  // bf16 results (outputs, or the partials of a split that holds tokens)
+  // leave through LDS as whole 512-byte head rows (end of the kernel)
+  const bool stage_out = a.num_splits == 1 ? !a.out_f32 : (a.part_bf16 && N > 0);
+
   // Every wave passes the same barriers: one after staging Q, one per
-  // iteration i = 0 .. N+1, one before the epilogue.
+  // iteration i = 0 .. N+1, one before the epilogue (and one more before the
+  // staged stores).
   if (w < 4) {
     // ================= QK waves: S = K.Q^T -> LDS, per-wave block max
     constexpr int R = RK;
@@ -603,55 +608,59 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       lsum[ht] = (r4.x + r4.y) + (r4.z + r4.w);
       mh[ht] = m_run[ht];
     }
-    if (a.num_splits == 1) {
+    // O^T lane (g, c) of tile (dt, ht): head 16ht + c, features 64ww + 16dt +
+    // 4g .. +3. bf16 results go to LDS (the logits buffer, free now) as head
+    // rows of 32 16-byte chunks, chunk j of row hl at j ^ (hl & 31) (the 16
+    // heads of a store land in 16 different bank groups); fp32 results are
+    // stored directly and merge in L2.
+    uint2* stage2 = reinterpret_cast<uint2*>(&s_lds[0][0]);
+    const bool has_o = a.num_splits == 1 || N > 0;   // an empty split writes only (m, l)
+    const size_t row = static_cast<size_t>(b) * a.num_splits + split;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const float inv = lsum[ht] > 0.f ? 1.0f / lsum[ht] : 0.f;
-        const int head = h0 + ht * 16 + c;
+    for (int ht = 0; ht < HT; ++ht) {
+      const float inv = a.num_splits == 1 ? (lsum[ht] > 0.f ? 1.0f / lsum[ht] : 0.f) : 1.0f;
+      const int hl = ht * 16 + c, head = h0 + hl;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < 4; ++dt) {
+        if (!has_o) break;
+        const f32x4_t v = acc[dt][ht] * inv;
+        if (stage_out) {
+          const int j = 8 * ww + 2 * dt + (g >> 1);
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          stage2[(hl * 32 + (j ^ (hl & 31))) * 2 + (g & 1)] = pk;
+        } else {
           const int f = 64 * ww + 16 * dt + 4 * g;
-          const size_t o = (static_cast<size_t>(b) * kH + head) * kD + f;
-          const f32x4_t v = acc[dt][ht] * inv;
-          if (a.out_f32) {
-            store_nt(reinterpret_cast<float*>(a.out) + o, make_float4(v[0], v[1], v[2], v[3]));
-          } else {
-            uint2 pk;
-            pk.x = pack_bf16x2(v[0], v[1]);
-            pk.y = pack_bf16x2(v[2], v[3]);
-            store_nt(reinterpret_cast<uint16_t*>(a.out) + o, pk);
-          }
+          float* dst = a.num_splits == 1
+                           ? reinterpret_cast<float*>(a.out) + (static_cast<size_t>(b) * kH + head) * kD + f
+                           : static_cast<float*>(a.part_o) + (row * kH + head) * kD + f;
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
-    } else {
-      // an empty split writes only (m, l) = (-inf, 0): the combine gives it
-      // no weight and never uses its o
-      const size_t row = static_cast<size_t>(b) * a.num_splits + split;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const int head = h0 + ht * 16 + c;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          if (N == 0) break;
-          const int f = 64 * ww + 16 * dt + 4 * g;
-          const f32x4_t v = acc[dt][ht];
-          const size_t po = (row * kH + head) * kD + f;
-          if (a.part_bf16) {
-            uint2 pk;
-            pk.x = pack_bf16x2(v[0], v[1]);
-            pk.y = pack_bf16x2(v[2], v[3]);
-            store_nt(static_cast<uint16_t*>(a.part_o) + po, pk);
-          } else {
-            store_nt(static_cast<float*>(a.part_o) + po, make_float4(v[0], v[1], v[2], v[3]));
-          }
-        }
-        if (ww == 0 && g == 0) {
-          float2 ml;
-          ml.x = mh[ht] * kLn2;     // natural-log units of the scaled logits
-          ml.y = lsum[ht];
-          store_nt(a.part_ml + (row * kH + head) * 2, ml);
-        }
+      // (m, l) of every split, empty ones as (-inf, 0): the combine gives
+      // those no weight and never uses their o
+      if (a.num_splits > 1 && ww == 0 && g == 0) {
+        float2 ml;
+        ml.x = mh[ht] * kLn2;     // natural-log units of the scaled logits
+        ml.y = lsum[ht];
+        store_nt(a.part_ml + (row * kH + head) * 2, ml);
       }
+    }
+  }
+  if (stage_out) {
+    __syncthreads();   // head rows staged by the PV waves
+    // the workgroup's kHW head rows are one contiguous range of the output
+    // (or of this split's partials): 16 bytes per thread per pass
+    uint16_t* dst = a.num_splits == 1
+                        ? static_cast<uint16_t*>(a.out) + (static_cast<size_t>(b) * kH + h0) * kD
+                        : static_cast<uint16_t*>(a.part_o) +
+                              ((static_cast<size_t>(b) * a.num_splits + split) * kH + h0) * kD;
+    const uint4* stage4 = reinterpret_cast<const uint4*>(&s_lds[0][0]);
+#pragma unroll
+    for (int i = tid; i < kHW * 32; i += 512) {
+      const int hl = i >> 5, j = i & 31;
+      store_nt(dst + static_cast<size_t>(i) * 8, stage4[hl * 32 + (j ^ (hl & 31))]);
     }
   }
 }

@@ -252,6 +252,19 @@ def test_qproj_packed_matches_oracle(gpu_lib, B):
     check_bf16(to_np(q_rm), orun.query(inp), f"qproj row-major B={B}")
 
 
+def test_qproj_max_batch(gpu_lib):
+    """The largest batch the query path takes (256 rows: four passes of 64),
+    Step-3's query shape on a smaller hidden width."""
+    import decode_attention_02_amd as mfa
+    w = dataclasses.replace(W[2], batch=256, hidden=1024, context=65)
+    inp = workloads.make_inputs(2, workload=w, seed=23)
+    T = workloads.to_torch(inp)
+    say("qproj B=256")
+    q = mfa.qproj(T["x"], T["w_qdown"], T["g"], T["w_qup"], 64, 256)
+    torch.cuda.synchronize()
+    check_bf16(to_np(q), orun.query(inp), "qproj B=256")
+
+
 def test_qproj_split_k_and_reuse(gpu_lib):
     """A query shape whose up-projection is split over K (partials summed by
     the reduction kernel) and whose down-projection is not; repeated calls on
@@ -453,6 +466,30 @@ def test_multi_token_decode(gpu_lib, name, base, over, lens, T, splits):
         check_bf16(got, want, f"multi-token {name} T={T}")
 
 
+def test_multi_token_max_query_tokens(gpu_lib):
+    """q_len = 16, the most the library takes, with sequences shorter than
+    q_len (their first queries see nothing), 2 splits."""
+    import decode_attention_02_amd as mfa
+    lens = [0, 5, 15, 16, 200]
+    w = small(3, batch=len(lens))
+    inp = workloads.make_inputs(3, workload=w, seed=43, prefill_lens=lens, q_len=16)
+    say("multi-token q_len=16")
+    T_, cache, step = setup(inp)
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    out = mfa.decode_attn_multi(T_["q_multi"], cache, T_["seq_lens"], maxlen, num_splits=2,
+                                chunk_tokens=-(-(-(-maxlen // 2)) // 64) * 64)
+    torch.cuda.synchronize()
+    want = orun.decode_step_multi(inp)
+    got = to_np(out)
+    # query token j of sequence b sees L_b - (15 - j) tokens; none: zeros
+    for b, L in enumerate(inp["seq_lens"]):
+        for j in range(16):
+            if L - (15 - j) <= 0:
+                assert not np.any(got[b, j]), (b, j)
+    check_bf16(got, want, "multi-token q_len=16")
+
+
 def test_multi_token_one_is_single_token(gpu_lib):
     """q_len = 1 through mfa_decode_attn_multi is bit-identical to mfa_decode_attn."""
     import decode_attention_02_amd as mfa
@@ -561,6 +598,7 @@ def check_a2f(y, codes, scales, want, what):
 OUTPROJ = [
     # (B, heads*head_dim via heads, hidden, packed)
     (1, 4, 512, False),
+    (256, 4, 8192, True),           # the limits: two passes of 128 rows, hidden 8192
     (5, 64, 7168, False),
     (64, 4, 1024, True),
     (70, 64, 2048, False),

@@ -118,6 +118,13 @@ hipError_t launch_rmsnorm_reduce(const float* part, int ksplit, const float* g, 
 // 0), codes = RNE e4m3(y / scale). N % 8 == 0, N <= 8192.
 hipError_t launch_outproj_pack(const float* part, int ksplit, int M, int N, uint16_t* y,
                                uint8_t* codes, float* scales, hipStream_t stream);
+// 65 .. 128 rows, packed weights, row-major A: fp32 partials part[ks][M][N]
+// from the row-split kernel (waves own 16-row slices, the weight tile is
+// shared through LDS). N % 128 == 0, (K / ksplit) % 128 == 0.
+hipError_t launch_gemm_rows_bf16(const uint16_t* A, const uint16_t* Wp, float* part, int M, int N,
+                                 int K, int ksplit, bool stream_w, hipStream_t stream);
+// its K split for N columns (fills the 256 compute units once)
+int gemm_rows_splits(int N, int K);
 // out[m][n] = sum over ksplit partials, cast to bf16 or kept f32.
 hipError_t launch_reduce_cast(const float* part, int ksplit, int M, int N, void* out,
                               int out_f32, hipStream_t stream);

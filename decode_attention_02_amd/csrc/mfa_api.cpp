@@ -167,14 +167,17 @@ size_t mfa_qproj_workspace_bytes(int B, int hidden, int q_rank, int H, int d, in
 namespace {
 struct OutProjPlan {
   int rows;
-  GemmPlan g;
+  GemmPlan g;          // K-split kernel (passes of up to 64 rows, row-major weights)
+  int rows_ks;         // row-split kernel's K slices for passes of 65 .. 128 rows (0: not used)
   size_t total;
 };
 OutProjPlan plan_out_proj(int B, int HD, int hidden) {
   OutProjPlan p{};
   p.rows = B < kOutProjRows ? B : kOutProjRows;
   p.g = plan_gemm(hidden, HD, p.rows);
-  p.total = round_up(static_cast<size_t>(p.g.ks) * p.rows * hidden * 4, 256);
+  p.rows_ks = (B > 64 && hidden % 128 == 0) ? mfa::gemm_rows_splits(hidden, HD) : 0;
+  const int ks = p.g.ks > p.rows_ks ? p.g.ks : p.rows_ks;
+  p.total = round_up(static_cast<size_t>(ks) * p.rows * hidden * 4, 256);
   return p;
 }
 mfa_status check_out_proj_shape(int B, int HD, int hidden, int dtype) {
@@ -210,13 +213,19 @@ mfa_status mfa_out_proj(const void* o, const void* w_o, int weight_layout, int B
   for (int r0 = 0; r0 < B; r0 += p.rows) {
     const int M = (B - r0) < p.rows ? (B - r0) : p.rows;
     const uint16_t* oa = static_cast<const uint16_t*>(o) + static_cast<size_t>(r0) * HD;
-    hipError_t e = mfa::launch_gemm_bf16(oa, static_cast<const uint16_t*>(w_o), part, nullptr, M,
-                                         hidden, HD, p.g.ks, p.g.ntiles,
-                                         weight_layout == MFA_WEIGHTS_PACKED, false, st, nullptr,
-                                         0, true);
+    // 65 .. 128 rows with packed weights: the row-split kernel
+    const bool rows = M > 64 && p.rows_ks > 0 && weight_layout == MFA_WEIGHTS_PACKED;
+    const int ks = rows ? p.rows_ks : p.g.ks;
+    hipError_t e =
+        rows ? mfa::launch_gemm_rows_bf16(oa, static_cast<const uint16_t*>(w_o), part, M, hidden,
+                                          HD, ks, true, st)
+             : mfa::launch_gemm_bf16(oa, static_cast<const uint16_t*>(w_o), part, nullptr, M,
+                                     hidden, HD, ks, p.g.ntiles,
+                                     weight_layout == MFA_WEIGHTS_PACKED, false, st, nullptr, 0,
+                                     true);
     if (e != hipSuccess) return MFA_ERR_HIP;
     e = mfa::launch_outproj_pack(
-        part, p.g.ks, M, hidden, y ? static_cast<uint16_t*>(y) + static_cast<size_t>(r0) * hidden : nullptr,
+        part, ks, M, hidden, y ? static_cast<uint16_t*>(y) + static_cast<size_t>(r0) * hidden : nullptr,
         codes ? static_cast<uint8_t*>(codes) + static_cast<size_t>(r0) * hidden : nullptr,
         scales ? scales + r0 : nullptr, st);
     if (e != hipSuccess) return MFA_ERR_HIP;

@@ -13,6 +13,8 @@
 // splits K across workgroups when the output alone cannot fill the chip,
 // and leaves fp32 partials that the RMSNorm pass sums (down product) or
 // writes bf16 directly (up product, one K slice).
+#include <type_traits>
+
 #include "append_one.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -464,6 +466,159 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, u
     else launch_gemm_variant<false, false, false>(c, ksplit, ntiles, stream);
   }
   return hipGetLastError();
+}
+
+// Skinny bf16 product for 65 .. 128 rows (packed weights, row-major A):
+// part[ks][m][n] = sum over K slice ks of A[m][k] * W[n][k].
+//
+// The K-split kernel above keeps every wave's full 128 x 64 fp32 tile in
+// registers (half the register file at 128 rows), which leaves room for only
+// two k-steps of weights in flight per wave. Here the waves split the rows
+// instead: wave w owns rows 16w .. 16w+15 over the whole K slice, so its
+// accumulators are the NT 16x16 tiles of its own rows (32 registers at
+// NT = 8). The weight tile goes through LDS: chunks of CH k-steps (NT*CH KB)
+// are loaded by all 512 threads, P chunks in flight in registers, staged into
+// one of two LDS buffers and read by every wave; one barrier per chunk. The
+// 128-column tile halves the activation reads of a 64-column one (every
+// workgroup reads all of its rows of A through L2).
+template <int NT, int CH, int P>
+struct RowsCfg {
+  static constexpr int kUnits = NT * CH;               // 1 KB weight units per chunk
+  static constexpr int kPer = kUnits * 64 / 512;       // 16-byte pieces per thread per chunk
+  static_assert(kPer * 512 == kUnits * 64, "a chunk splits evenly over 512 threads");
+};
+
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void rows_static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    rows_static_for<I0 + 1, I1>(f);
+  }
+}
+
+template <int NT, int CH, int P, bool NTW>
+__global__ __launch_bounds__(512) void gemm_rows_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ W,
+                                                        float* __restrict__ part, int M, int N,
+                                                        int K, int kchunk) {
+  using C = RowsCfg<NT, CH, P>;
+  __shared__ __attribute__((aligned(16))) uint4 wl[2][C::kUnits * 64];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int n0 = blockIdx.x * NT * 16;
+  const int ks = blockIdx.y;
+  const int kbeg = ks * kchunk;
+  const int nchunks = kchunk / (32 * CH);
+  // the tile's NT row groups, this K slice: unit (nt, kt) at nt*(K/32) + kt
+  // from the first; the resource ends after the last unit the tile reads
+  const uint16_t* wbase = W + (static_cast<size_t>(n0 / 16) * (K / 32) + kbeg / 32) * 512;
+  const int wbytes = ((NT - 1) * (K / 32) + nchunks * CH) * 1024;
+  const auto wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wbase), 0, wbytes,
+                                                    0x00020000);
+  // piece q = tid + 512 i of a chunk: unit u = q / 64 = (nt = u / CH, kt = u % CH), lane q % 64
+  int voff[C::kPer];
+#pragma unroll
+  for (int i = 0; i < C::kPer; ++i) {
+    const int q = tid + 512 * i, u = q >> 6;
+    voff[i] = (((u / CH) * (K / 32) + u % CH) * 64 + (q & 63)) * 16;
+  }
+  const int m = min(16 * w + c, M - 1);            // rows >= M feed only rows >= M of C
+  const uint16_t* arow = A + static_cast<size_t>(m) * K + kbeg + g * 8;
+  uint4 wreg[P][C::kPer];
+  uint4 areg[2][CH];
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto issue_w = [&](auto slot_c, int ch) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int co = ch < nchunks ? ch * CH * 1024 : 0;   // past the end: chunk 0 again, unused
+#pragma unroll
+    for (int i = 0; i < C::kPer; ++i)
+      wreg[slot][i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff[i] + co, 0, NTW ? 2 : 0));
+  };
+  auto issue_a = [&](auto buf_c, int ch) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int cc = ch < nchunks ? ch : 0;
+#pragma unroll
+    for (int kt = 0; kt < CH; ++kt)
+      areg[buf][kt] = *reinterpret_cast<const uint4*>(arow + (cc * CH + kt) * 32);
+  };
+  auto stage = [&](auto slot_c, auto buf_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value, buf = decltype(buf_c)::value;
+#pragma unroll
+    for (int i = 0; i < C::kPer; ++i) wl[buf][tid + 512 * i] = wreg[slot][i];
+  };
+  auto compute = [&](auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+#pragma unroll
+    for (int kt = 0; kt < CH; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = mfma_16x16x32(as_bf16x8(areg[buf][kt]), as_bf16x8(wl[buf][(nt * CH + kt) * 64 + lane]),
+                                acc[nt]);
+  };
+  // prologue: chunks 0 .. P-1 in flight, A of chunk 0, chunk 0 staged
+  rows_static_for<0, P>([&](auto sc) { issue_w(sc, decltype(sc)::value); });
+  issue_a(std::integral_constant<int, 0>{}, 0);
+  stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+  __syncthreads();
+  // chunk ch: refill its register slot with chunk ch+P, load A of ch+1,
+  // multiply from LDS buffer ch%2, stage chunk ch+1 into the other buffer
+  // (read last in chunk ch-1, before the previous barrier), barrier. Groups
+  // of U keep slots and buffers static.
+  constexpr int U = (P % 2) ? 2 * P : P;
+  for (int base = 0; base < nchunks; base += U) {
+    rows_static_for<0, U>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const int ch = base + r;
+      if (ch < nchunks) {
+        issue_w(std::integral_constant<int, r % P>{}, ch + P);
+        issue_a(std::integral_constant<int, (r + 1) & 1>{}, ch + 1);
+        compute(std::integral_constant<int, r & 1>{});
+        if (ch + 1 < nchunks)
+          stage(std::integral_constant<int, (r + 1) % P>{}, std::integral_constant<int, (r + 1) & 1>{});
+        __syncthreads();
+      }
+    });
+  }
+  // lane (g, c) of tile nt: rows 16w + 4g + i, column n0 + 16nt + c
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mm = 16 * w + 4 * g + i;
+      if (mm < M) part[(static_cast<size_t>(ks) * M + mm) * N + n0 + 16 * nt + c] = acc[nt][i];
+    }
+}
+
+// 128-column tiles, 4 k-steps per chunk, 3 chunks in flight (measured at
+// 128 x 7168 x 16384 with 4 K slices: 56 us against 87 us for the K-split
+// kernel with 128-row tiles).
+constexpr int kRowsNT = 8, kRowsCH = 4, kRowsP = 3;
+
+hipError_t launch_gemm_rows_bf16(const uint16_t* A, const uint16_t* Wp, float* part, int M, int N,
+                                 int K, int ksplit, bool stream_w, hipStream_t stream) {
+  if (M <= 64 || M > 128 || N % (16 * kRowsNT) || ksplit < 1 || K % ksplit ||
+      (K / ksplit) % (32 * kRowsCH))
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(N / (16 * kRowsNT)), static_cast<unsigned>(ksplit));
+  if (stream_w)
+    hipLaunchKernelGGL((gemm_rows_kernel<kRowsNT, kRowsCH, kRowsP, true>), grid, dim3(512), 0,
+                       stream, A, Wp, part, M, N, K, K / ksplit);
+  else
+    hipLaunchKernelGGL((gemm_rows_kernel<kRowsNT, kRowsCH, kRowsP, false>), grid, dim3(512), 0,
+                       stream, A, Wp, part, M, N, K, K / ksplit);
+  return hipGetLastError();
+}
+
+int gemm_rows_splits(int N, int K) {
+  // fill the 256 compute units once with N/128 column tiles
+  const int tiles = N / (16 * kRowsNT);
+  int ks = 1;
+  while (tiles * ks * 2 <= 256 && K % (ks * 2) == 0 && (K / (ks * 2)) % (32 * kRowsCH) == 0) ks *= 2;
+  return ks;
 }
 
 // Pack a row-major bf16 weight [N][K] into operand order (see above); one

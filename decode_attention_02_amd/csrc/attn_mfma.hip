@@ -298,6 +298,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         ring[slot][5] = buf_load16(rvs, so);
       }
     };
+    // Q8: the query codes and scales of the workgroup's heads stay in
+    // registers once staged (64 + HT registers), not re-read from LDS per block
+    i32x8_t qreg[Q8 ? 2 * HT : 1];
+    float qsr[Q8 ? HT : 1];
     // S^T of block n (16 tokens x kHW heads of this wave) -> s_lds[par], the
     // wave's per-head max -> red[par] (FP8: V scales -> vs_lds[par])
     auto scores = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
@@ -316,15 +320,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
                                static_cast<int>(u1.x), static_cast<int>(u1.y),
                                static_cast<int>(u1.z), static_cast<int>(u1.w)};
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            const int qi = ((ht * 2 + k2) * 64 + lane) * 2;
-            const uint4 qa = q_lds[qi], qb = q_lds[qi + 1];
-            const i32x8_t qop = {static_cast<int>(qa.x), static_cast<int>(qa.y),
-                                 static_cast<int>(qa.z), static_cast<int>(qa.w),
-                                 static_cast<int>(qb.x), static_cast<int>(qb.y),
-                                 static_cast<int>(qb.z), static_cast<int>(qb.w)};
-            s_acc[ht] = mfma_16x16x128_e4m3(kop, qop, s_acc[ht]);
-          }
+          for (int ht = 0; ht < HT; ++ht)
+            s_acc[ht] = mfma_16x16x128_e4m3(kop, qreg[Q8 ? ht * 2 + k2 : 0], s_acc[ht]);
         });
       }
       // bf16: the Q operands of k-step s+1 are read from LDS while step s
@@ -363,7 +360,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
           // Q8: and the q scale of head h0 + 16ht + c
-          const float qsc = Q8 ? qs_lds[Q8 ? 16 * ht + c : 0] : 1.0f;
+          const float qsc = Q8 ? qsr[Q8 ? ht : 0] : 1.0f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) s_acc[ht][e] *= Q8 ? ks[e] * qsc : ks[e];
         }
@@ -397,6 +394,21 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // before it leaves R-1 blocks outstanding.
     prologue_qk(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // Q staged
+    if constexpr (Q8) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int qi = ((ht * 2 + k2) * 64 + lane) * 2;
+          const uint4 qa = q_lds[qi], qb = q_lds[qi + 1];
+          qreg[ht * 2 + k2] = i32x8_t{static_cast<int>(qa.x), static_cast<int>(qa.y),
+                                      static_cast<int>(qa.z), static_cast<int>(qa.w),
+                                      static_cast<int>(qb.x), static_cast<int>(qb.y),
+                                      static_cast<int>(qb.z), static_cast<int>(qb.w)};
+        }
+        qsr[ht] = qs_lds[16 * ht + c];
+      }
+    }
     // iterations i = 0 .. N+1, S(i) for i < N; groups of U keep ring slots
     // and parities static (i = base + r, base a multiple of U)
     int base = 0;

@@ -78,12 +78,21 @@ def counters_for(workload_name: str, kernel_sig: str):
     return c.get("hbm_bytes_per_launch")
 
 
+def code_text(src: str) -> str:
+    """Source text without // comments, trailing blanks and empty lines: the
+    signature follows the code, not its commentary."""
+    import re
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_sig() -> str:
+    """sha256 over the code of the attention kernel's sources."""
     import hashlib
     h = hashlib.sha256()
     for name in ("attn_mfma.hip", "device_common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "decode_attention_02_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "decode_attention_02_amd", "csrc", name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -30,7 +30,10 @@
 // of block i, the P.V product of block i-2 and the softmax of block i-1.
 // Every iteration issues the same number of loads (past the walk through
 // empty buffer resources, which read nothing), so the compiler's wait before
-// a ring slot is consumed leaves the younger slots in flight.
+// a ring slot is consumed leaves the younger slots in flight. The ring loads
+// are non-temporal (each cache byte is read once). At the end the PV waves
+// stage their bf16 results in LDS and all eight waves store whole 512-byte
+// head rows.
 // The running max is updated lazily: only when a block's max exceeds it by
 // more than 2^8 (log2 units) are O and the row sums rescaled, so p <= 256;
 // the result is the same softmax, normalised by the same reference at the end.

@@ -16,8 +16,7 @@ namespace mfa {
 // Partial o is bf16 (PBF16) or fp32; m and l are fp32.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); the remap
 // gives each XCD a contiguous range of sequences, the same range whose
-// splits the attention kernel ran there, so the partials are read through
-// the L2 they were written to.
+// splits the attention kernel ran there.
 template <bool PBF16>
 __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,

@@ -55,7 +55,10 @@ __device__ __forceinline__ f32x4_t mfma_16x16x128_e4m3(const i32x8_t& a, const i
 // Non-temporal stores for results the next kernel reads: they leave the
 // L2 write-back path early, so less dirty data is left for the write-back
 // at the end of the kernel (measured: ~1.5 us less between back-to-back
-// attention launches with 16 MB of split partials).
+// attention launches with 16 MB of split partials). They pay only for whole
+// lines: lanes that store small pieces far apart (one head row each) write
+// several times the bytes, so such results are gathered first (the
+// attention kernel stages its rows in LDS).
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

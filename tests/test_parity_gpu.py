@@ -72,6 +72,22 @@ def test_small_f32_generic(gpu_lib):
         assert r <= REL_L2_F32
 
 
+@pytest.mark.parametrize("base,over", [(3, dict()), (4, dict())], ids=["bf16-paged", "fp8-paged"])
+def test_waves_of_workgroups(gpu_lib, base, over):
+    """More (sequence, split) pairs than compute units (64 ragged sequences x
+    8 splits = 512 workgroups, so they run in waves), empty tail splits
+    included."""
+    rng = np.random.default_rng(71)
+    lens = rng.integers(0, 1500, size=64).tolist()
+    lens[:4] = [0, 1, 63, 1499]
+    w = small(base, batch=64, **over)
+    inp = workloads.make_inputs(base, workload=w, seed=72, prefill_lens=lens)
+    say(f"waves of workgroups {w.kv_dtype}: 64 x 8 splits")
+    T, cache, step = setup(inp, num_splits=8, chunk_tokens=192)
+    _, out = run(T, step)
+    check_bf16(to_np(out), orun.decode_step(inp)["o"], f"64 x 8 splits {w.kv_dtype}")
+
+
 def test_single_token_returns_v_exactly(gpu_lib):
     """Context of one token: the output is V bit for bit (bf16 cache, bf16 out)."""
     w = small(3, paged=False)

@@ -342,6 +342,60 @@ def test_graph_replay_matches_eager(gpu_lib):
     check_bf16(to_np(eager), orun.decode_step(inp)["o"], "graph step")
 
 
+def test_graph_replay_multi_q8_out_proj(gpu_lib):
+    """KV append of the new token, FP8-query multi-token attention over the
+    last 2 tokens of every sequence (3 splits, combine) and the output
+    projection with its FP8 pack, captured in one HIP graph: every replay,
+    with eager work and synchronisations in between, equals the eager run
+    bit for bit."""
+    import decode_attention_02_amd as mfa
+    w = small(4, batch=5)
+    inp = workloads.make_inputs(4, workload=w, seed=26, prefill_lens=[1, 63, 64, 200, 700],
+                                q_len=2, out_proj=True)
+    T, cache, step = setup(inp)
+    say("graph replay: append + q8 multi + out_proj")
+    B, d = 5, 256
+    maxlen = int(inp["seq_lens"].max())
+    chunk = -(-(-(-maxlen // 3)) // 64) * 64
+    wo = mfa.pack_weight(T["w_o"])
+    ws = torch.empty(mfa.split_workspace_bytes(B * 2, 64, d, 3), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, 2, 64, d), dtype=torch.bfloat16, device="cuda")
+    hid = T["w_o"].shape[0]
+    wsp = torch.empty(max(mfa.load().mfa_out_proj_workspace_bytes(B * 2, 64 * d, hid, 1), 16),
+                      dtype=torch.uint8, device="cuda")
+    outs = (torch.empty((B * 2, hid), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((B * 2, hid), dtype=torch.uint8, device="cuda"),
+            torch.empty(B * 2, dtype=torch.float32, device="cuda"))
+
+    def work():
+        mfa.kv_append(cache, T["k_new"], T["v_new"], T["prefill_lens"])
+        mfa.decode_attn_multi(T["q_multi"], cache, T["seq_lens"], maxlen, num_splits=3,
+                              chunk_tokens=chunk, out=o, workspace=ws, fp8_queries=True)
+        mfa.out_proj(o.view(B * 2, -1), wo, packed=True, workspace=wsp, out=outs)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (o,) + outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for r in range(3):
+        for t in (o,) + outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((o,) + outs, eager):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r}"
+    check_bf16(to_np(eager[0]), orun.decode_step_multi(inp, fp8_queries=True), "graph q8 multi")
+
+
 @pytest.mark.parametrize("idx,shrink", [(2, dict(batch=6, hidden=1024, q_rank=512, context=300)),
                                         (4, dict(batch=3, context=400)),
                                         (1, {})])

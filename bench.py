@@ -13,8 +13,10 @@ The steps are captured once into HIP graphs (no allocation happens inside a
 step) and replayed, so the GPU runs them back to back. Prints one JSON line:
 throughput in decode tokens/s over K timed steps; the attention kernel's
 roofline (algorithmic KV bytes per launch / its average duration, from HIP
-events around K back-to-back attention launches on the same buffers); and
-the fp64 oracle timed on the same workload on the host cores.
+events around K back-to-back attention launches on the same buffers); the
+spread of single-step times; a pure read stream of the attention's bytes on
+the same device, for reference (libmfa_probe.so); and the fp64 oracle timed
+on the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the pure read-stream reference measurement")
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence decoded together (multi-token decode, "
                          "workloads without a query path)")
@@ -129,6 +133,43 @@ def cpu_baseline(inp, min_seconds: float = 10.0, fp8_queries: bool = False):
             "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
                       f"tokens{', with output projection' if 'w_o' in inp else ''}), fp64 numpy, "
                       f"mean of {runs} runs ({dt:.2f} s each)"}
+
+
+def stream_ceiling(device, nbytes: int = 134217728, copies: int = 4, reps: int = 20) -> dict:
+    """Read bandwidth of a pure stream of nbytes (16-byte non-temporal loads,
+    one workgroup per compute unit) over `copies` rotating buffers, so the
+    last-level cache cannot hold them: the same bytes the 4K attention reads,
+    streamed with nothing else to do."""
+    import ctypes
+
+    import torch
+    from decode_attention_02_amd import build as mbuild
+    lib = ctypes.CDLL(mbuild.PROBE)
+    lib.mfa_probe_stream.restype = ctypes.c_int
+    lib.mfa_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=device) for _ in range(copies)]
+    sink = torch.empty(512 * 16, dtype=torch.uint8, device=device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+    def launch(i):
+        rc = lib.mfa_probe_stream(ctypes.c_void_p(bufs[i % copies].data_ptr()), nbytes, 256, 1,
+                                  ctypes.c_void_p(sink.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe failed ({rc})")
+    for i in range(copies * 2):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del bufs
+    return {"GBps": nbytes / (us * 1e-6) / 1e9, "bytes": nbytes, "us": us,
+            "kind": "non-temporal 16-byte loads, 256 workgroups, 4 rotating buffers"}
 
 
 def copy_calibration(mib: int) -> None:
@@ -309,6 +350,7 @@ def main():
 
     use_graph = not args.eager
     if use_graph:
+        g_ones = [capture(lambda r=r: one(r)) for r in range(rotate)]
         g_warm = capture(lambda: [one(i) for i in range(args.warmup)])
         g_steps = capture(lambda: [one(i) for i in range(args.steps)])
         g_attn = capture(lambda: [attention(i, q_fixed[i % rotate]) for i in range(args.steps)])
@@ -344,6 +386,21 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     attn_avg = a0.elapsed_time(a1) / args.steps
+    # per-step spread: one step at a time (same buffer rotation), events around each
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        if use_graph:
+            g_ones[i % rotate].replay()
+        else:
+            one(i)
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
     op_rec = None
     if args.out_proj:
         # timed region 3: K output projections back to back
@@ -402,7 +459,15 @@ def main():
                      "kernel_avg_us": attn_avg * 1e3,
                      "algorithmic_bytes_per_launch": kv_bytes},
         "step_kv_plus_weights_GBps": (kv_bytes + w_bytes) / (ms * 1e-3) / 1e9,
+        "kv_tokens_per_s": int(inp["seq_lens"].sum()) / (ms * 1e-3),
+        "step_us_single": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                           "note": "one step per replay, events around each (adds the per-replay "
+                                   "launch); value/ms_per_step time K steps in one replay"},
     }
+    if not args.no_stream_ceiling:
+        ceil = stream_ceiling(dev)
+        ceil["attention_frac_of_ceiling"] = achieved / ceil["GBps"]
+        rec["stream_ceiling"] = ceil
     if op_rec is not None:
         rec["out_proj_roofline"] = op_rec
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Build libmfa.so in-tree with hipcc for gfx950.
+"""Build libmfa.so (and the benchmark's stream probe, libmfa_probe.so)
+in-tree with hipcc for gfx950.
 
 Usage: ``python -m decode_attention_02_amd.build`` (or ``build()``). Every
 call compiles from source; the result lands next to this file.
@@ -15,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmfa.so")
+# measurement aid for bench.py (a pure read stream), built beside the library
+PROBE = os.path.join(HERE, "libmfa_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 
 SOURCES = ["mfa_api.cpp", "attn_mfma.hip", "attn_valu.hip", "combine.hip", "kv_append.hip",
            "qproj.hip"]
@@ -44,6 +48,12 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    psrcs = [os.path.join(CSRC, s) for s in PROBE_SOURCES]
+    cmd = [hipcc(), *FLAGS, "-x", "hip", *psrcs, "-o", PROBE + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 

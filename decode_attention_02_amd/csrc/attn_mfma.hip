@@ -27,7 +27,9 @@
 // Each wave holds only its own role's operands in a register ring of RK
 // (QK) or RV (PV) blocks, filled with buffer loads. The stages are skewed
 // across iterations separated by one barrier each: iteration i computes S
-// of block i, the P.V product of block i-2 and the softmax of block i-1.
+// of unit i, the P.V product of unit i-2 and the softmax of unit i-1, where a
+// unit is one cache block, or two consecutive blocks for FP8 caches (the same
+// bytes between barriers as one bf16 block, twice the independent work).
 // Every iteration issues the same number of loads (past the walk through
 // empty buffer resources, which read nothing), so the compiler's wait before
 // a ring slot is consumed leaves the younger slots in flight. The ring loads
@@ -109,9 +111,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
 // HT: 16-head tiles per workgroup (4: all 64 heads; 2: half of them, two
 // workgroups per (sequence, split) reading the same K/V blocks).
-template <bool FP8, int RK, int RV, int HT, bool Q8 = false>
+template <bool FP8, int RK, int RV, int HT, bool Q8 = false, int BPI = 1>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   static_assert(!Q8 || FP8, "FP8 queries run against FP8 caches");
+  static_assert(BPI == 1 || (BPI == 2 && !Q8), "two blocks per iteration: plain FP8 and bf16 only");
   using C = Cfg<FP8>;
   constexpr int kHW = 16 * HT;                                          // heads of this workgroup
   constexpr int kHS = kH / kHW;                                         // workgroups per split
@@ -120,10 +123,11 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // and [128k2 + 64 + 16gg .. +16] (the K ring's unit pair for k2)
   __shared__ __attribute__((aligned(16))) uint4 q_lds[HT * (Q8 ? 4 : 8) * 64];
   __shared__ float qs_lds[Q8 ? kHW : 1];                                 // Q8: q scale per head
-  __shared__ __attribute__((aligned(16))) uint4 p_lds[2][HT * 2 * 64];  // 2 x HT x 2 KB, operand order
-  __shared__ __attribute__((aligned(16))) f32x4_t s_lds[2][4 * HT * 64]; // logits by (QK wave, tile, lane)
+  // per parity, per block of the iteration unit (bb < BPI)
+  __shared__ __attribute__((aligned(16))) uint4 p_lds[2][BPI * HT * 2 * 64];  // HT x 2 KB per block, operand order
+  __shared__ __attribute__((aligned(16))) f32x4_t s_lds[2][BPI * 4 * HT * 64]; // logits by (block, QK wave, tile, lane)
   __shared__ __attribute__((aligned(16))) float red[2][kHW * 4];        // block max [head][QK wave]
-  __shared__ __attribute__((aligned(16))) uint4 vs_lds[2][16];          // FP8 V scales by (QK wave, row)
+  __shared__ __attribute__((aligned(16))) uint4 vs_lds[2][BPI * 16];    // FP8 V scales by (block, QK wave, row)
   __shared__ __attribute__((aligned(16))) float lred[kHW * 4];          // row sums [head][PV wave]
 
   const int tid = threadIdx.x;
@@ -154,6 +158,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int t1 = min(t0 + a.chunk_tokens, L);
   const int blk0 = t0 >> 6;
   const int N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;   // blocks to walk
+  // iterations walk units of BPI consecutive blocks (a unit's second block
+  // past the walk reads nothing and is masked out)
+  const int NU = (N + BPI - 1) / BPI;
 
   // Q rows of the workgroup's heads -> LDS in operand order: block (ht, s),
   // lane (gg, cc) holds Q[h0+ht*16+cc][qk_dim(s, gg) .. +8]. The QK waves
@@ -268,18 +275,22 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const bool stage_out = a.num_splits == 1 ? !a.out_f32 : (a.part_bf16 && N > 0);
 
   // Every wave passes the same barriers: one after staging Q, one per
-  // iteration i = 0 .. N+1, one before the epilogue (and one more before the
+  // iteration i = 0 .. NU+1 (NU units of BPI blocks), one before the epilogue (and one more before the
   // staged stores).
   if (w < 4) {
     // ================= QK waves: S = K.Q^T -> LDS, per-wave block max
     constexpr int R = RK;
     constexpr int U = unroll_for(RK);
-    uint4 ring[R][C::kSlot];             // K units of 16 tokens (+ FP8 K, V scales)
-    // Loads block n into a ring slot; n >= N (past the walk) issues the same
-    // number of loads through empty resources, which return zeros and read
-    // nothing, so the loop's load count is the same on every path.
-    auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {
+    uint4 ring[R][BPI][C::kSlot];        // K units of 16 tokens (+ FP8 K, V scales) per block
+    // Loads iteration unit u (blocks BPI*u ..) into a ring slot; blocks past
+    // the walk issue the same number of loads through empty resources, which
+    // return zeros and read nothing, so the loop's load count is the same on
+    // every path.
+    auto issue = [&](auto slot_c, int u) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+      for (int bb = 0; bb < BPI; ++bb) {
+      const int n = u * BPI + bb;
       const bool real = n < N;
       const size_t pb = phys(real ? n : 0);
       // units (tg = ww, s): K[16ww + c][..], 1 KB contiguous per load
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       const int vo = (ww * C::kLoads) * 1024 + lane * 16;
       static_for<0, C::kLoads>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
-        ring[slot][s] = buf_load16(rk, vo + s * 1024);
+        ring[slot][bb][s] = buf_load16(rk, vo + s * 1024);
       });
       if constexpr (FP8) {
         const int so = (16 * ww + 4 * g) * 4;
@@ -297,34 +308,38 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
             const_cast<float*>(a.k_scale) + pb * kBlockTokens, 0, nr, kRsrcFlags);
         const auto rvs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(a.v_scale) + pb * kBlockTokens, 0, nr, kRsrcFlags);
-        ring[slot][4] = buf_load16(rks, so);
-        ring[slot][5] = buf_load16(rvs, so);
+        ring[slot][bb][4] = buf_load16(rks, so);
+        ring[slot][bb][5] = buf_load16(rvs, so);
+      }
       }
     };
     // Q8: the query codes and scales of the workgroup's heads stay in
     // registers once staged (64 + HT registers), not re-read from LDS per block
     i32x8_t qreg[Q8 ? 2 * HT : 1];
     float qsr[Q8 ? HT : 1];
-    // S^T of block n (16 tokens x kHW heads of this wave) -> s_lds[par], the
-    // wave's per-head max -> red[par] (FP8: V scales -> vs_lds[par])
-    auto scores = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
+    // S^T of the blocks of unit u (16 tokens x kHW heads of this wave per
+    // block) -> s_lds[par], the wave's per-head max over the unit -> red[par]
+    // (FP8: V scales -> vs_lds[par])
+    auto scores = [&](auto slot_c, auto par_c, int u) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int par = decltype(par_c)::value;
-      f32x4_t s_acc[HT];
+      f32x4_t s_acc[BPI][HT];
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) s_acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int bb = 0; bb < BPI; ++bb)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) s_acc[bb][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if constexpr (Q8) {
         // two 128-deep k-steps: the K unit pair (2k2, 2k2+1) as codes
         static_for<0, 2>([&](auto kc) {
           constexpr int k2 = decltype(kc)::value;
-          const uint4 u0 = ring[slot][2 * k2], u1 = ring[slot][2 * k2 + 1];
+          const uint4 u0 = ring[slot][0][2 * k2], u1 = ring[slot][0][2 * k2 + 1];
           const i32x8_t kop = {static_cast<int>(u0.x), static_cast<int>(u0.y),
                                static_cast<int>(u0.z), static_cast<int>(u0.w),
                                static_cast<int>(u1.x), static_cast<int>(u1.y),
                                static_cast<int>(u1.z), static_cast<int>(u1.w)};
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
-            s_acc[ht] = mfma_16x16x128_e4m3(kop, qreg[Q8 ? ht * 2 + k2 : 0], s_acc[ht]);
+            s_acc[0][ht] = mfma_16x16x128_e4m3(kop, qreg[Q8 ? ht * 2 + k2 : 0], s_acc[0][ht]);
         });
       }
       // bf16: the Q operands of k-step s+1 are read from LDS while step s
@@ -343,47 +358,61 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
             qop[(s + 1) & 1][ht] = as_bf16x8(q_lds[(ht * 8 + s + 1) * 64 + lane]);
           __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's products
         }
-        bf16x8_t kop;
-        if constexpr (FP8) {
-          const uint4 u = ring[slot][s >> 1];
-          kop = (s & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
-        } else {
-          kop = as_bf16x8(ring[slot][s]);
+        bf16x8_t kop[BPI];
+#pragma unroll
+        for (int bb = 0; bb < BPI; ++bb) {
+          if constexpr (FP8) {
+            const uint4 kw = ring[slot][bb][s >> 1];
+            kop[bb] = (s & 1) ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
+          } else {
+            kop[bb] = as_bf16x8(ring[slot][bb][s]);
+          }
         }
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-          if constexpr (kQdb) s_acc[ht] = mfma_16x16x32(kop, qop[s & 1][ht], s_acc[ht]);
-          else s_acc[ht] = mfma_16x16x32(kop, as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]), s_acc[ht]);
+          // one Q operand serves every block of the unit
+          const bf16x8_t qv = kQdb ? qop[s & 1][ht] : as_bf16x8(q_lds[(ht * 8 + s) * 64 + lane]);
+#pragma unroll
+          for (int bb = 0; bb < BPI; ++bb) s_acc[bb][ht] = mfma_16x16x32(kop[bb], qv, s_acc[bb][ht]);
         }
       });
-      if constexpr (FP8) {
-        const uint4 k4 = ring[slot][4];
-        const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
-                             __uint_as_float(k4.w)};
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          // Q8: and the q scale of head h0 + 16ht + c
-          const float qsc = Q8 ? qsr[Q8 ? ht : 0] : 1.0f;
+      for (int bb = 0; bb < BPI; ++bb) {
+        if constexpr (FP8) {
+          const uint4 k4 = ring[slot][bb][4];
+          const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
+                               __uint_as_float(k4.w)};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s_acc[ht][e] *= Q8 ? ks[e] * qsc : ks[e];
+          for (int ht = 0; ht < HT; ++ht) {
+            // Q8: and the q scale of head h0 + 16ht + c
+            const float qsc = Q8 ? qsr[Q8 ? ht : 0] : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_acc[bb][ht][e] *= Q8 ? ks[e] * qsc : ks[e];
+          }
+          vs_lds[par][bb * 16 + ww * 4 + g] = ring[slot][bb][5];   // same value from the 16 lanes of a row
         }
-        vs_lds[par][ww * 4 + g] = ring[slot][5];   // same value from the 16 lanes of a row
-      }
-      const int lim = tokens_in(n);
-      if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
-        const int tt0 = 16 * ww + 4 * g;
+        const int lim = tokens_in(u * BPI + bb);
+        if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
+          const int tt0 = 16 * ww + 4 * g;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+          for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s_acc[ht][e] = (tt0 + e < lim) ? s_acc[ht][e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) s_acc[bb][ht][e] = (tt0 + e < lim) ? s_acc[bb][ht][e] : -INFINITY;
+        }
       }
-      // per-head max over the wave's 16 tokens; lane row g ends with the max
-      // of tile g (HT 4) or g/2 (HT 2), so one store per lane covers them all
+      // per-head max over the wave's 16 tokens of each block; lane row g
+      // ends with the max of tile g (HT 4) or g/2 (HT 2), so one store per
+      // lane covers them all
       float mt[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        mt[ht] = max_nonan(max3_nonan(s_acc[ht][0], s_acc[ht][1], s_acc[ht][2]), s_acc[ht][3]);
-        s_lds[par][(ww * HT + ht) * 64 + lane] = s_acc[ht];
+        mt[ht] = max_nonan(max3_nonan(s_acc[0][ht][0], s_acc[0][ht][1], s_acc[0][ht][2]), s_acc[0][ht][3]);
+#pragma unroll
+        for (int bb = 1; bb < BPI; ++bb)
+          mt[ht] = max_nonan(mt[ht], max_nonan(max3_nonan(s_acc[bb][ht][0], s_acc[bb][ht][1],
+                                                          s_acc[bb][ht][2]), s_acc[bb][ht][3]));
+#pragma unroll
+        for (int bb = 0; bb < BPI; ++bb) s_lds[par][((bb * 4 + ww) * HT + ht) * 64 + lane] = s_acc[bb][ht];
       }
       if constexpr (HT == 4) {
         red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
@@ -412,10 +441,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         qsr[ht] = qs_lds[16 * ht + c];
       }
     }
-    // iterations i = 0 .. N+1, S(i) for i < N; groups of U keep ring slots
+    // iterations i = 0 .. NU+1, S(unit i) for i < NU; groups of U keep ring slots
     // and parities static (i = base + r, base a multiple of U)
     int base = 0;
-    for (; base + U <= N; base += U) {
+    for (; base + U <= NU; base += U) {
       static_for<0, U>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         constexpr int slot = r % R, par = r & 1;
@@ -425,13 +454,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         __syncthreads();
       });
     }
-    // the rest: i = base .. N+1 (at most U+1 iterations)
+    // the rest: i = base .. NU+1 (at most U+1 iterations)
     static_for<0, U + 1>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
       constexpr int slot = r % R, par = r & 1;
       const int i = base + r;
-      if (i <= N + 1) {
-        if (i < N) {
+      if (i <= NU + 1) {
+        if (i < NU) {
           scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
           issue(std::integral_constant<int, slot>{}, i + R);
         }
@@ -456,29 +485,35 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     float m_run[HT], l_run[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
-    uint4 ring[R][C::kLoads];
-    auto issue = [&](auto slot_c, int n) __attribute__((always_inline)) {   // as for K
+    uint4 ring[R][BPI][C::kLoads];
+    auto issue = [&](auto slot_c, int u) __attribute__((always_inline)) {   // as for K
       constexpr int slot = decltype(slot_c)::value;
-      const bool real = n < N;
-      const size_t pb = phys(real ? n : 0);
-      // bf16 units (fg = 4ww + s/2, ks = s%2); FP8 units fg = 4ww + s
-      const auto rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(a.v) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
-      const int vo = (ww * C::kLoads) * 1024 + lane * 16;
-      static_for<0, C::kLoads>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        ring[slot][s] = buf_load16(rv, vo + s * 1024);
-      });
+#pragma unroll
+      for (int bb = 0; bb < BPI; ++bb) {
+        const int n = u * BPI + bb;
+        const bool real = n < N;
+        const size_t pb = phys(real ? n : 0);
+        // bf16 units (fg = 4ww + s/2, ks = s%2); FP8 units fg = 4ww + s
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(a.v) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
+        const int vo = (ww * C::kLoads) * 1024 + lane * 16;
+        static_for<0, C::kLoads>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          ring[slot][bb][s] = buf_load16(rv, vo + s * 1024);
+        });
+      }
     };
-    auto pv = [&](auto slot_c, auto par_c, int n) __attribute__((always_inline)) {
+    auto pv = [&](auto slot_c, auto par_c, int u) __attribute__((always_inline)) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int par = decltype(par_c)::value;
-      const int lim = tokens_in(n);
+#pragma unroll
+      for (int bb = 0; bb < BPI; ++bb) {
+      const int lim = tokens_in(u * BPI + bb);
       if (lim < kBlockTokens) {
         // tokens past the end: zero their V so 0 * (stale data) cannot reach O
         static_for<0, C::kLoads>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
-          uint4 u = ring[slot][s];
+          uint4 u = ring[slot][bb][s];
           if constexpr (FP8) {
             uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -497,79 +532,91 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
             u.z = keep_bf16(u.z, tb + 4 < lim, tb + 5 < lim);
             u.w = keep_bf16(u.w, tb + 6 < lim, tb + 7 < lim);
           }
-          ring[slot][s] = u;
+          ring[slot][bb][s] = u;
         });
       }
       static_for<0, 2>([&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
         bf16x8_t pop[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) pop[ht] = as_bf16x8(p_lds[par][(ht * 2 + ks) * 64 + lane]);
+        for (int ht = 0; ht < HT; ++ht)
+          pop[ht] = as_bf16x8(p_lds[par][bb * HT * 2 * 64 + (ht * 2 + ks) * 64 + lane]);
         static_for<0, 4>([&](auto dtc) {
           constexpr int dt = decltype(dtc)::value;
           bf16x8_t vop;
           if constexpr (FP8) {
-            const uint4 u = ring[slot][dt];
-            vop = ks ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
+            const uint4 vw = ring[slot][bb][dt];
+            vop = ks ? e4m3x8_to_bf16x8(vw.z, vw.w) : e4m3x8_to_bf16x8(vw.x, vw.y);
           } else {
-            vop = as_bf16x8(ring[slot][dt * 2 + ks]);
+            vop = as_bf16x8(ring[slot][bb][dt * 2 + ks]);
           }
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) acc[dt][ht] = mfma_16x16x32(vop, pop[ht], acc[dt][ht]);
         });
       });
+      }
     };
 
-    // softmax of block n for this wave's 16 tokens (those QK wave ww
-    // scored): block max from all four QK waves, lazy update of the running
+    // softmax of one unit for this wave's 16 tokens per block (those QK wave
+    // ww scored): unit max from all four QK waves, lazy update of the running
     // max (O rescaled here, so the next products add to a consistent sum),
     // P^T (bf16, FP8: times the V scales) -> p_lds[par]
     auto softmax = [&](auto par_c) __attribute__((always_inline)) {
       constexpr int par = decltype(par_c)::value;
       float4 r4[HT];
-      f32x4_t sv[HT];
+      f32x4_t sv[BPI][HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         r4[ht] = reinterpret_cast<const float4*>(red[par])[ht * 16 + c];
-        sv[ht] = s_lds[par][(ww * HT + ht) * 64 + lane];
+#pragma unroll
+        for (int bb = 0; bb < BPI; ++bb) sv[bb][ht] = s_lds[par][((bb * 4 + ww) * HT + ht) * 64 + lane];
       }
-      float vs[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (FP8) {
-        const uint4 v4 = vs_lds[par][ww * 4 + g];
-        vs[0] = __uint_as_float(v4.x); vs[1] = __uint_as_float(v4.y);
-        vs[2] = __uint_as_float(v4.z); vs[3] = __uint_as_float(v4.w);
+      float vs[BPI][4];
+#pragma unroll
+      for (int bb = 0; bb < BPI; ++bb) {
+        vs[bb][0] = vs[bb][1] = vs[bb][2] = vs[bb][3] = 1.f;
+        if constexpr (FP8) {
+          const uint4 v4 = vs_lds[par][bb * 16 + ww * 4 + g];
+          vs[bb][0] = __uint_as_float(v4.x); vs[bb][1] = __uint_as_float(v4.y);
+          vs[bb][2] = __uint_as_float(v4.z); vs[bb][3] = __uint_as_float(v4.w);
+        }
       }
       bool rescale = false;
       float alpha[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        // block max over all 64 tokens (finite: every walked block has a valid token)
+        // max over the unit's tokens (finite: every walked unit has a valid token)
         const float tz = max_nonan(max3_nonan(r4[ht].x, r4[ht].y, r4[ht].z), r4[ht].w) * cl2;
         alpha[ht] = 1.0f;
-        if (tz > m_run[ht] + kLazy) {          // also true for the first block
+        if (tz > m_run[ht] + kLazy) {          // also true for the first unit
           alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - tz);
           m_run[ht] = tz;
           rescale = true;
         }
         const float nm = -m_run[ht];
-        float p[4];
+        float lsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ht][e], cl2, nm));
-        l_run[ht] = l_run[ht] * alpha[ht] + ((p[0] + p[1]) + (p[2] + p[3]));
-        if constexpr (FP8) {
+        for (int bb = 0; bb < BPI; ++bb) {
+          float p[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] *= vs[e];
+          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[bb][ht][e], cl2, nm));
+          lsum += (p[0] + p[1]) + (p[2] + p[3]);
+          if constexpr (FP8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] *= vs[bb][e];
+          }
+          // P^T into operand block (ht, ks) of block bb of buffer par
+          int ks, gr;
+          if constexpr (FP8) { ks = g >> 1; gr = ww; }
+          else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
+          uint2 pk;
+          pk.x = pack_bf16x2(p[0], p[1]);
+          pk.y = pack_bf16x2(p[2], p[3]);
+          uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[par] + bb * HT * 2 * 64) +
+                         ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
+          *reinterpret_cast<uint2*>(dst) = pk;
         }
-        // P^T into operand block (ht, ks) of buffer par
-        int ks, gr;
-        if constexpr (FP8) { ks = g >> 1; gr = ww; }
-        else { ks = ww >> 1; gr = 2 * (ww & 1) + (g >> 1); }
-        uint2 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
-        uint8_t* dst = reinterpret_cast<uint8_t*>(p_lds[par]) +
-                       ((ht * 2 + ks) * 64 + gr * 16 + c) * 16 + (g & 1) * 8;
-        *reinterpret_cast<uint2*>(dst) = pk;
+        l_run[ht] = l_run[ht] * alpha[ht] + lsum;
       }
       if (__ballot(rescale) != 0ull) {   // uniform: every PV wave takes the same branch
 #pragma unroll
@@ -581,19 +628,19 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 
     __syncthreads();   // Q staged
     prologue_pv(std::integral_constant<int, R>{}, issue);
-    __syncthreads();   // iteration 0 (S of block 0 on the QK waves)
-    if (N > 0) softmax(std::integral_constant<int, 0>{});
+    __syncthreads();   // iteration 0 (S of unit 0 on the QK waves)
+    if (NU > 0) softmax(std::integral_constant<int, 0>{});
     __syncthreads();   // iteration 1
-    // iteration n + 2: P.V of block n, then the softmax of block n + 1
+    // iteration n + 2: P.V of unit n, then the softmax of unit n + 1
     int nb = 0;
-    for (; nb + U <= N; nb += U) {
+    for (; nb + U <= NU; nb += U) {
       static_for<0, U>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         constexpr int slot = r % R, par = r & 1;
         const int n = nb + r;
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
-        if (n + 1 < N) softmax(std::integral_constant<int, par ^ 1>{});
+        if (n + 1 < NU) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       });
     }
@@ -601,10 +648,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       constexpr int r = decltype(rc)::value;
       constexpr int slot = r % R, par = r & 1;
       const int n = nb + r;
-      if (n < N) {
+      if (n < NU) {
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
-        if (n + 1 < N) softmax(std::integral_constant<int, par ^ 1>{});
+        if (n + 1 < NU) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       }
     });
@@ -692,8 +739,9 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
     if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4, true>), grid, block, 0, stream, a);
   } else if (fp8) {
-    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4>), grid, block, 0, stream, a);
+    // two 32 KB FP8 blocks per iteration: the same bytes between barriers as one bf16 block
+    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, 2, false, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, 4, false, 2>), grid, block, 0, stream, a);
   } else {
     if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 4, 2>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, 4>), grid, block, 0, stream, a);

@@ -36,16 +36,20 @@ struct GemmPlan {
 // Wide outputs (>= 512 tiles of 32 columns) run one K slice on 32-column
 // tiles; narrower ones use 64-column tiles (80 when that fills the 256
 // compute units better: the down-projection with the K/V columns, 2560
-// columns, is 32 x 8 workgroups of 80 columns instead of 40 x 8 of 64) and
-// halve K until the grid reaches 256 workgroups or a slice would drop below
-// 16 k-steps of 32 (two per wave).
+// columns, is 32 x 8 workgroups of 80 columns instead of 40 x 4 of 64) and
+// halve K while the grid stays within one round of 256 workgroups (one per
+// compute unit) and a slice keeps at least 16 k-steps of 32 (two per wave).
+// A second, partial round costs more than the compute units one round
+// leaves idle: the 7168-column output projection runs 112 x 2 workgroups
+// (K slices of 8192) in 43.0 / 49.4 / 63.3 us at 16 / 32 / 64 tokens, and
+// 112 x 4 in 48.1 / 52.5 / 66 us.
 GemmPlan plan_gemm(int N, int K, int rows) {
   if (N % 32 == 0 && N / 32 >= 512) return GemmPlan{2, 1};
   auto split = [&](int ntiles) {
     GemmPlan p{ntiles, 1};
     const int tiles = N / (16 * ntiles);
     const int steps = K / 32;
-    while (static_cast<long long>(tiles) * p.ks < 256 && steps % (p.ks * 2) == 0 &&
+    while (static_cast<long long>(tiles) * p.ks * 2 <= 256 && steps % (p.ks * 2) == 0 &&
            steps / (p.ks * 2) >= 16)
       p.ks *= 2;
     return p;

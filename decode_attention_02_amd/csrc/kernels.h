@@ -89,7 +89,7 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // Query path.
 // bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 128. With ksplit > 1 writes fp32
 // partials part[ks][M][N] (K slice ks); with ksplit == 1 and out_bf16 set,
-// writes bf16 C directly. ntiles (2, 4, or 5 with M <= 32) = 16-column tiles
+// writes bf16 C directly. ntiles (2, 4, or 5 or 7 with M <= 32) = 16-column tiles
 // per workgroup.
 // Requires N % (16*ntiles) == 0 and (K/ksplit) % 32 == 0. packed / a_packed:
 // W / A in operand order (qproj.hip); a packed A holds gemm_row_tiles(M)

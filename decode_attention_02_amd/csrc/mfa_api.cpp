@@ -29,7 +29,7 @@ constexpr int kRowsPerPass = 64;     // rows per pass of the query path
 constexpr int kOutProjRows = 128;    // rows per pass of the output projection (GEMM limit)
 
 struct GemmPlan {
-  int ntiles;        // 16-column tiles per workgroup (2 or 4)
+  int ntiles;        // 16-column tiles per workgroup (2, 4, 5 or 7)
   int ks;            // K slices
 };
 
@@ -63,6 +63,10 @@ GemmPlan plan_gemm(int N, int K, int rows) {
   if (N % 80 == 0 && rows <= 32) {      // 80-column tiles hold at most 32 rows
     const GemmPlan p5 = split(5);
     if (fill(p5) > fill(best) + 1e-9) best = p5;
+  }
+  if (N % 112 == 0 && rows <= 32) {     // so do 112-column tiles
+    const GemmPlan p7 = split(7);
+    if (fill(p7) > fill(best) + 1e-9) best = p7;
   }
   return best;
 }

@@ -429,6 +429,11 @@ static void launch_gemm_variant(const GemmCall& c, int ksplit, int ntiles, hipSt
     else if (M <= 32) launch_gemm_shape<2, 4, 4, PACKED, PA, NTW>(grid, c, stream);
     else if (M <= 64) launch_gemm_shape<4, 4, 3, PACKED, PA, NTW>(grid, c, stream);
     else launch_gemm_shape<8, 4, 2, PACKED, PA, NTW>(grid, c, stream);
+  } else if (ntiles == 7) {
+    // 112-column tiles: 7168 columns are 64 of them, x 4 K slices = 256 workgroups
+    dim3 grid(static_cast<unsigned>(c.N / 112), static_cast<unsigned>(ksplit));
+    if (M <= 16) launch_gemm_shape<1, 7, 4, PACKED, PA, NTW>(grid, c, stream);
+    else launch_gemm_shape<2, 7, 4, PACKED, PA, NTW>(grid, c, stream);
   } else if (ntiles == 5) {
     dim3 grid(static_cast<unsigned>(c.N / 80), static_cast<unsigned>(ksplit));
     // (64 rows x 80 columns would need more LDS than a CU has for the reduction)
@@ -449,8 +454,8 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, float* part, u
                             int M, int N, int K, int ksplit, int ntiles, bool packed, bool a_packed,
                             hipStream_t stream, const uint16_t* W2, int N1, bool stream_w) {
   if (M < 1 || M > 128) return hipErrorInvalidValue;
-  if (ntiles != 2 && ntiles != 4 && ntiles != 5) return hipErrorInvalidValue;
-  if (ntiles == 5 && M > 32) return hipErrorInvalidValue;
+  if (ntiles != 2 && ntiles != 4 && ntiles != 5 && ntiles != 7) return hipErrorInvalidValue;
+  if ((ntiles == 5 || ntiles == 7) && M > 32) return hipErrorInvalidValue;
   if (N % (16 * ntiles)) return hipErrorInvalidValue;
   if (W2 && (N1 <= 0 || N1 >= N || N1 % 16)) return hipErrorInvalidValue;
   const GemmCall c{A, W, W2, part, out_bf16, M, N, K, K / ksplit, W2 ? N1 : N};

@@ -537,7 +537,8 @@ __global__ __launch_bounds__(512) void gemm_rows_kernel(const uint16_t* __restri
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto issue_w = [&](auto slot_c, int ch) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    const int co = ch < nchunks ? ch * CH * 1024 : 0;   // past the end: chunk 0 again, unused
+    // past the end: an offset beyond the resource, which reads nothing (zeros, unused)
+    const int co = ch < nchunks ? ch * CH * 1024 : wbytes;
 #pragma unroll
     for (int i = 0; i < C::kPer; ++i)
       wreg[slot][i] = __builtin_bit_cast(

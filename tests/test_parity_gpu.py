@@ -433,8 +433,10 @@ def test_fused_step_matches_staged(gpu_lib, idx, shrink):
     (2, dict(batch=5, hidden=512, q_rank=256, context=200, kv_dtype="fp8", paged=True), True),
     (5, dict(batch=3, context=300), True),                              # 80-column tiles, 16 rows
     (2, dict(batch=24, context=130), True),                             # 80-column tiles, 32 rows
+    (2, dict(batch=48, context=130), True),                             # 64-column tiles x 4 K slices
     (1, {}, False),                                                     # fp32 path
-], ids=["bf16", "bf16-packed", "bf16-two-passes", "fp8-paged", "split", "full-width", "f32"])
+], ids=["bf16", "bf16-packed", "bf16-two-passes", "fp8-paged", "split", "full-width",
+        "full-width-48", "f32"])
 def test_kv_projection_step(gpu_lib, idx, shrink, packed):
     """The K/V projection fused into the step (w_kv): the new token equals
     the oracle's x W_k^T, x W_v^T rounded to the activation dtype; the cache
@@ -670,6 +672,7 @@ OUTPROJ = [
     (1, 4, 512, False),
     (256, 4, 8192, True),           # the limits: two passes of 128 rows, hidden 8192
     (5, 64, 7168, False),
+    (32, 64, 7168, True),           # 112-column tiles x 4 K slices: 256 workgroups
     (64, 4, 1024, True),
     (70, 64, 2048, False),
     (128, 64, 7168, True),
@@ -681,7 +684,9 @@ OUTPROJ = [
 def test_out_proj(gpu_lib, B, heads, hidden, packed):
     """y = o W_o^T and its per-token FP8 pack (mfa_out_proj) against the
     oracle; 128 tokens of Step-3's shape is the page's A2F payload (the last
-    two cases). B = 70 and 128 take two passes of at most 64 rows."""
+    two cases). Up to 32 rows at 7168 columns run 112-column tiles; 65 to
+    128 rows with packed weights run the row-split kernel; B = 256 takes two
+    passes of 128 rows."""
     import decode_attention_02_amd as mfa
     w = small(2, batch=B, heads=heads, hidden=hidden, context=65)
     inp = workloads.make_inputs(2, workload=w, seed=51, out_proj=True)

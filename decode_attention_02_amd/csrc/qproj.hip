@@ -237,6 +237,17 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
     }
   }
   float cv[kMaxChunks][8];
+  // the gain is loaded with the partials, not after the barrier, so its
+  // latency overlaps theirs
+  float4 gv[kMaxChunks][2];
+#pragma unroll
+  for (int ch = 0; ch < kMaxChunks; ++ch) {
+    const int j0 = ch * 2048 + tid * 8;
+    if (j0 < R) {
+      gv[ch][0] = *reinterpret_cast<const float4*>(g + j0);
+      gv[ch][1] = *reinterpret_cast<const float4*>(g + j0 + 4);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int ch = 0; ch < kMaxChunks; ++ch) {
@@ -277,9 +288,11 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* __rest
   for (int ch = 0; ch < kMaxChunks; ++ch) {
     const int j0 = ch * 2048 + tid * 8;
     if (j0 < R) {
+      const float gg[8] = {gv[ch][0].x, gv[ch][0].y, gv[ch][0].z, gv[ch][0].w,
+                           gv[ch][1].x, gv[ch][1].y, gv[ch][1].z, gv[ch][1].w};
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = cv[ch][j] * inv * g[j0 + j];
+      for (int j = 0; j < 8; ++j) v[j] = cv[ch][j] * inv * gg[j];
       const size_t o = static_cast<size_t>(m) * R + j0;
       if (out_f32) {
         float* d = reinterpret_cast<float*>(out) + o;

@@ -1,11 +1,13 @@
 """Benchmark of one MFA decode step on one MI355X.
 
 A step is the whole hot path over one batch: query path (down-projection,
-RMSNorm, up-projection), KV append of the new token, split-KV decode
-attention, split combine -- each one libmfa C-ABI call on one stream.
-Default workload: the Step-3-shaped bf16 decode (batch 32, hidden 7168,
-query rank 2048, 64 heads x 256 sharing one KV head, 4096-token contiguous
-cache). Inputs are seeded and synthetic and resident in HBM before timing;
+RMSNorm, up-projection; workloads that have one), KV append of the new
+token, split-KV decode attention, split combine -- each one libmfa C-ABI
+call on one stream. Default workload: the largest one, paged bf16 decode of
+128 sequences with mixed contexts (uniform in 1024..8192 tokens before the
+append, 64-token blocks at permuted physical ids; 64 heads x 256 sharing one
+KV head; 620 MB of KV per step). Inputs are seeded and synthetic and
+resident in HBM before timing;
 ``--rotate`` independent copies of cache and weights are cycled so that the
 256 MB last-level cache cannot hold a step's working set.
 
@@ -39,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload index 1..5")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index 1..5 (default 3: the largest, paged mixed lengths)")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
     ap.add_argument("--splits", type=int, default=0, help="override split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,39 +103,74 @@ def kernel_source_sig() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0, fp8_queries: bool = False):
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0, fp8_queries: bool = False,
+                 one_thread_seconds: float = 4.0):
     """fp64 oracle on the same inputs: the whole batch (query path, cache
     fill, attention of every sequence, and the output projection with its FP8
     pack when the inputs hold W_o), repeated until ``min_seconds`` of
-    host time have passed. Returns the record."""
+    host time have passed, on the BLAS threads the host gives; then the same
+    oracle on one thread over the first sequences of the batch (at most 16),
+    repeated for ``one_thread_seconds``. Returns the record."""
     import numpy as np  # noqa: F401
     from oracle import run as orun
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
     w = inp["workload"]
-    runs, total = 0, 0.0
     multi = "q_multi" in inp
     tq = inp["q_multi"].shape[1] if multi else 1
-    while total < min_seconds and runs < 50:
-        t0 = time.perf_counter()
-        if multi:
-            orun.decode_step_multi(inp, fp8_queries=fp8_queries)
-        else:
-            res = orun.decode_step(inp, fp8_queries=fp8_queries)
-            if "w_o" in inp:
-                orun.output_projection(inp, res["o"])
-        total += time.perf_counter() - t0
-        runs += 1
-    dt = total / runs
+
+    def timed(seqs, seconds):
+        runs, total = 0, 0.0
+        while total < seconds and runs < 50:
+            t0 = time.perf_counter()
+            if multi:
+                orun.decode_step_multi(inp, fp8_queries=fp8_queries, seqs=seqs)
+            else:
+                res = orun.decode_step(inp, seqs=seqs, fp8_queries=fp8_queries)
+                if "w_o" in inp and seqs is None:
+                    orun.output_projection(inp, res["o"])
+            total += time.perf_counter() - t0
+            runs += 1
+        return total / runs, runs
+
+    dt, runs = timed(None, min_seconds)
     toks = int(inp["seq_lens"].sum())
-    return {"value": w.batch * tq / dt, "unit": "decode tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
-                      f"tokens{', with output projection' if 'w_o' in inp else ''}), fp64 numpy, "
-                      f"mean of {runs} runs ({dt:.2f} s each)"}
+    rec = {"value": w.batch * tq / dt, "unit": "decode tokens/s", "cores": int(threads),
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "kv_tokens_per_s": toks / dt,
+           "sample": f"whole batch of workload {w.name} ({w.batch} sequences, {toks} cached "
+                     f"tokens{', with output projection' if 'w_o' in inp else ''}), fp64 numpy, "
+                     f"{threads} BLAS threads, mean of {runs} runs ({dt:.2f} s each)"}
+    if threadpool_limits is not None:
+        nseq = min(16, w.batch)
+        seqs = list(range(nseq))
+        with threadpool_limits(1):
+            dt1, runs1 = timed(seqs, one_thread_seconds)
+        toks1 = int(inp["seq_lens"][:nseq].sum())
+        rec["one_thread"] = {
+            "value": nseq * tq / dt1, "unit": "decode tokens/s", "cores": 1,
+            "kv_tokens_per_s": toks1 / dt1,
+            "sample": f"sequences 0..{nseq - 1} of {w.name} ({toks1} cached tokens; the query "
+                      f"path of the whole batch included), fp64 numpy on 1 thread, mean of "
+                      f"{runs1} runs ({dt1:.2f} s each)"}
+    return rec
 
 
 def stream_ceiling(device, nbytes: int = 134217728, copies: int = 4, reps: int = 20) -> dict:
@@ -241,7 +279,8 @@ def main():
         w_bytes += T["w_o"].numel() * 2
         # algorithmic bytes of one output projection: W_o, o, y, FP8 codes, scales
         op_bytes = hid * HDo * 2 + B * HDo * 2 + B * hid * 2 + B * hid + B * 4
-    rotate = args.rotate or max(2, min(8, -(-2 * 256 * 2 ** 20 // max(kv_bytes + w_bytes, 1))))
+    # at least 4 sets, and together at least twice the 256 MB last-level cache
+    rotate = args.rotate or max(4, min(8, -(-2 * 256 * 2 ** 20 // max(kv_bytes + w_bytes, 1))))
 
     sets = []
     for r in range(rotate):

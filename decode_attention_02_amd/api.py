@@ -157,8 +157,12 @@ def decode_plan(batch: int, heads: int, head_dim: int, max_seq_len: int, kv_dtyp
     return ns.value, ch.value
 
 
-def split_workspace_bytes(batch: int, heads: int, head_dim: int, num_splits: int) -> int:
-    return int(_lib.load().mfa_split_workspace_bytes(batch, heads, head_dim, num_splits))
+def decode_workspace_bytes(batch: int, heads: int, head_dim: int, num_splits: int) -> int:
+    """Bytes of split workspace (mfa_decode_workspace_bytes)."""
+    return int(_lib.load().mfa_decode_workspace_bytes(batch, heads, head_dim, num_splits))
+
+
+split_workspace_bytes = decode_workspace_bytes
 
 
 def decode_attn(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq_len: int,

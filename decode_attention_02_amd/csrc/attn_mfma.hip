@@ -142,6 +142,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // through one L2 at about the same time, and the splits of a sequence
   // share that L2 for their query reads.
   int id = blockIdx.x;
+  if (id == 0 && tid == 0 && a.num_splits > 1) *a.part_tag = a.part_bf16 ? kPartTagBf16 : kPartTagF32;
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int hg = id % kHS;
   const int split = (id / kHS) % a.num_splits;
@@ -378,6 +379,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       });
 #pragma unroll
       for (int bb = 0; bb < BPI; ++bb) {
+        const int lim = tokens_in(u * BPI + bb);
+        const int tt0 = 16 * ww + 4 * g;         // this lane's first token of the block
         if constexpr (FP8) {
           const uint4 k4 = ring[slot][bb][4];
           const float ks[4] = {__uint_as_float(k4.x), __uint_as_float(k4.y), __uint_as_float(k4.z),
@@ -389,11 +392,19 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s_acc[bb][ht][e] *= Q8 ? ks[e] * qsc : ks[e];
           }
-          vs_lds[par][bb * 16 + ww * 4 + g] = ring[slot][bb][5];   // same value from the 16 lanes of a row
+          // V scales (same value from the 16 lanes of a row); the scale slots
+          // of tokens past the end were never written and may hold anything
+          // (a NaN would survive p = 0 in p * scale), so they become 0
+          uint4 v4 = ring[slot][bb][5];
+          if (lim < kBlockTokens) {
+            v4.x = tt0 + 0 < lim ? v4.x : 0u;
+            v4.y = tt0 + 1 < lim ? v4.y : 0u;
+            v4.z = tt0 + 2 < lim ? v4.z : 0u;
+            v4.w = tt0 + 3 < lim ? v4.w : 0u;
+          }
+          vs_lds[par][bb * 16 + ww * 4 + g] = v4;
         }
-        const int lim = tokens_in(u * BPI + bb);
         if (lim < kBlockTokens) {        // tail block (uniform): tokens past the end -> -inf
-          const int tt0 = 16 * ww + 4 * g;
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll

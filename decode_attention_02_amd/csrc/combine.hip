@@ -17,11 +17,18 @@ namespace mfa {
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); the remap
 // gives each XCD a contiguous range of sequences, the same range whose
 // splits the attention kernel ran there.
+// The workspace's tag word names the element type the attention call wrote
+// part_o in; when it is not the type this launch reads, the output is NaN
+// (a combine called with another out_dtype than the attention call).
 template <bool PBF16>
 __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
+                                                          const uint32_t* __restrict__ part_tag,
                                                           int S, int H, int d, void* out,
                                                           int out_f32) {
+  // scalar load, issued first and checked only before the stores
+  using cu32 = const __attribute__((address_space(4))) uint32_t;
+  const uint32_t tag = ((cu32*)part_tag)[0];
   const int tpb = d >> 2;                        // threads per head
   const int hpb = 256 / tpb;                     // heads per workgroup
   const int groups = (H + hpb - 1) / hpb;
@@ -80,7 +87,8 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
       }
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  float inv = den > 0.f ? 1.0f / den : 0.f;
+  if (tag != (PBF16 ? kPartTagBf16 : kPartTagF32)) inv = __builtin_nanf("");
   const size_t oi = (static_cast<size_t>(b) * H + h) * d + f;
   if (out_f32) {
     store_nt(reinterpret_cast<float*>(out) + oi, make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
@@ -92,18 +100,19 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
   }
 }
 
-hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml, int B, int H,
-                          int d, int num_splits, void* out, int out_f32, hipStream_t stream) {
+hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml,
+                          const uint32_t* part_tag, int B, int H, int d, int num_splits, void* out,
+                          int out_f32, hipStream_t stream) {
   if (d % 4 || d > 1024) return hipErrorInvalidValue;
   const int hpb = 256 / (d / 4);
   const int groups = (H + hpb - 1) / hpb;
   const dim3 grid(static_cast<unsigned>(B * groups));
   if (part_bf16)
     hipLaunchKernelGGL(mfa_combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_ml,
-                       num_splits, H, d, out, out_f32);
+                       part_tag, num_splits, H, d, out, out_f32);
   else
     hipLaunchKernelGGL(mfa_combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_ml,
-                       num_splits, H, d, out, out_f32);
+                       part_tag, num_splits, H, d, out, out_f32);
   return hipGetLastError();
 }
 

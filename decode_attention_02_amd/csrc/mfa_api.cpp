@@ -121,6 +121,20 @@ mfa_status check_qproj_shape(int B, int hidden, int q_rank, int H, int d, int dt
 }
 
 // ---- attention planning --------------------------------------------------
+// Split workspace: part_o [rows][d] (rows = sequences x splits x heads; room
+// for fp32 even when bf16 is stored) at 0, part_ml fp32 [rows][2] at off_ml,
+// the partial-type tag word at off_tag.
+struct SplitLayout {
+  size_t off_ml, off_tag, total;
+};
+SplitLayout split_layout(size_t rows, int d) {
+  SplitLayout l;
+  l.off_ml = round_up(rows * static_cast<size_t>(d) * 4, 256);
+  l.off_tag = round_up(l.off_ml + rows * 2 * 4, 16);
+  l.total = l.off_tag + 16;
+  return l;
+}
+
 bool mfma_shape(int H, int d, int kv_dtype) {
   return H == 64 && d == 256 && (kv_dtype == MFA_BF16 || kv_dtype == MFA_FP8_E4M3);
 }
@@ -470,10 +484,13 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, i
   return MFA_OK;
 }
 
-size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits) {
+size_t mfa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   if (B < 1 || H < 1 || d < 1 || num_splits <= 1) return 0;
-  const size_t rows = static_cast<size_t>(B) * num_splits * H;
-  return round_up(rows * d * 4, 256) + rows * 2 * 4;
+  return split_layout(static_cast<size_t>(B) * num_splits * H, d).total;
+}
+
+size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits) {
+  return mfa_decode_workspace_bytes(B, H, d, num_splits);
 }
 
 }  // extern "C"
@@ -527,7 +544,7 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
     if (!out) return MFA_ERR_NULL;
   } else {
     if (!workspace) return MFA_ERR_WORKSPACE;
-    if (workspace_bytes < mfa_split_workspace_bytes(Bv, H, d, num_splits)) return MFA_ERR_WORKSPACE;
+    if (workspace_bytes < mfa_decode_workspace_bytes(Bv, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   }
 
   mfa::AttnArgs& a = c->a;
@@ -552,11 +569,12 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.q_len = q_len;
   a.fp8_queries = fp8_queries ? 1 : 0;
-  const size_t rows = static_cast<size_t>(Bv) * num_splits * H;
   if (num_splits > 1) {
+    const SplitLayout l = split_layout(static_cast<size_t>(Bv) * num_splits * H, d);
     a.part_o = workspace;
     a.part_bf16 = out_dtype == MFA_BF16;
-    a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + round_up(rows * d * 4, 256));
+    a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + l.off_ml);
+    a.part_tag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + l.off_tag);
   }
   a.out = out;
   a.out_f32 = out_dtype == MFA_F32;
@@ -574,8 +592,8 @@ mfa_status launch_attn(const AttnCall& c, hipStream_t st) {
   hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st) : mfa::launch_decode_valu(a, c.B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
   if (c.num_splits > 1 && c.out) {
-    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, c.B, c.H, c.d, c.num_splits, c.out,
-                            a.out_f32, st);
+    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, a.part_tag, c.B, c.H, c.d,
+                            c.num_splits, c.out, a.out_f32, st);
     if (e != hipSuccess) return MFA_ERR_HIP;
   }
   return MFA_OK;
@@ -669,12 +687,13 @@ mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int
   if (B < 1 || H < 1 || num_splits < 2) return MFA_ERR_SHAPE;
   if (d != 64 && d != 128 && d != 256) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
-  if (workspace_bytes < mfa_split_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
-  const size_t rows = static_cast<size_t>(B) * num_splits * H;
-  const float* pml =
-      reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + round_up(rows * d * 4, 256));
-  return from_hip(mfa::launch_combine(workspace, out_dtype == MFA_BF16, pml, B, H, d, num_splits,
-                                      out, out_dtype == MFA_F32, as_stream(stream)));
+  if (workspace_bytes < mfa_decode_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
+  const SplitLayout l = split_layout(static_cast<size_t>(B) * num_splits * H, d);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  return from_hip(mfa::launch_combine(workspace, out_dtype == MFA_BF16,
+                                      reinterpret_cast<const float*>(ws + l.off_ml),
+                                      reinterpret_cast<const uint32_t*>(ws + l.off_tag), B, H, d,
+                                      num_splits, out, out_dtype == MFA_F32, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define MFA_ABI_VERSION 2
+#define MFA_ABI_VERSION 3
 #define MFA_BLOCK_TOKENS 64
 /* Most query tokens per sequence in mfa_decode_attn_multi. */
 #define MFA_MAX_QUERY_TOKENS 16
@@ -201,14 +201,24 @@ mfa_status mfa_kv_append(const void *k_new, const void *v_new, int in_dtype,
 mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
                            int *num_splits, int *chunk_tokens);
 
-/* Bytes of split workspace for mfa_decode_attn / mfa_combine: the
- * unnormalised partial outputs part_o [B][num_splits][H][d] at offset 0,
- * then part_ml fp32 [B][num_splits][H][2] (running max m in natural-log
- * units of the scaled logits, then l = sum_t exp(s_t - m)) at offset
- * round_up(B*num_splits*H*d*4, 256). part_o holds bf16 values when the
- * out_dtype of the call is MFA_BF16 and fp32 values when it is MFA_F32, so
- * mfa_combine must be called with the out_dtype mfa_decode_attn was given.
- * 0 when num_splits == 1. */
+/* Bytes of split workspace for mfa_decode_attn / mfa_combine (the split
+ * partials of the long-context case, "Step-3 is Large yet Affordable"
+ * summary page, §4 Cost Analysis for LLM Decoding: attention cost grows with
+ * context and dominates from 8K on). With R = B*num_splits*H rows:
+ *   part_o  [B][num_splits][H][d] unnormalised partial outputs at offset 0
+ *           (bf16 when the attention call's out_dtype is MFA_BF16, fp32 when
+ *           it is MFA_F32; R*d*4 bytes are reserved either way)
+ *   part_ml fp32 [B][num_splits][H][2] at offset round_up(R*d*4, 256): the
+ *           running max m in natural-log units of the scaled logits, then
+ *           l = sum_t exp(s_t - m)
+ *   tag     one uint32 at offset round_up(off_ml + R*8, 16), written by the
+ *           attention call: 0x31464250 when part_o is bf16, 0x32334650 when
+ *           fp32. mfa_combine checks it against the type its own out_dtype
+ *           implies and writes NaN outputs when they differ.
+ * Total round_up(off_ml + R*8, 16) + 16 bytes; 0 when num_splits == 1. The
+ * caller owns it; the library keeps nothing in it between calls. */
+size_t mfa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+/* The same function under its earlier name. */
 size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
 
 /*
@@ -223,7 +233,7 @@ size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
  * num_splits >= 1 KV splits per sequence; split j covers tokens
  *            [j*chunk_tokens, min((j+1)*chunk_tokens, seq_len)). Requires
  *            chunk_tokens % 64 == 0 and num_splits*chunk_tokens >= max_seq_len.
- * workspace  mfa_split_workspace_bytes(...) bytes when num_splits > 1
+ * workspace  mfa_decode_workspace_bytes(...) bytes when num_splits > 1
  *            (receives the per-split partials), else may be NULL.
  * out        [B][H][d] of out_dtype (MFA_BF16 or MFA_F32). With
  *            num_splits > 1, out may be NULL: only the partials are
@@ -253,7 +263,7 @@ mfa_status mfa_decode_attn(const void *q, int q_dtype, int B, int H,
  *   q_len    1 .. MFA_MAX_QUERY_TOKENS; q_len == 1 is mfa_decode_attn
  * Every other argument is as in mfa_decode_attn, with the split partials and
  * the combine over the B * q_len rows (sequence, query token): the workspace
- * is mfa_split_workspace_bytes(B * q_len, H, d, num_splits) bytes and a
+ * is mfa_decode_workspace_bytes(B * q_len, H, d, num_splits) bytes and a
  * separate mfa_combine takes B * q_len as its batch. The query tokens of a
  * sequence run on one XCD side by side, so its KV blocks are read from HBM
  * about once and from that XCD's L2 q_len times.
@@ -287,12 +297,19 @@ mfa_status mfa_decode_attn_q8(const void *q, int q_dtype, int B, int q_len, int 
                               void *out, int out_dtype, void *stream);
 
 /*
- * Split combine: merges the num_splits partials (layout as in
- * mfa_split_workspace_bytes) of every (sequence, head) by log-sum-exp:
+ * Split combine ("Step-3 is Large yet Affordable" summary page, §4 Cost
+ * Analysis for LLM Decoding: attention cost grows with context and
+ * dominates the FFN from 8K on, so one sequence's context is spread over
+ * many workgroups and their partial softmax sums are merged here): merges
+ * the num_splits partials (layout as in mfa_decode_workspace_bytes) of
+ * every (sequence, head) by log-sum-exp:
  *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.
  * Splits with l_j == 0 (empty) get weight 0; a head whose splits are all
- * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32).
- * num_splits >= 2; d in {64, 128, 256}.
+ * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32), which
+ * must be the out_dtype the attention call was given (it fixes the type of
+ * part_o); otherwise the workspace tag does not match and out is NaN.
+ * num_splits >= 2; d in {64, 128, 256}. Host checks as for every call;
+ * MFA_ERR_WORKSPACE when workspace_bytes is below the required size.
  */
 mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,
                        int H, int d, int num_splits, void *out, int out_dtype,

@@ -34,8 +34,11 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=True):
-    """Upload inputs, allocate + prefill the cache, build the decode step."""
+def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=True,
+          poison=False):
+    """Upload inputs, allocate + prefill the cache, build the decode step.
+    ``poison``: fill every byte of the cache (and FP8 scales) with 0xFF
+    before the prefill, so slots no token was written to hold NaNs."""
     import decode_attention_02_amd as mfa
     from decode_attention_02_amd.step import DecodeStep, prefill
 
@@ -43,6 +46,10 @@ def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=Tru
     T = workloads.to_torch(inp, device)
     cache = mfa.KVCache(inp["num_blocks"], w.head_dim, w.kv_dtype, inp["max_blocks_per_seq"],
                         block_table=T["block_table"], device=device, zero=zero_cache)
+    if poison:
+        for t in (cache.k, cache.v, cache.k_scale, cache.v_scale):
+            if t is not None:
+                t.view(torch.uint8).fill_(0xFF)
     prefill(cache, T["k_ctx"], T["v_ctx"], inp["ctx_offsets"], inp["prefill_lens"])
     act = torch.float32 if w.act_dtype == "f32" else torch.bfloat16
     if num_splits is None and w.num_splits is not None:

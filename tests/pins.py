@@ -377,6 +377,82 @@ def _bf16_bits(vals):
     return bits
 
 
+# ------------------------------------------------------- FP8 scale rounding
+# The codec's scale is ONE correctly rounded fp32 division amax / 448 (the
+# reading of the Step-3 summary page's 8-bit KV, §5 Model-System Co-design).
+# The helpers below round exact rationals to fp32 on their own (no numpy
+# float arithmetic), so they check the oracle's division from outside it.
+def _f32_rne_exact(q: "Fraction") -> "Fraction":
+    """Nearest fp32 value of a rational in the normal range, ties to even."""
+    from fractions import Fraction
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = q / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def _f32_bits(v) -> int:
+    return int(np.array([float(v)], dtype=np.float32).view(np.uint32)[0])
+
+
+# A worked row (bf16 bits), derived by hand with exact rationals:
+#   amax = 1.015625 = 65/64; 65/64/448 = 65/28672 lies between the fp32 values
+#   0x3B149249 and 0x3B14924A and is nearer the first, which is the scale.
+#   The reciprocal route amax * fl(1/448) gives 0x3B14924A instead.
+#   0x3782 = 0x1.04p-16 = amax * 2^-16: its quotient rounds to exactly
+#   448 * 2^-16 = 3.5 * 2^-9, the midpoint between the subnormal codes 3 and
+#   4, which ties to the even code 4 (3 with the reciprocal scale's quotient,
+#   just below it). 0.25 / s = 110.3 -> 112 (0x6E); 0.9375 / s = 413.5 -> 416
+#   (0xFD); 0.0078125 / s = 3.446 -> 3.5 (0x46); -0.5078125 / s = -224 (0xF6).
+FP8_WORKED_ROW_BITS = [0x3F82, 0xBF02, 0x3782, 0xB782, 0x0000, 0x3E80, 0xBF70, 0x3C00]
+FP8_WORKED_SCALE_BITS = 0x3B149249
+FP8_WORKED_CODES = [0x7E, 0xF6, 0x04, 0x84, 0x00, 0x6E, 0xFD, 0x46]
+
+
+def _worked_row_f64():
+    return (np.asarray(FP8_WORKED_ROW_BITS, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _check_worked_fp8(codes, scale_bits, what):
+    """Failure messages if a coded worked row differs from the literals."""
+    fails = []
+    if int(scale_bits) != FP8_WORKED_SCALE_BITS:
+        fails.append(f"{what}: worked-row scale bits {int(scale_bits):#010x} != "
+                     f"{FP8_WORKED_SCALE_BITS:#010x} (amax/448 not one correctly rounded division)")
+    if [int(c) for c in codes] != FP8_WORKED_CODES:
+        fails.append(f"{what}: worked-row codes {[hex(int(c)) for c in codes]}")
+    return fails
+
+
+def _check_scales_exact(amax_f32, scales, what):
+    """Every scale equals the exactly rounded amax / 448 (1 for amax 0)."""
+    from fractions import Fraction
+    for a, s in zip(np.asarray(amax_f32, np.float32).tolist(), np.asarray(scales, np.float32).tolist()):
+        want = 1.0 if a == 0 else float(_f32_rne_exact(Fraction(a) / 448))
+        if _f32_bits(s) != _f32_bits(want):
+            return [f"{what}: scale of amax {a!r} is {s!r}, the rounded quotient is {want!r}"]
+    return []
+
+
+def _bf16_rne_bits(a32):
+    """bf16 bits of fp32 values, round to nearest even (torch's cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def check_a2f_pack(O):
     fails = []
     # worked rows: 448 -> s = 1, codes are the values' own e4m3 codes
@@ -406,6 +482,9 @@ def check_a2f_pack(O):
     step = np.where(r < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(r, 2.0 ** -6))) - 3))
     if not np.all(np.abs(deq - yb) / s[:, None] <= step / 2 * (1 + 1e-6) + 1e-30):
         fails.append("A2F pack error beyond half a step of the bf16 values")
+    fails += _check_scales_exact(np.max(np.abs(yb), axis=1), s, "A2F pack")
+    wc, ws = O.a2f_pack(np.asarray([FP8_WORKED_ROW_BITS], np.uint16))
+    fails += _check_worked_fp8(wc[0], _f32_bits(ws[0]), "A2F pack")
     with open(os.path.join(GOLDEN, "page_figures.json")) as f:
         figs = {e["id"]: e["value"] for e in json.load(f)["figures"]}
     if O.hidden_payload_bytes(128, 7168, 1) != figs["a2f_bytes_batch128"]:
@@ -507,6 +586,14 @@ def check_quantize(O):
         fails.append("quantisation error beyond half a step")
     if not np.all((codes[9] & 0x80) == 0x80):
         fails.append("sign lost for negative row")
+    fails += _check_scales_exact(np.max(np.abs(x), axis=1), s, "quantize")
+    # random bf16 rows: the scale is the exactly rounded quotient
+    xb = (rng.standard_normal((400, 64)) * np.exp2(rng.integers(-12, 10, size=(400, 1))))
+    xb = (_bf16_rne_bits(xb.astype(np.float32)).astype(np.uint32) << 16).view(np.float32)
+    _, sb = O.quantize_tokens(xb.astype(np.float64))
+    fails += _check_scales_exact(np.max(np.abs(xb), axis=1), sb, "quantize bf16 rows")
+    wc, ws = O.quantize_tokens(_worked_row_f64()[None, :])
+    fails += _check_worked_fp8(wc[0], _f32_bits(ws[0]), "quantize")
     return fails
 
 
@@ -550,6 +637,10 @@ def check_fp8_queries(O):
     a2 = O.softmax_attention(qg[0], k, v, 0.01)
     if not np.array_equal(a1, a2):
         fails.append("FP8-query attention differs on exactly representable queries")
+    # the worked row as head 1 of a token, next to another head
+    qw = np.stack([rng.standard_normal(8), _worked_row_f64()])[None]      # [1][H=2][8]
+    cw, sw = O.quantize_queries(qw)
+    fails += _check_worked_fp8(cw[0, 1], _f32_bits(sw[0, 1]), "FP8 queries")
     return fails
 
 

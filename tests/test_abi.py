@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mfa_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.mfa_abi_version() == _lib.ABI_VERSION == 3
     for s in range(8):
         assert lib.mfa_status_str(s)
     assert lib.mfa_status_str(99) == b"unknown status"
@@ -181,9 +181,17 @@ def test_plan_and_split_workspace(lib):
         assert lib.mfa_decode_plan(B, 64, 256, L, BF16, ctypes.byref(ns), ctypes.byref(ch)) == OK
         assert ns.value >= 1 and ch.value % 64 == 0 and ns.value * ch.value >= L
     assert lib.mfa_decode_plan(0, 64, 256, 10, BF16, ctypes.byref(ns), ctypes.byref(ch)) == SHAPE
-    assert lib.mfa_split_workspace_bytes(4, 64, 256, 1) == 0
+    assert lib.mfa_decode_workspace_bytes(4, 64, 256, 1) == 0
     rows = 4 * 32 * 64
-    assert lib.mfa_split_workspace_bytes(4, 64, 256, 32) == rows * 256 * 4 + rows * 2 * 4
+    off_ml = rows * 256 * 4                      # a multiple of 256 already
+    off_tag = -(-(off_ml + rows * 8) // 16) * 16
+    assert lib.mfa_decode_workspace_bytes(4, 64, 256, 32) == off_tag + 16
+    rows = 3 * 5 * 7
+    off_ml = -(-rows * 64 * 4 // 256) * 256
+    off_tag = -(-(off_ml + rows * 8) // 16) * 16
+    assert lib.mfa_decode_workspace_bytes(3, 7, 64, 5) == off_tag + 16
+    for args in ((4, 64, 256, 32), (3, 7, 64, 5), (1, 1, 1, 1)):
+        assert lib.mfa_split_workspace_bytes(*args) == lib.mfa_decode_workspace_bytes(*args)
     assert lib.mfa_combine(None, 0, 4, 64, 256, 32, P, BF16, None) == NULL
     assert lib.mfa_combine(P, 16, 4, 64, 256, 32, P, BF16, None) == WS
     assert lib.mfa_combine(P, 1 << 30, 4, 64, 256, 1, P, BF16, None) == SHAPE

@@ -109,6 +109,25 @@ def _quant_wrong_max(x):
     return e4m3.encode_rne((x32 / s[:, None]).astype(np.float32)), s
 
 
+def _quant_scale_by_reciprocal(x):
+    # s = amax * fl(1/448): two roundings instead of one correctly rounded division
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    s = (amax * (np.float32(1.0) / np.float32(448.0))).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    return e4m3.encode_rne((x32 / s[:, None]).astype(np.float32)), s
+
+
+def _a2f_scale_by_reciprocal(bits):
+    return _quant_scale_by_reciprocal(mfa.bf16_bits_to_f64(bits))
+
+
+def _qq_scale_by_reciprocal(q):
+    q = np.asarray(q, float)
+    c, sc = _quant_scale_by_reciprocal(q.reshape(-1, q.shape[-1]))
+    return c.reshape(q.shape), sc.reshape(q.shape[:-1])
+
+
 def _ai_qk_only(H, d, b, sb=0):
     return 2 * H * d / (2 * d * b + 2 * sb)
 
@@ -246,6 +265,9 @@ MUTANTS = {
     "e4m3_ties_away": dict(e4m3_encode=_encode_ties_away),
     "e4m3_truncates": dict(e4m3_encode=_encode_truncate),
     "quant_wrong_max": dict(quantize_tokens=_quant_wrong_max),
+    "quant_scale_by_reciprocal": dict(quantize_tokens=_quant_scale_by_reciprocal),
+    "a2f_pack_scale_by_reciprocal": dict(a2f_pack=_a2f_scale_by_reciprocal),
+    "fp8_queries_scale_by_reciprocal": dict(quantize_queries=_qq_scale_by_reciprocal),
     "cost_counts_qk_only": dict(arithmetic_intensity=_ai_qk_only),
     "layout_lane_order_swapped": dict(k_blocks=_k_blocks_gc_swapped),
 }

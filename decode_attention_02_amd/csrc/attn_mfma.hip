@@ -34,8 +34,8 @@
 // empty buffer resources, which read nothing), so the compiler's wait before
 // a ring slot is consumed leaves the younger slots in flight. The ring loads
 // are non-temporal (each cache byte is read once). At the end the PV waves
-// stage their bf16 results in LDS and all eight waves store whole 512-byte
-// head rows.
+// stage bf16 outputs in LDS and all eight waves store whole 512-byte head
+// rows; fp32 results (split partials, fp32 outputs) are stored directly.
 // The running max is updated lazily: only when a block's max exceeds it by
 // more than 2^8 (log2 units) are O and the row sums rescaled, so p <= 256;
 // the result is the same softmax, normalised by the same reference at the end.
@@ -142,7 +142,6 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // through one L2 at about the same time, and the splits of a sequence
   // share that L2 for their query reads.
   int id = blockIdx.x;
-  if (id == 0 && tid == 0 && a.num_splits > 1) *a.part_tag = a.part_bf16 ? kPartTagBf16 : kPartTagF32;
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int hg = id % kHS;
   const int split = (id / kHS) % a.num_splits;
@@ -271,9 +270,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   };
   auto tokens_in = [&](int n) __attribute__((always_inline)) { return t1 - (blk0 + n) * kBlockTokens; };   // valid tokens of block n (>= 1)
 
-  // bf16 results (outputs, or the partials of a split that holds tokens)
-  // leave through LDS as whole 512-byte head rows (end of the kernel)
-  const bool stage_out = a.num_splits == 1 ? !a.out_f32 : (a.part_bf16 && N > 0);
+  // bf16 outputs leave through LDS as whole 512-byte head rows (end of the
+  // kernel); fp32 outputs and the fp32 split partials are stored directly
+  const bool stage_out = a.num_splits == 1 && !a.out_f32;
 
   // Every wave passes the same barriers: one after staging Q, one per
   // iteration i = 0 .. NU+1 (NU units of BPI blocks), one before the epilogue (and one more before the
@@ -707,7 +706,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
           const int f = 64 * ww + 16 * dt + 4 * g;
           float* dst = a.num_splits == 1
                            ? reinterpret_cast<float*>(a.out) + (static_cast<size_t>(b) * kH + head) * kD + f
-                           : static_cast<float*>(a.part_o) + (row * kH + head) * kD + f;
+                           : a.part_o + (row * kH + head) * kD + f;
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
@@ -723,12 +722,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   }
   if (stage_out) {
     __syncthreads();   // head rows staged by the PV waves
-    // the workgroup's kHW head rows are one contiguous range of the output
-    // (or of this split's partials): 16 bytes per thread per pass
-    uint16_t* dst = a.num_splits == 1
-                        ? static_cast<uint16_t*>(a.out) + (static_cast<size_t>(b) * kH + h0) * kD
-                        : static_cast<uint16_t*>(a.part_o) +
-                              ((static_cast<size_t>(b) * a.num_splits + split) * kH + h0) * kD;
+    // the workgroup's kHW head rows are one contiguous range of the output:
+    // 16 bytes per thread per pass
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(b) * kH + h0) * kD;
     const uint4* stage4 = reinterpret_cast<const uint4*>(&s_lds[0][0]);
 #pragma unroll
     for (int i = tid; i < kHW * 32; i += 512) {

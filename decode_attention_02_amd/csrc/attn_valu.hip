@@ -29,7 +29,6 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
   const int H = a.heads;
   const int HD = H * D;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0 && a.num_splits > 1) *a.part_tag = a.part_bf16 ? kPartTagBf16 : kPartTagF32;
   const int split = blockIdx.x % a.num_splits;
   const int b = blockIdx.x / a.num_splits;          // virtual row (q, partials, out)
   const int ql = a.q_len > 0 ? a.q_len : 1;
@@ -151,8 +150,7 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
     for (int r = 0; r < kMaxPerThread; ++r) {
       const int e = tid + 256 * r;
       if (e < HD) {
-        if (a.part_bf16) static_cast<uint16_t*>(a.part_o)[row * HD + e] = f32_to_bf16(o[r]);
-        else static_cast<float*>(a.part_o)[row * HD + e] = o[r];
+        a.part_o[row * HD + e] = o[r];
       }
     }
     if (tid < H) {

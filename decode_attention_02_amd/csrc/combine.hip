@@ -13,22 +13,14 @@ namespace mfa {
 
 // One workgroup of 256 threads covers 1024/d heads of one sequence; a thread
 // owns 4 consecutive features of one head and reads one float4 per split.
-// Partial o is bf16 (PBF16) or fp32; m and l are fp32.
+// Partials are fp32 (o, m and l).
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); the remap
 // gives each XCD a contiguous range of sequences, the same range whose
 // splits the attention kernel ran there.
-// The workspace's tag word names the element type the attention call wrote
-// part_o in; when it is not the type this launch reads, the output is NaN
-// (a combine called with another out_dtype than the attention call).
-template <bool PBF16>
-__global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict__ part_o,
+__global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
-                                                          const uint32_t* __restrict__ part_tag,
                                                           int S, int H, int d, void* out,
                                                           int out_f32) {
-  // scalar load, issued first and checked only before the stores
-  using cu32 = const __attribute__((address_space(4))) uint32_t;
-  const uint32_t tag = ((cu32*)part_tag)[0];
   const int tpb = d >> 2;                        // threads per head
   const int hpb = 256 / tpb;                     // heads per workgroup
   const int groups = (H + hpb - 1) / hpb;
@@ -55,15 +47,7 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
       ml[j] = in ? *reinterpret_cast<const float2*>(part_ml + ((row0 + s0 + j) * H + h) * 2)
                  : make_float2(-INFINITY, 0.f);
       const size_t po = ((row0 + s0 + j) * H + h) * d + f;
-      if constexpr (PBF16) {
-        const uint2 u = in ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(part_o) + po)
-                           : make_uint2(0u, 0u);
-        o[j] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-      } else {
-        o[j] = in ? *reinterpret_cast<const float4*>(static_cast<const float*>(part_o) + po)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      o[j] = in ? *reinterpret_cast<const float4*>(part_o + po) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float bmax = -INFINITY;
 #pragma unroll
@@ -87,8 +71,7 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
       }
     }
   }
-  float inv = den > 0.f ? 1.0f / den : 0.f;
-  if (tag != (PBF16 ? kPartTagBf16 : kPartTagF32)) inv = __builtin_nanf("");
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
   const size_t oi = (static_cast<size_t>(b) * H + h) * d + f;
   if (out_f32) {
     store_nt(reinterpret_cast<float*>(out) + oi, make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
@@ -100,19 +83,14 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const void* __restrict
   }
 }
 
-hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml,
-                          const uint32_t* part_tag, int B, int H, int d, int num_splits, void* out,
-                          int out_f32, hipStream_t stream) {
+hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
+                          int num_splits, void* out, int out_f32, hipStream_t stream) {
   if (d % 4 || d > 1024) return hipErrorInvalidValue;
   const int hpb = 256 / (d / 4);
   const int groups = (H + hpb - 1) / hpb;
   const dim3 grid(static_cast<unsigned>(B * groups));
-  if (part_bf16)
-    hipLaunchKernelGGL(mfa_combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_ml,
-                       part_tag, num_splits, H, d, out, out_f32);
-  else
-    hipLaunchKernelGGL(mfa_combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_ml,
-                       part_tag, num_splits, H, d, out, out_f32);
+  hipLaunchKernelGGL(mfa_combine_kernel, grid, dim3(256), 0, stream, part_o, part_ml, num_splits,
+                     H, d, out, out_f32);
   return hipGetLastError();
 }
 

@@ -8,12 +8,6 @@
 
 namespace mfa {
 
-// Tag word at the end of the split workspace: the element type of part_o,
-// written by the attention kernels, checked by the combine (which writes NaN
-// when its expected type differs).
-constexpr uint32_t kPartTagBf16 = 0x31464250u;   // "PBF1"
-constexpr uint32_t kPartTagF32 = 0x32334650u;    // "PF32"
-
 // Decode attention arguments (shared by the matrix-core and VALU kernels).
 struct AttnArgs {
   const uint16_t* q;          // bf16 bits or (VALU kernel, f32 q) reinterpret
@@ -34,10 +28,8 @@ struct AttnArgs {
   int kv_f32;                 // VALU kernel: cache dtype (else bf16)
   float sm_scale;             // VALU kernel (natural exp)
   float scale_log2;           // matrix-core kernel: sm_scale * log2(e)
-  void* part_o;               // [B][S][H][d] when num_splits > 1: bf16 or fp32
-  int part_bf16;              // part_o element type: bf16 (1) or fp32 (0)
+  float* part_o;              // [B][S][H][d] fp32 when num_splits > 1
   float* part_ml;             // [B][S][H][2]
-  uint32_t* part_tag;         // the workspace's tag word (num_splits > 1)
   void* out;                  // [B][H][d] when num_splits == 1
   int out_f32;
   // Query tokens per sequence (>= 1). Rows of q, the partials and out are
@@ -55,9 +47,8 @@ struct AttnArgs {
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
 
-hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_ml,
-                          const uint32_t* part_tag, int B, int H, int d, int num_splits, void* out,
-                          int out_f32, hipStream_t stream);
+hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
+                          int num_splits, void* out, int out_f32, hipStream_t stream);
 
 struct AppendArgs {
   const void* k_new;          // [B][n_new][d]

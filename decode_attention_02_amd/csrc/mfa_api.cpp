@@ -121,17 +121,15 @@ mfa_status check_qproj_shape(int B, int hidden, int q_rank, int H, int d, int dt
 }
 
 // ---- attention planning --------------------------------------------------
-// Split workspace: part_o [rows][d] (rows = sequences x splits x heads; room
-// for fp32 even when bf16 is stored) at 0, part_ml fp32 [rows][2] at off_ml,
-// the partial-type tag word at off_tag.
+// Split workspace: part_o fp32 [rows][d] (rows = sequences x splits x
+// heads) at 0, part_ml fp32 [rows][2] at off_ml.
 struct SplitLayout {
-  size_t off_ml, off_tag, total;
+  size_t off_ml, total;
 };
 SplitLayout split_layout(size_t rows, int d) {
   SplitLayout l;
   l.off_ml = round_up(rows * static_cast<size_t>(d) * 4, 256);
-  l.off_tag = round_up(l.off_ml + rows * 2 * 4, 16);
-  l.total = l.off_tag + 16;
+  l.total = l.off_ml + rows * 2 * 4;
   return l;
 }
 
@@ -571,10 +569,8 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.fp8_queries = fp8_queries ? 1 : 0;
   if (num_splits > 1) {
     const SplitLayout l = split_layout(static_cast<size_t>(Bv) * num_splits * H, d);
-    a.part_o = workspace;
-    a.part_bf16 = out_dtype == MFA_BF16;
+    a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + l.off_ml);
-    a.part_tag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + l.off_tag);
   }
   a.out = out;
   a.out_f32 = out_dtype == MFA_F32;
@@ -592,8 +588,8 @@ mfa_status launch_attn(const AttnCall& c, hipStream_t st) {
   hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st) : mfa::launch_decode_valu(a, c.B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
   if (c.num_splits > 1 && c.out) {
-    e = mfa::launch_combine(a.part_o, a.part_bf16, a.part_ml, a.part_tag, c.B, c.H, c.d,
-                            c.num_splits, c.out, a.out_f32, st);
+    e = mfa::launch_combine(a.part_o, a.part_ml, c.B, c.H, c.d, c.num_splits, c.out, a.out_f32,
+                            st);
     if (e != hipSuccess) return MFA_ERR_HIP;
   }
   return MFA_OK;
@@ -690,9 +686,8 @@ mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int
   if (workspace_bytes < mfa_decode_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
   const SplitLayout l = split_layout(static_cast<size_t>(B) * num_splits * H, d);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-  return from_hip(mfa::launch_combine(workspace, out_dtype == MFA_BF16,
-                                      reinterpret_cast<const float*>(ws + l.off_ml),
-                                      reinterpret_cast<const uint32_t*>(ws + l.off_tag), B, H, d,
+  return from_hip(mfa::launch_combine(reinterpret_cast<const float*>(ws),
+                                      reinterpret_cast<const float*>(ws + l.off_ml), B, H, d,
                                       num_splits, out, out_dtype == MFA_F32, as_stream(stream)));
 }
 

@@ -205,18 +205,15 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
  * partials of the long-context case, "Step-3 is Large yet Affordable"
  * summary page, §4 Cost Analysis for LLM Decoding: attention cost grows with
  * context and dominates from 8K on). With R = B*num_splits*H rows:
- *   part_o  [B][num_splits][H][d] unnormalised partial outputs at offset 0
- *           (bf16 when the attention call's out_dtype is MFA_BF16, fp32 when
- *           it is MFA_F32; R*d*4 bytes are reserved either way)
+ *   part_o  fp32 [B][num_splits][H][d] unnormalised partial outputs at
+ *           offset 0
  *   part_ml fp32 [B][num_splits][H][2] at offset round_up(R*d*4, 256): the
  *           running max m in natural-log units of the scaled logits, then
  *           l = sum_t exp(s_t - m)
- *   tag     one uint32 at offset round_up(off_ml + R*8, 16), written by the
- *           attention call: 0x31464250 when part_o is bf16, 0x32334650 when
- *           fp32. mfa_combine checks it against the type its own out_dtype
- *           implies and writes NaN outputs when they differ.
- * Total round_up(off_ml + R*8, 16) + 16 bytes; 0 when num_splits == 1. The
- * caller owns it; the library keeps nothing in it between calls. */
+ * Total round_up(R*d*4, 256) + R*8 bytes; 0 when num_splits == 1. The
+ * partials are fp32 whatever the output type, so mfa_combine may write
+ * either output type. The caller owns the workspace; the library keeps
+ * nothing in it between calls. */
 size_t mfa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 /* The same function under its earlier name. */
 size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
@@ -305,10 +302,9 @@ mfa_status mfa_decode_attn_q8(const void *q, int q_dtype, int B, int q_len, int 
  * every (sequence, head) by log-sum-exp:
  *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.
  * Splits with l_j == 0 (empty) get weight 0; a head whose splits are all
- * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32), which
- * must be the out_dtype the attention call was given (it fixes the type of
- * part_o); otherwise the workspace tag does not match and out is NaN.
- * num_splits >= 2; d in {64, 128, 256}. Host checks as for every call;
+ * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32; the
+ * partials are fp32 either way). num_splits >= 2; d in {64, 128, 256}.
+ * Host checks as for every call;
  * MFA_ERR_WORKSPACE when workspace_bytes is below the required size.
  */
 mfa_status mfa_combine(const void *workspace, size_t workspace_bytes, int B,

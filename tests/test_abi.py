@@ -183,13 +183,10 @@ def test_plan_and_split_workspace(lib):
     assert lib.mfa_decode_plan(0, 64, 256, 10, BF16, ctypes.byref(ns), ctypes.byref(ch)) == SHAPE
     assert lib.mfa_decode_workspace_bytes(4, 64, 256, 1) == 0
     rows = 4 * 32 * 64
-    off_ml = rows * 256 * 4                      # a multiple of 256 already
-    off_tag = -(-(off_ml + rows * 8) // 16) * 16
-    assert lib.mfa_decode_workspace_bytes(4, 64, 256, 32) == off_tag + 16
+    assert lib.mfa_decode_workspace_bytes(4, 64, 256, 32) == rows * 256 * 4 + rows * 2 * 4
     rows = 3 * 5 * 7
     off_ml = -(-rows * 64 * 4 // 256) * 256
-    off_tag = -(-(off_ml + rows * 8) // 16) * 16
-    assert lib.mfa_decode_workspace_bytes(3, 7, 64, 5) == off_tag + 16
+    assert lib.mfa_decode_workspace_bytes(3, 7, 64, 5) == off_ml + rows * 2 * 4
     for args in ((4, 64, 256, 32), (3, 7, 64, 5), (1, 1, 1, 1)):
         assert lib.mfa_split_workspace_bytes(*args) == lib.mfa_decode_workspace_bytes(*args)
     assert lib.mfa_combine(None, 0, 4, 64, 256, 32, P, BF16, None) == NULL

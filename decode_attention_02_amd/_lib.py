@@ -16,10 +16,11 @@ MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
 MFA_WEIGHTS_ROWMAJOR, MFA_WEIGHTS_PACKED = 0, 1
 BLOCK_TOKENS = 64
 MAX_QUERY_TOKENS = 16
+STATIC_SCRATCH = 32 << 20
 ABI_VERSION = 3
 STATUS_NAMES = {0: "MFA_OK", 1: "MFA_ERR_NULL", 2: "MFA_ERR_SHAPE", 3: "MFA_ERR_DTYPE",
                 4: "MFA_ERR_ALIGN", 5: "MFA_ERR_UNSUPPORTED", 6: "MFA_ERR_WORKSPACE",
-                7: "MFA_ERR_HIP"}
+                7: "MFA_ERR_HIP", 8: "MFA_ERR_TOO_LARGE"}
 
 
 class KVCacheDesc(ctypes.Structure):
@@ -78,6 +79,7 @@ SIGNATURES = {
     "mfa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_split_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_decode_attn": (_i, [_p, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p, _i, _p]),
+    "mfa_decode_attn_static": (_i, [_p, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _i, _p]),
     "mfa_decode_attn_multi": (_i, [_p, _i, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p,
                                    _i, _p]),
     "mfa_decode_attn_q8": (_i, [_p, _i, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p,

@@ -297,3 +297,32 @@ def decode_step(args: "_lib.StepArgs", device) -> None:
     alive."""
     lib = _lib.load()
     check("mfa_decode_step", lib.mfa_decode_step(ctypes.byref(args), _stream(device)))
+
+
+def decode_attn_static(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq_len: int,
+                       sm_scale: Optional[float] = None, num_splits: int = 1,
+                       chunk_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                       out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """``decode_attn`` with the split partials in the library's own static
+    scratch (mfa_decode_attn_static): no workspace is passed and the call
+    allocates nothing when ``out`` is given."""
+    lib = _lib.load()
+    B, H, d = q.shape
+    _dev(q, "q")
+    _dev(seq_lens, "seq_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if chunk_tokens is None:
+        per = -(-max(max_seq_len, 1) // num_splits)
+        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    _dev(out, "out")
+    desc = cache.desc()
+    check("mfa_decode_attn_static", lib.mfa_decode_attn_static(
+        _ptr(q), _DTYPES[q.dtype], B, H, ctypes.byref(desc), _ptr(seq_lens), int(max_seq_len),
+        float(sm_scale), int(num_splits), int(chunk_tokens), _ptr(out), _DTYPES[out_dtype],
+        _stream(q.device)))
+    return out

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -174,6 +175,7 @@ const char* mfa_status_str(int s) {
     case MFA_ERR_UNSUPPORTED: return "the library has no kernel for this shape";
     case MFA_ERR_WORKSPACE: return "workspace missing or too small";
     case MFA_ERR_HIP: return "HIP runtime reported a launch failure";
+    case MFA_ERR_TOO_LARGE: return "request needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -607,6 +609,59 @@ mfa_status mfa_decode_attn(const void* q, int q_dtype, int B, int H, const mfa_k
   const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
                                      num_splits, chunk_tokens, workspace, workspace_bytes, out,
                                      out_dtype, &c);
+  if (st != MFA_OK) return st;
+  return launch_attn(c, as_stream(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The split partials of mfa_decode_attn_static. In host code `scratch` only
+// names the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress and is what the kernels are given.
+static __device__ __align__(256) unsigned char scratch[MFA_STATIC_SCRATCH];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+mfa_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MFA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MFA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return MFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfa_status mfa_decode_attn_static(const void* q, int q_dtype, int B, int H,
+                                  const mfa_kv_cache* cache, const int32_t* seq_lens,
+                                  int max_seq_len, float sm_scale, int num_splits,
+                                  int chunk_tokens, void* out, int out_dtype, void* stream) {
+  if (!out) return MFA_ERR_NULL;
+  if (cache && num_splits > 1 && B > 0 && H > 0 &&
+      mfa_decode_workspace_bytes(B, H, cache->head_dim, num_splits) > MFA_STATIC_SCRATCH)
+    return MFA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (num_splits > 1) {
+    const mfa_status ss = scratch_for_current_device(&ws);
+    if (ss != MFA_OK) return ss;
+    ws_bytes = MFA_STATIC_SCRATCH;
+  }
+  AttnCall c;
+  const mfa_status st = prepare_attn(q, q_dtype, B, H, cache, seq_lens, max_seq_len, sm_scale,
+                                     num_splits, chunk_tokens, ws, ws_bytes, out, out_dtype, &c);
   if (st != MFA_OK) return st;
   return launch_attn(c, as_stream(stream));
 }

@@ -99,7 +99,8 @@ typedef enum {
   MFA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned       */
   MFA_ERR_UNSUPPORTED = 5,  /* valid request the library has no kernel for  */
   MFA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required    */
-  MFA_ERR_HIP = 7           /* the HIP runtime reported a launch failure     */
+  MFA_ERR_HIP = 7,          /* the HIP runtime reported a launch failure     */
+  MFA_ERR_TOO_LARGE = 8     /* needs more than the library's static scratch  */
 } mfa_status;
 
 typedef enum {
@@ -245,6 +246,30 @@ mfa_status mfa_decode_attn(const void *q, int q_dtype, int B, int H,
                            int chunk_tokens, void *workspace,
                            size_t workspace_bytes, void *out, int out_dtype,
                            void *stream);
+
+/*
+ * Decode attention that allocates nothing, for callers that cannot allocate
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): mfa_decode_attn with its split partials
+ * in a scratch array the library holds in device memory, MFA_STATIC_SCRATCH
+ * bytes on every GPU it runs on, until the process ends. Arguments as in
+ * mfa_decode_attn, less the workspace; out is required (the library merges
+ * the splits into it). A call whose partials need more than
+ * MFA_STATIC_SCRATCH bytes (mfa_decode_workspace_bytes(B, H, d, num_splits))
+ * returns MFA_ERR_TOO_LARGE and enqueues nothing. All calls on one GPU share
+ * that GPU's scratch: calls that can overlap on one GPU (other streams,
+ * other host threads without ordering) race and give wrong results; calls
+ * ordered on one stream do not. Nothing in the scratch needs clearing
+ * between calls (every split writes its own partials). The first call on a
+ * device looks up that device's scratch address (MFA_ERR_HIP if that
+ * fails).
+ */
+#define MFA_STATIC_SCRATCH (32u << 20)
+mfa_status mfa_decode_attn_static(const void *q, int q_dtype, int B, int H,
+                                  const mfa_kv_cache *cache, const int32_t *seq_lens,
+                                  int max_seq_len, float sm_scale, int num_splits,
+                                  int chunk_tokens, void *out, int out_dtype,
+                                  void *stream);
 
 /*
  * Multi-token decode attention: q_len new tokens per sequence (several

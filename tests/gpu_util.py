@@ -30,6 +30,13 @@ def max_abs(got, want) -> float:
     return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))))
 
 
+def check_bf16_bars(got, want, what: str) -> None:
+    """The bf16 / FP8-KV parity bars: rel-L2 <= 5e-3 and max abs <= 2e-2."""
+    r, m = rel_l2(got, want), max_abs(got, want)
+    say(f"{what}: rel_l2={r:.3e} max_abs={m:.3e}")
+    assert r <= REL_L2_BF16 and m <= MAX_ABS_BF16, (what, r, m)
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

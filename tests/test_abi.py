@@ -194,6 +194,20 @@ def test_plan_and_split_workspace(lib):
     assert lib.mfa_combine(P, 1 << 30, 4, 64, 256, 1, P, BF16, None) == SHAPE
 
 
+def test_static_scratch_refuses_oversize(lib):
+    """mfa_decode_attn_static refuses partials beyond its static scratch on the
+    host, before any HIP call (so it runs without a GPU)."""
+    desc = _lib.KVCacheDesc(k=P, v=P, num_blocks=1 << 20, max_blocks_per_seq=4096, head_dim=256,
+                            dtype=BF16)
+    too_many = 300                      # 2 x 300 splits x 64 KB of partials > 32 MiB
+    assert lib.mfa_decode_workspace_bytes(2, 64, 256, too_many) > 32 << 20
+    rc = lib.mfa_decode_attn_static(P, BF16, 2, 64, ctypes.byref(desc), P, 64 * too_many,
+                                    0.0625, too_many, 64, P, BF16, None)
+    assert rc == 8 and lib.mfa_status_str(8) == b"request needs more than the library's static scratch"
+    assert lib.mfa_decode_attn_static(P, BF16, 2, 64, ctypes.byref(desc), P, 100, 0.0625, 2, 64,
+                                      None, BF16, None) == NULL
+
+
 def _c_layout(struct, fields):
     """sizeof and offsetof of a struct of mfa.h, from a C program built by gcc."""
     import shutil

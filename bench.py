@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3,
                     help="workload index 1..5 (default 3: the largest, paged mixed lengths)")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets cycled (0: auto)")
-    ap.add_argument("--splits", type=int, default=0, help="override split count")
+    ap.add_argument("--splits", type=int, default=-1,
+                    help="override the split count (0: the balanced partition; -1: the plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the pure read-stream reference measurement")
@@ -287,10 +288,11 @@ def main():
         cache = mfa.KVCache(inp["num_blocks"], w.head_dim, w.kv_dtype, inp["max_blocks_per_seq"],
                             block_table=T["block_table"], device=dev, zero=False)
         prefill(cache, T["k_ctx"], T["v_ctx"], inp["ctx_offsets"], inp["prefill_lens"])
-        ns = args.splits or w.num_splits
+        ns = args.splits if args.splits >= 0 else w.num_splits
         packed = w.has_qproj and w.act_dtype == "bf16"
         step = DecodeStep(cache, B, w.heads, maxlen, hidden=w.hidden, q_rank=w.q_rank,
-                          act_dtype=act, num_splits=ns, packed_weights=packed, device=dev)
+                          act_dtype=act, num_splits=ns, packed_weights=packed, device=dev,
+                          seq_lens_host=inp["seq_lens"])
         wts, wkv = None, None
         if w.has_qproj:
             # weights are static: packed once into operand order, like a load step
@@ -323,9 +325,9 @@ def main():
         # positions) and attends with the TQ queries of each, causal among them
         # (TQ = 1 with FP8 queries: the single-token step through the same call)
         ns_m, ch_m = mfa.decode_plan(B * TQ, w.heads, w.head_dim, maxlen, w.kv_dtype)
-        if args.splits:
+        if args.splits >= 0:
             ns_m = args.splits
-            ch_m = -(-(-(-maxlen // ns_m)) // 64) * 64
+            ch_m = mfa.api._chunk(maxlen, ns_m)
         k_m = T["k_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
         v_m = T["v_new"].unsqueeze(1).expand(B, TQ, w.head_dim).contiguous()
         pos_m = (T["seq_lens"] - TQ).to(torch.int32)
@@ -348,7 +350,7 @@ def main():
             attention_multi(i, combine=ns_m == 1)
             return
         step = sets[i % rotate][0]
-        if step.num_splits > 1:
+        if step.num_splits != 1:
             mfa.decode_attn(q, step.cache, T["seq_lens"], step.max_seq_len, step.sm_scale,
                             step.num_splits, step.chunk_tokens, workspace=step.split_ws,
                             combine=False)

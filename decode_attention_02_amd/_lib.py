@@ -76,6 +76,7 @@ SIGNATURES = {
     "mfa_pack_weight": (_i, [_p, _p, _i, _i, _i, _p]),
     "mfa_kv_append": (_i, [_p, _p, _i, _p, _i, _i, _pdesc, _p]),
     "mfa_decode_plan": (_i, [_i, _i, _i, _i, _i, _pi, _pi]),
+    "mfa_decode_plan_lens": (_i, [_i, _i, _i, _p, _i, _pi, _pi]),
     "mfa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_split_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "mfa_decode_attn": (_i, [_p, _i, _i, _i, _pdesc, _p, _i, _f, _i, _i, _p, _sz, _p, _i, _p]),

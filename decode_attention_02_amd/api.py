@@ -146,6 +146,21 @@ def kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
                                              _stream(k_new.device)))
 
 
+def decode_plan_lens(heads: int, head_dim: int, seq_lens, kv_dtype: str):
+    """(num_splits, chunk_tokens) the library picks for these host lengths
+    (mfa_decode_plan_lens): the split plan, or (0, 0) for the balanced
+    partition."""
+    import numpy as np
+    lib = _lib.load()
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    ns, ch = ctypes.c_int(), ctypes.c_int()
+    check("mfa_decode_plan_lens", lib.mfa_decode_plan_lens(
+        len(lens), heads, head_dim, lens.ctypes.data_as(ctypes.c_void_p),
+        {"f32": MFA_F32, "bf16": MFA_BF16, "fp8": MFA_FP8_E4M3}[kv_dtype],
+        ctypes.byref(ns), ctypes.byref(ch)))
+    return ns.value, ch.value
+
+
 def decode_plan(batch: int, heads: int, head_dim: int, max_seq_len: int, kv_dtype: str):
     """(num_splits, chunk_tokens) the library picks (mfa_decode_plan)."""
     lib = _lib.load()
@@ -155,6 +170,17 @@ def decode_plan(batch: int, heads: int, head_dim: int, max_seq_len: int, kv_dtyp
         {"f32": MFA_F32, "bf16": MFA_BF16, "fp8": MFA_FP8_E4M3}[kv_dtype],
         ctypes.byref(ns), ctypes.byref(ch)))
     return ns.value, ch.value
+
+
+BALANCED = 0   # num_splits value of the balanced (equal-work) partition
+
+
+def _chunk(max_seq_len: int, num_splits: int) -> int:
+    """Tokens per split for num_splits splits (0 for the balanced partition)."""
+    if num_splits == BALANCED:
+        return 0
+    per = -(-max(max_seq_len, 1) // num_splits)
+    return -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
 
 
 def decode_workspace_bytes(batch: int, heads: int, head_dim: int, num_splits: int) -> int:
@@ -172,8 +198,10 @@ def decode_attn(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq
                 combine: bool = True) -> Optional[torch.Tensor]:
     """Attention of q [B][H][d] over the cache (mfa_decode_attn).
 
-    With num_splits > 1 and ``combine`` False, only the partials are written
-    to ``workspace`` (run ``combine_splits`` afterwards) and None is returned.
+    num_splits 0 (``BALANCED``) runs the equal-work partition over all the
+    batch's cached blocks. With num_splits != 1 and ``combine`` False, only
+    the partials are written to ``workspace`` (run ``combine_splits``
+    afterwards) and None is returned.
     """
     lib = _lib.load()
     B, H, d = q.shape
@@ -182,13 +210,12 @@ def decode_attn(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, max_seq
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if chunk_tokens is None:
-        per = -(-max(max_seq_len, 1) // num_splits)
-        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+        chunk_tokens = _chunk(max_seq_len, num_splits)
     if out_dtype is None:
         out_dtype = q.dtype
     if out is None and (num_splits == 1 or combine):
         out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
-    if num_splits > 1 and workspace is None:
+    if num_splits != 1 and workspace is None:
         workspace = torch.empty(split_workspace_bytes(B, H, d, num_splits), dtype=torch.uint8,
                                 device=q.device)
     desc = cache.desc()
@@ -219,13 +246,12 @@ def decode_attn_multi(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, m
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if chunk_tokens is None:
-        per = -(-max(max_seq_len, 1) // num_splits)
-        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+        chunk_tokens = _chunk(max_seq_len, num_splits)
     if out_dtype is None:
         out_dtype = q.dtype
     if out is None and (num_splits == 1 or combine):
         out = torch.empty((B, T, H, d), dtype=out_dtype, device=q.device)
-    if num_splits > 1 and workspace is None:
+    if num_splits != 1 and workspace is None:
         workspace = torch.empty(split_workspace_bytes(B * T, H, d, num_splits), dtype=torch.uint8,
                                 device=q.device)
     desc = cache.desc()
@@ -313,8 +339,7 @@ def decode_attn_static(q: torch.Tensor, cache: KVCache, seq_lens: torch.Tensor, 
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if chunk_tokens is None:
-        per = -(-max(max_seq_len, 1) // num_splits)
-        chunk_tokens = -(-per // BLOCK_TOKENS) * BLOCK_TOKENS
+        chunk_tokens = _chunk(max_seq_len, num_splits)
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else q.dtype
     if out is None:

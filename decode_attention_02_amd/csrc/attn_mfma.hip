@@ -63,6 +63,9 @@ namespace {
 constexpr int kH = 64;
 constexpr int kD = 256;
 constexpr float kLazy = 8.0f;           // rescale only when the max grows by > 2^8
+// balanced partition: extra cost of a row start, in quarter blocks (a piece
+// that ends inside a walk stalls its workgroup for about 1.5 blocks' time)
+constexpr int kBalRowCost = 6;
 
 template <bool FP8>
 struct Cfg {
@@ -111,10 +114,20 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
 // HT: 16-head tiles per workgroup (4: all 64 heads; 2: half of them, two
 // workgroups per (sequence, split) reading the same K/V blocks).
-template <bool FP8, int RK, int RV, int HT, bool Q8 = false, int BPI = 1>
+// BAL: the balanced partition (num_splits == 0). The rows' 64-token blocks,
+// concatenated in row order, are cut into gridDim.x equal ranges, one per
+// workgroup (fewer when there are fewer blocks than workgroups). A workgroup
+// walks its range across row boundaries: each row it touches is a "piece"
+// with its own partial (o, m, l) in slot (workgroup + row). At the first
+// block of a new piece the QK waves switch Q (loaded into registers one
+// piece ahead) behind one extra barrier that both roles pass, and the PV
+// waves write out the finished piece's o, then its (m, l) one iteration
+// later, once the four PV waves' row sums have met in LDS.
+template <bool FP8, int RK, int RV, int HT, bool Q8 = false, int BPI = 1, bool BAL = false>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   static_assert(!Q8 || FP8, "FP8 queries run against FP8 caches");
   static_assert(BPI == 1 || (BPI == 2 && !Q8), "two blocks per iteration: plain FP8 and bf16 only");
+  static_assert(!BAL || (BPI == 1 && HT == 4 && !Q8), "balanced walk: one block per unit, 64 heads");
   using C = Cfg<FP8>;
   constexpr int kHW = 16 * HT;                                          // heads of this workgroup
   constexpr int kHS = kH / kHW;                                         // workgroups per split
@@ -129,6 +142,15 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float red[2][kHW * 4];        // block max [head][QK wave]
   __shared__ __attribute__((aligned(16))) uint4 vs_lds[2][BPI * 16];    // FP8 V scales by (block, QK wave, row)
   __shared__ __attribute__((aligned(16))) float lred[kHW * 4];          // row sums [head][PV wave]
+  // balanced walk: prefix sums of the rows' block counts, row lengths, the
+  // scan's per-wave sums (+ the first row), and the row sums of pieces
+  // finished inside the walk, by piece parity
+  __shared__ int bal_pfx[BAL ? kBalancedMaxRows + 1 : 1];
+  __shared__ int bal_len[BAL ? kBalancedMaxRows : 1];
+  __shared__ int bal_cpfx[BAL ? kBalancedMaxRows + 1 : 1];
+  __shared__ int bal_rc[BAL ? kBalancedMaxRows : 1];
+  __shared__ int bal_wsum[20];
+  __shared__ __attribute__((aligned(16))) float lred2[2][BAL ? kHW * 4 : 4];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: the role branches below are uniform per wave
@@ -143,21 +165,169 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // share that L2 for their query reads.
   int id = blockIdx.x;
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-  const int hg = id % kHS;
-  const int split = (id / kHS) % a.num_splits;
-  const int b = id / kHS / a.num_splits;                                // virtual row (q, partials, out)
-  const int h0 = hg * kHW;                                              // first head
   const int ql = a.q_len > 0 ? a.q_len : 1;
-  const int bs = b / ql;                                                // its sequence (cache, lengths)
-  const int jq = b - bs * ql;                                           // its query token
-
-  // query token jq sees the sequence up to and including itself
-  int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[bs] - (ql - 1 - jq);
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int t0 = split * a.chunk_tokens;
-  const int t1 = min(t0 + a.chunk_tokens, L);
-  const int blk0 = t0 >> 6;
-  const int N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;   // blocks to walk
+  int hg = 0, split = 0, b = 0, bs = 0, t1 = 0, blk0 = 0, N = 0;
+  int lo = 0, hi = 0;                   // balanced walk: the workgroup's global block range
+  if constexpr (BAL) {
+    // rows 2 tid, 2 tid + 1: lengths (clamped like the split path), block
+    // counts and costs; exclusive scans of both over all rows.
+    // The partition cuts the rows' concatenated cost evenly: a block costs
+    // U units and an interior row start kBalRowCost more (the price of a
+    // piece that ends inside a walk: its partial stores and the Q switch),
+    // so a workgroup that crosses row starts gets fewer blocks. With fewer
+    // than 4 blocks per workgroup the cost is the block count alone (U = 1,
+    // no row-start charge) and only min(blocks, workgroups) workgroups run.
+    const int rows = a.bal_rows;
+    int nb2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * tid + e;
+      int Lr = 0;
+      if (r < rows) {
+        const int sq = r / ql;
+        Lr = a.seq_lens[sq] - (ql - 1 - (r - sq * ql));
+        Lr = Lr < 0 ? 0 : (Lr > a.max_seq_len ? a.max_seq_len : Lr);
+        bal_len[r] = Lr;
+      }
+      nb2[e] = (Lr + kBlockTokens - 1) >> 6;
+    }
+    // block counts: wave-inclusive scan; wave totals in bal_wsum[0..7]
+    const int s2 = nb2[0] + nb2[1];
+    int inc = s2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) bal_wsum[w] = inc;
+    __syncthreads();
+    int wpre = 0, NB = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int v = bal_wsum[k];
+      wpre += k < w ? v : 0;
+      NB += v;
+    }
+    NB = __builtin_amdgcn_readfirstlane(NB);
+    const int G = static_cast<int>(gridDim.x);
+    const bool weighted = NB >= 4 * G;
+    const int U = weighted ? 4 : 1;                  // cost of a block
+    const int RC = weighted ? kBalRowCost : 0;       // extra cost of an interior row start
+    const int Geff = NB < G ? NB : G;                // every workgroup below Geff gets >= 1 block
+    // A row start is interior when it is not one of the plain partition's
+    // cuts floor(v NB / Geff): only there does a piece end inside a walk
+    // (uniform rows that line up with the cuts are not charged).
+    const int ex = wpre + inc - s2;                  // first block of row 2 tid
+    auto interior = [&](int st) {
+      const unsigned v = (static_cast<unsigned>(st) * Geff + NB - 1) / NB;
+      return !(v < static_cast<unsigned>(Geff) && v * NB / Geff == static_cast<unsigned>(st));
+    };
+    const int ch0 = nb2[0] > 0 && interior(ex), ch1 = nb2[1] > 0 && interior(ex + nb2[0]);
+    const int c2 = ch0 + ch1;
+    int inc_c = c2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc_c, off);
+      if (lane >= off) inc_c += t;
+    }
+    if (lane == 63) bal_wsum[8 + w] = inc_c;
+    __syncthreads();
+    int wpre_c = 0, NC = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int v = bal_wsum[8 + k];
+      wpre_c += k < w ? v : 0;
+      NC += v;
+    }
+    NC = __builtin_amdgcn_readfirstlane(NC);
+    const int TC = U * NB + RC * NC;                 // total cost
+    {
+      const int ex_c = wpre_c + inc_c - c2;
+      const int r0 = 2 * tid, r1 = r0 + 1;
+      if (r0 < rows) {
+        bal_pfx[r0] = ex;
+        bal_cpfx[r0] = U * ex + RC * ex_c;
+        bal_rc[r0] = RC * ch0;
+      }
+      if (r1 < rows) {
+        bal_pfx[r1] = ex + nb2[0];
+        bal_cpfx[r1] = U * (ex + nb2[0]) + RC * (ex_c + ch0);
+        bal_rc[r1] = RC * ch1;
+      }
+      if (tid == 0) {
+        bal_pfx[rows] = NB;
+        bal_cpfx[rows] = TC;
+      }
+    }
+    __syncthreads();   // prefix sums complete
+    // the workgroup whose cost range [floor(w TC / Geff), floor((w+1) TC / Geff))
+    // holds cost position x (32-bit products: the host bounds NB by 2^21)
+    auto wg_of = [&](int x) {
+      int v = static_cast<int>(static_cast<unsigned>(x) * Geff / TC);
+      if (static_cast<unsigned>(v + 1) * TC / Geff <= static_cast<unsigned>(x)) ++v;
+      return v;
+    };
+    // block j of a nonempty row r starts at cost position cpfx[r] + rc[r] + U j;
+    // the workgroup's blocks are those starting inside its cost range
+    // (first slot, slot count) of this workgroup's share of the rows
+    {
+      const int r = id * rows / G + tid;
+      const int rend = (id + 1) * rows / G;
+      if (r < rend) {
+        const int nb = bal_pfx[r + 1] - bal_pfx[r];
+        int2 m = make_int2(0, 0);
+        if (nb > 0) {
+          const int c0 = bal_cpfx[r] + bal_rc[r];
+          const int wf = wg_of(c0), wl = wg_of(c0 + U * (nb - 1));
+          m = make_int2(wf + r, wl - wf + 1);
+        }
+        reinterpret_cast<int2*>(a.bal_meta)[r] = m;
+      }
+    }
+    if (id >= Geff) return;              // no blocks for this workgroup
+    // first block at or after cost position cut: in the nonempty row r with
+    // cpfx[r] - U < cut <= its last block start, block max(0, ceil((cut -
+    // cpfx[r] - rc[r]) / U))
+    const int lo_c = static_cast<int>(static_cast<unsigned>(id) * TC / Geff);
+    const int hi_c = static_cast<int>(static_cast<unsigned>(id + 1) * TC / Geff);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * tid + e;
+      if (r < rows) {
+        const int nb = bal_pfx[r + 1] - bal_pfx[r];
+        const int c = bal_cpfx[r], rc = bal_rc[r];
+        const int last = c + rc + U * (nb - 1);
+        if (nb > 0 && c - U < lo_c && lo_c <= last) {
+          const int j = lo_c <= c + rc ? 0 : (lo_c - c - rc + U - 1) / U;
+          bal_wsum[16] = r;
+          bal_wsum[17] = bal_pfx[r] + j;
+        }
+        if (nb > 0 && id + 1 < Geff && c - U < hi_c && hi_c <= last) {
+          const int j = hi_c <= c + rc ? 0 : (hi_c - c - rc + U - 1) / U;
+          bal_wsum[18] = bal_pfx[r] + j;
+        }
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(bal_wsum[16]);
+    lo = __builtin_amdgcn_readfirstlane(bal_wsum[17]);
+    hi = id + 1 < Geff ? __builtin_amdgcn_readfirstlane(bal_wsum[18]) : NB;
+    N = hi - lo;
+  } else {
+    hg = id % kHS;
+    split = (id / kHS) % a.num_splits;
+    b = id / kHS / a.num_splits;                                        // virtual row (q, partials, out)
+    bs = b / ql;                                                        // its sequence (cache, lengths)
+    const int jq = b - bs * ql;                                         // its query token
+    // query token jq sees the sequence up to and including itself
+    int L = ((const __attribute__((address_space(4))) int*)a.seq_lens)[bs] - (ql - 1 - jq);
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    const int t0 = split * a.chunk_tokens;
+    t1 = min(t0 + a.chunk_tokens, L);
+    blk0 = t0 >> 6;
+    N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;            // blocks to walk
+  }
+  const int h0 = hg * kHW;                                              // first head
   // iterations walk units of BPI consecutive blocks (a unit's second block
   // past the walk reads nothing and is masked out)
   const int NU = (N + BPI - 1) / BPI;
@@ -176,16 +346,16 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   constexpr int kTPH = 256 / kHW;
   constexpr int kDPT = kD / kTPH;
   static_assert(kDPT == 8 * kQLoads, "Q8 staging: one 16-byte load per 8 dims");
-  auto q_src = [&](int r) __attribute__((always_inline)) -> const uint4* {
+  auto q_src = [&](int row, int r) __attribute__((always_inline)) -> const uint4* {
     if constexpr (Q8) {
-      return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
+      return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(row) * kH * kD +
                                             (h0 + tid / kTPH) * kD + (tid % kTPH) * kDPT + 8 * r);
     }
     const int idx = tid + 256 * r;
     const int ln = idx & 63, blk = idx >> 6;
     const int ht = blk >> 3, s = blk & 7;
     const int gg = ln >> 4, cc = ln & 15;
-    return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(b) * kH * kD +
+    return reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(row) * kH * kD +
                                           (h0 + ht * 16 + cc) * kD + qk_dim<FP8>(s, gg));
   };
   // Q8: this thread's kDPT bf16 values of head h0 + tid/kTPH -> e4m3 codes
@@ -234,8 +404,10 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       // named registers, not an array: an array held across the scheduling
       // barriers below would be left in scratch memory
       uint4 q0, q1, q2, q3, q4, q5, q6, q7;
-      q0 = *q_src(0); q1 = *q_src(1); q2 = *q_src(2); q3 = *q_src(3);
-      if constexpr (kQLoads == 8) { q4 = *q_src(4); q5 = *q_src(5); q6 = *q_src(6); q7 = *q_src(7); }
+      q0 = *q_src(b, 0); q1 = *q_src(b, 1); q2 = *q_src(b, 2); q3 = *q_src(b, 3);
+      if constexpr (kQLoads == 8) {
+        q4 = *q_src(b, 4); q5 = *q_src(b, 5); q6 = *q_src(b, 6); q7 = *q_src(b, 7);
+      }
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
       __builtin_amdgcn_sched_barrier(0);
@@ -270,9 +442,67 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   };
   auto tokens_in = [&](int n) __attribute__((always_inline)) { return t1 - (blk0 + n) * kBlockTokens; };   // valid tokens of block n (>= 1)
 
+  // Balanced walk: a cursor over the rows of the workgroup's range. For the
+  // row r holding global block x: rb = its first global block, gs / ge = the
+  // part of its blocks inside [lo, hi), L = its length, sq = its sequence.
+  struct Cur {
+    int r, rb, gs, ge, L, sq;
+  };
+  auto cur_set = [&](Cur& cu, int r) __attribute__((always_inline)) {
+    cu.r = r;
+    cu.rb = __builtin_amdgcn_readfirstlane(bal_pfx[r]);
+    cu.ge = min(__builtin_amdgcn_readfirstlane(bal_pfx[r + 1]), hi);
+    cu.gs = max(cu.rb, lo);
+    cu.L = __builtin_amdgcn_readfirstlane(bal_len[r]);
+    cu.sq = r / ql;
+  };
+  // moves the cursor forward to the row holding global block x (< hi)
+  auto cur_at = [&](Cur& cu, int x) __attribute__((always_inline)) {
+    while (x >= cu.ge) cur_set(cu, cu.r + 1);
+  };
+  auto phys_bal = [&](const Cur& cu, int x) __attribute__((always_inline)) -> size_t {
+    const int j = x - cu.rb;
+    int pid = a.block_table ? ((cint*)a.block_table)[static_cast<size_t>(cu.sq) * a.max_blocks_per_seq + j]
+                            : cu.sq * a.max_blocks_per_seq + j;
+    pid = pid < 0 ? 0 : (pid >= a.num_blocks ? a.num_blocks - 1 : pid);
+    return static_cast<size_t>(pid);
+  };
+  auto lim_bal = [&](const Cur& cu, int x) __attribute__((always_inline)) {
+    return min(kBlockTokens, cu.L - (x - cu.rb) * kBlockTokens);
+  };
+  auto cur_init = [&](Cur& cu) __attribute__((always_inline)) {
+    if constexpr (BAL) cur_set(cu, b);
+  };
+  // Paged caches: physical ids of walk blocks base .. base + 63, one per lane,
+  // fetched by one gather; issuing a block then takes its id with readlane
+  // instead of waiting on a scalar load of the table in every iteration.
+  auto bt_window = [&](int base) __attribute__((always_inline)) -> int {
+    const int n = base + lane;
+    int pid = 0;
+    if (n < N) {
+      int sq, j;
+      if constexpr (BAL) {
+        const int x = lo + n;
+        int r = b;
+        while (x >= bal_pfx[r + 1]) ++r;
+        j = x - bal_pfx[r];
+        sq = r / ql;
+      } else {
+        sq = bs;
+        j = blk0 + n;
+      }
+      pid = a.block_table[static_cast<size_t>(sq) * a.max_blocks_per_seq + j];
+      pid = pid < 0 ? 0 : (pid >= a.num_blocks ? a.num_blocks - 1 : pid);
+    }
+    return pid;
+  };
+  const bool paged = a.block_table != nullptr;
+
+  // partial results (split or balanced) or the final output
+  const bool partial = BAL || a.num_splits > 1;
   // bf16 outputs leave through LDS as whole 512-byte head rows (end of the
   // kernel); fp32 outputs and the fp32 split partials are stored directly
-  const bool stage_out = a.num_splits == 1 && !a.out_f32;
+  const bool stage_out = !partial && !a.out_f32;
 
   // Every wave passes the same barriers: one after staging Q, one per
   // iteration i = 0 .. NU+1 (NU units of BPI blocks), one before the epilogue (and one more before the
@@ -282,6 +512,11 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     constexpr int R = RK;
     constexpr int U = unroll_for(RK);
     uint4 ring[R][BPI][C::kSlot];        // K units of 16 tokens (+ FP8 K, V scales) per block
+    Cur kc, sc;                          // balanced walk: K issue and scores cursors
+    cur_init(kc);
+    cur_init(sc);
+    int wbase = 0;                       // paged: the block-id window of the K issue
+    int win = paged ? bt_window(0) : 0;
     // Loads iteration unit u (blocks BPI*u ..) into a ring slot; blocks past
     // the walk issue the same number of loads through empty resources, which
     // return zeros and read nothing, so the loop's load count is the same on
@@ -292,7 +527,23 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       for (int bb = 0; bb < BPI; ++bb) {
       const int n = u * BPI + bb;
       const bool real = n < N;
-      const size_t pb = phys(real ? n : 0);
+      size_t pb = 0;
+      if (paged) {
+        if (real) {
+          if (n - wbase >= kWave) {
+            wbase += kWave;
+            win = bt_window(wbase);
+          }
+          pb = static_cast<size_t>(__builtin_amdgcn_readlane(win, n - wbase));
+        }
+      } else if constexpr (BAL) {
+        if (real) {
+          cur_at(kc, lo + n);
+          pb = phys_bal(kc, lo + n);
+        }
+      } else {
+        pb = phys(real ? n : 0);
+      }
       // units (tg = ww, s): K[16ww + c][..], 1 KB contiguous per load
       const auto rk = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(a.k) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
@@ -378,7 +629,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       });
 #pragma unroll
       for (int bb = 0; bb < BPI; ++bb) {
-        const int lim = tokens_in(u * BPI + bb);
+        int lim;
+        if constexpr (BAL) lim = lim_bal(sc, lo + u);
+        else lim = tokens_in(u * BPI + bb);
         const int tt0 = 16 * ww + 4 * g;         // this lane's first token of the block
         if constexpr (FP8) {
           const uint4 k4 = ring[slot][bb][4];
@@ -451,6 +704,38 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         qsr[ht] = qs_lds[16 * ht + c];
       }
     }
+    // balanced walk: Q of the next piece, in registers until its first block
+    uint4 qn0, qn1, qn2, qn3, qn4, qn5, qn6, qn7;
+    // before S of unit i: at the first block of a piece after the first, Q
+    // of the piece goes to LDS (every QK wave has finished reading the old Q
+    // at the previous barrier) behind the extra barrier both roles pass.
+    // Returns whether unit i starts a piece.
+    auto piece_start = [&](int i) __attribute__((always_inline)) -> bool {
+      if constexpr (BAL) {
+        cur_at(sc, lo + i);
+        const bool first = lo + i == sc.gs;
+        if (first && i > 0) {
+          q_lds[tid] = qn0; q_lds[tid + 256] = qn1; q_lds[tid + 512] = qn2; q_lds[tid + 768] = qn3;
+          q_lds[tid + 1024] = qn4; q_lds[tid + 1280] = qn5; q_lds[tid + 1536] = qn6;
+          q_lds[tid + 1792] = qn7;
+          __syncthreads();
+        }
+        return first;
+      }
+      return false;
+    };
+    // after S of the first unit of a piece, before the ring loads: Q of the
+    // piece after it (if any) into registers
+    auto prefetch_q = [&](bool first) __attribute__((always_inline)) {
+      if constexpr (BAL) {
+        if (first && sc.ge < hi) {
+          Cur nc = sc;
+          cur_at(nc, sc.ge);
+          qn0 = *q_src(nc.r, 0); qn1 = *q_src(nc.r, 1); qn2 = *q_src(nc.r, 2); qn3 = *q_src(nc.r, 3);
+          qn4 = *q_src(nc.r, 4); qn5 = *q_src(nc.r, 5); qn6 = *q_src(nc.r, 6); qn7 = *q_src(nc.r, 7);
+        }
+      }
+    };
     // iterations i = 0 .. NU+1, S(unit i) for i < NU; groups of U keep ring slots
     // and parities static (i = base + r, base a multiple of U)
     int base = 0;
@@ -459,7 +744,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         constexpr int r = decltype(rc)::value;
         constexpr int slot = r % R, par = r & 1;
         const int i = base + r;
+        const bool first = piece_start(i);
         scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
+        prefetch_q(first);
         issue(std::integral_constant<int, slot>{}, i + R);
         __syncthreads();
       });
@@ -471,7 +758,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       const int i = base + r;
       if (i <= NU + 1) {
         if (i < NU) {
+          const bool first = piece_start(i);
           scores(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, i);
+          prefetch_q(first);
           issue(std::integral_constant<int, slot>{}, i + R);
         }
         __syncthreads();
@@ -496,13 +785,35 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -INFINITY; l_run[ht] = 0.f; }
     uint4 ring[R][BPI][C::kLoads];
+    Cur vc, bc, pc;        // balanced walk: V issue, piece-start and P.V cursors
+    cur_init(vc);
+    cur_init(bc);
+    cur_init(pc);
+    int wbase = 0;         // paged: the block-id window of the V issue
+    int win = paged ? bt_window(0) : 0;
     auto issue = [&](auto slot_c, int u) __attribute__((always_inline)) {   // as for K
       constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
       for (int bb = 0; bb < BPI; ++bb) {
         const int n = u * BPI + bb;
         const bool real = n < N;
-        const size_t pb = phys(real ? n : 0);
+        size_t pb = 0;
+        if (paged) {
+          if (real) {
+            if (n - wbase >= kWave) {
+              wbase += kWave;
+              win = bt_window(wbase);
+            }
+            pb = static_cast<size_t>(__builtin_amdgcn_readlane(win, n - wbase));
+          }
+        } else if constexpr (BAL) {
+          if (real) {
+            cur_at(vc, lo + n);
+            pb = phys_bal(vc, lo + n);
+          }
+        } else {
+          pb = phys(real ? n : 0);
+        }
         // bf16 units (fg = 4ww + s/2, ks = s%2); FP8 units fg = 4ww + s
         const auto rv = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(a.v) + pb * C::kBlockBytes, 0, real ? C::kBlockBytes : 0, kRsrcFlags);
@@ -518,7 +829,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       constexpr int par = decltype(par_c)::value;
 #pragma unroll
       for (int bb = 0; bb < BPI; ++bb) {
-      const int lim = tokens_in(u * BPI + bb);
+      int lim;
+      if constexpr (BAL) {
+        cur_at(pc, lo + u);
+        lim = lim_bal(pc, lo + u);
+      } else {
+        lim = tokens_in(u * BPI + bb);
+      }
       if (lim < kBlockTokens) {
         // tokens past the end: zero their V so 0 * (stale data) cannot reach O
         static_for<0, C::kLoads>([&](auto sc) {
@@ -636,9 +953,70 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
     };
 
+    // balanced walk: a piece that ends inside the walk is written out after
+    // its last P.V: o from the accumulators (fp32, unnormalised), this wave's
+    // row-sum share to lred2[parity]; wave 4 writes (m, l) in the next
+    // iteration, after the barrier, from the four shares and the saved max
+    float m_done[HT];
+    bool ml_pending = false;
+    int ml_slot = 0, ml_par = 0, piece_par = 0;
+    auto finish_piece = [&](int row) __attribute__((always_inline)) {
+      const size_t slot = static_cast<size_t>(id + row);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const f32x4_t v = acc[dt][ht];
+          float* dst = a.part_o + (slot * kH + 16 * ht + c) * kD + 64 * ww + 16 * dt + 4 * g;
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const float l = rows4_sum(l_run[ht]);
+        if (g == 0) lred2[piece_par][(ht * 16 + c) * 4 + ww] = l;
+        m_done[ht] = m_run[ht];
+        m_run[ht] = -INFINITY;
+        l_run[ht] = 0.f;
+      }
+      ml_pending = true;
+      ml_slot = static_cast<int>(slot);
+      ml_par = piece_par;
+      piece_par ^= 1;
+    };
+    auto write_pending_ml = [&]() __attribute__((always_inline)) {
+      if (ml_pending) {
+        if (ww == 0 && g == 0) {
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const float4 r4 = reinterpret_cast<const float4*>(lred2[ml_par])[ht * 16 + c];
+            float2 ml;
+            ml.x = m_done[ht] * kLn2;
+            ml.y = (r4.x + r4.y) + (r4.z + r4.w);
+            store_nt(a.part_ml + (static_cast<size_t>(ml_slot) * kH + 16 * ht + c) * 2, ml);
+          }
+        }
+        ml_pending = false;
+      }
+    };
+    // the extra barrier of iteration i when unit i starts a piece (i > 0)
+    auto piece_barrier = [&](int i) __attribute__((always_inline)) {
+      if constexpr (BAL) {
+        if (i < NU) {
+          cur_at(bc, lo + i);
+          if (lo + i == bc.gs) __syncthreads();
+        }
+      }
+    };
+    // P.V of unit n done: finish its piece if the walk goes on past it
+    auto after_pv = [&](int n) __attribute__((always_inline)) {
+      if constexpr (BAL) {
+        if (n + 1 < NU && lo + n == pc.ge - 1) finish_piece(pc.r);
+      }
+    };
+
     __syncthreads();   // Q staged
     prologue_pv(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // iteration 0 (S of unit 0 on the QK waves)
+    piece_barrier(1);
     if (NU > 0) softmax(std::integral_constant<int, 0>{});
     __syncthreads();   // iteration 1
     // iteration n + 2: P.V of unit n, then the softmax of unit n + 1
@@ -648,8 +1026,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         constexpr int r = decltype(rc)::value;
         constexpr int slot = r % R, par = r & 1;
         const int n = nb + r;
+        if constexpr (BAL) {
+          write_pending_ml();
+          piece_barrier(n + 2);
+        }
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
+        after_pv(n);
         if (n + 1 < NU) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       });
@@ -659,8 +1042,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       constexpr int slot = r % R, par = r & 1;
       const int n = nb + r;
       if (n < NU) {
+        if constexpr (BAL) {
+          write_pending_ml();
+          piece_barrier(n + 2);
+        }
         pv(std::integral_constant<int, slot>{}, std::integral_constant<int, par>{}, n);
         issue(std::integral_constant<int, slot>{}, n + R);
+        after_pv(n);
         if (n + 1 < NU) softmax(std::integral_constant<int, par ^ 1>{});
         __syncthreads();
       }
@@ -686,11 +1074,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // heads of a store land in 16 different bank groups); fp32 results are
     // stored directly and merge in L2.
     uint2* stage2 = reinterpret_cast<uint2*>(&s_lds[0][0]);
-    const bool has_o = a.num_splits == 1 || N > 0;   // an empty split writes only (m, l)
-    const size_t row = static_cast<size_t>(b) * a.num_splits + split;
+    const bool has_o = !partial || N > 0;   // an empty split writes only (m, l)
+    // the partial slot: (row, split), or (workgroup + row of the last piece)
+    const size_t row = BAL ? static_cast<size_t>(id + pc.r)
+                           : static_cast<size_t>(b) * a.num_splits + split;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const float inv = a.num_splits == 1 ? (lsum[ht] > 0.f ? 1.0f / lsum[ht] : 0.f) : 1.0f;
+      const float inv = !partial ? (lsum[ht] > 0.f ? 1.0f / lsum[ht] : 0.f) : 1.0f;
       const int hl = ht * 16 + c, head = h0 + hl;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -704,7 +1094,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
           stage2[(hl * 32 + (j ^ (hl & 31))) * 2 + (g & 1)] = pk;
         } else {
           const int f = 64 * ww + 16 * dt + 4 * g;
-          float* dst = a.num_splits == 1
+          float* dst = !partial
                            ? reinterpret_cast<float*>(a.out) + (static_cast<size_t>(b) * kH + head) * kD + f
                            : a.part_o + (row * kH + head) * kD + f;
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
@@ -712,7 +1102,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
       // (m, l) of every split, empty ones as (-inf, 0): the combine gives
       // those no weight and never uses their o
-      if (a.num_splits > 1 && ww == 0 && g == 0) {
+      if (partial && ww == 0 && g == 0) {
         float2 ml;
         ml.x = mh[ht] * kLn2;     // natural-log units of the scaled logits
         ml.y = lsum[ht];
@@ -739,6 +1129,13 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
   // workgroup per compute unit (256), and only when the XCD remap keeps both
   // groups of a split on one XCD (pairs a multiple of 8): they then read the
   // K/V blocks once from HBM and twice from that XCD's L2.
+  if (a.num_splits == 0) {
+    // balanced partition: one workgroup per compute unit
+    const dim3 grid(kBalancedWorkgroups), block(512);
+    if (fp8) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4, false, 1, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, 4, false, 1, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   const long long pairs = static_cast<long long>(B) * a.num_splits;
   const bool half = pairs * 2 <= 256 && pairs % 8 == 0;
   const dim3 grid(static_cast<unsigned>(pairs * (half ? 2 : 1))), block(512);

@@ -13,12 +13,20 @@ namespace mfa {
 
 // One workgroup of 256 threads covers 1024/d heads of one sequence; a thread
 // owns 4 consecutive features of one head and reads one float4 per split.
-// Partials are fp32 (o, m and l).
+// Partials are fp32 (o, m and l). Row b's partials are the S slots from
+// b * S on, or, with meta (the balanced partition), meta[b] = (first slot,
+// slot count).
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); the remap
 // gives each XCD a contiguous range of sequences, the same range whose
 // splits the attention kernel ran there.
+// kBatch partials are loaded at once per batch; its registers (6 per
+// partial) bound the occupancy, so rows with few partials (the balanced
+// partition's 1..3, short split plans) use batches of 4, which fit every
+// workgroup of the grid on the chip at once.
+template <int kBatch>
 __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
+                                                          const int* __restrict__ meta,
                                                           int S, int H, int d, void* out,
                                                           int out_f32) {
   const int tpb = d >> 2;                        // threads per head
@@ -30,12 +38,16 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
   const int h = (id % groups) * hpb + threadIdx.x / tpb;
   const int f = (threadIdx.x % tpb) * 4;
   if (h >= H) return;
-  const size_t row0 = static_cast<size_t>(b) * S;
-  // One pass: each batch of up to 16 splits is loaded at once (every split's
+  size_t row0 = static_cast<size_t>(b) * S;
+  if (meta) {
+    using cint = const __attribute__((address_space(4))) int;
+    row0 = static_cast<size_t>(((cint*)meta)[2 * b]);
+    S = ((cint*)meta)[2 * b + 1];
+  }
+  // One pass: each batch of up to kBatch splits is loaded at once (every split's
   // partials are valid memory, empty ones too), then merged against a running
   // max; when a batch raises the max, the sums so far are rescaled by
   // exp(old - new), the same identity that merges the splits themselves.
-  constexpr int kBatch = 16;
   float mrun = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < S; s0 += kBatch) {
@@ -83,14 +95,19 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const float* __restric
   }
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
-                          int num_splits, void* out, int out_f32, hipStream_t stream) {
+hipError_t launch_combine(const float* part_o, const float* part_ml, const int* meta, int B,
+                          int H, int d, int num_splits, void* out, int out_f32,
+                          hipStream_t stream) {
   if (d % 4 || d > 1024) return hipErrorInvalidValue;
   const int hpb = 256 / (d / 4);
   const int groups = (H + hpb - 1) / hpb;
   const dim3 grid(static_cast<unsigned>(B * groups));
-  hipLaunchKernelGGL(mfa_combine_kernel, grid, dim3(256), 0, stream, part_o, part_ml, num_splits,
-                     H, d, out, out_f32);
+  if (meta || num_splits <= 4)
+    hipLaunchKernelGGL(mfa_combine_kernel<4>, grid, dim3(256), 0, stream, part_o, part_ml, meta,
+                       num_splits, H, d, out, out_f32);
+  else
+    hipLaunchKernelGGL(mfa_combine_kernel<16>, grid, dim3(256), 0, stream, part_o, part_ml, meta,
+                       num_splits, H, d, out, out_f32);
   return hipGetLastError();
 }
 

@@ -8,6 +8,13 @@
 
 namespace mfa {
 
+// Equal-work ("balanced") partition of the matrix-core attention: the grid
+// is kBalancedWorkgroups workgroups, which split the concatenated 64-token
+// blocks of all rows (at most kBalancedMaxRows) evenly; workgroup w writes
+// one partial per row it touches, in partial slot w + row.
+constexpr int kBalancedWorkgroups = 256;
+constexpr int kBalancedMaxRows = 1024;
+
 // Decode attention arguments (shared by the matrix-core and VALU kernels).
 struct AttnArgs {
   const uint16_t* q;          // bf16 bits or (VALU kernel, f32 q) reinterpret
@@ -30,6 +37,10 @@ struct AttnArgs {
   float scale_log2;           // matrix-core kernel: sm_scale * log2(e)
   float* part_o;              // [B][S][H][d] fp32 when num_splits > 1
   float* part_ml;             // [B][S][H][2]
+  // balanced partition (num_splits == 0): part_o / part_ml hold
+  // kBalancedWorkgroups + B slots; bal_meta[row] = (first slot, slot count)
+  int* bal_meta;
+  int bal_rows;               // rows of the balanced walk (virtual rows)
   void* out;                  // [B][H][d] when num_splits == 1
   int out_f32;
   // Query tokens per sequence (>= 1). Rows of q, the partials and out are
@@ -47,8 +58,11 @@ struct AttnArgs {
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, int B, int H, int d,
-                          int num_splits, void* out, int out_f32, hipStream_t stream);
+// meta (nullable): per row (first partial slot, slot count), the balanced
+// partition's layout; otherwise row b's partials are slots b*num_splits ..
+hipError_t launch_combine(const float* part_o, const float* part_ml, const int* meta, int B,
+                          int H, int d, int num_splits, void* out, int out_f32,
+                          hipStream_t stream);
 
 struct AppendArgs {
   const void* k_new;          // [B][n_new][d]

@@ -122,16 +122,25 @@ mfa_status check_qproj_shape(int B, int hidden, int q_rank, int H, int d, int dt
 }
 
 // ---- attention planning --------------------------------------------------
-// Split workspace: part_o fp32 [rows][d] (rows = sequences x splits x
-// heads) at 0, part_ml fp32 [rows][2] at off_ml.
+// Split workspace: part_o fp32 [rows][d] (rows = partial slots x heads) at
+// 0, part_ml fp32 [rows][2] at off_ml; for the balanced partition also the
+// per-row metadata int32 [B][2] at off_meta.
 struct SplitLayout {
-  size_t off_ml, total;
+  size_t off_ml, off_meta, total;
 };
-SplitLayout split_layout(size_t rows, int d) {
+SplitLayout split_layout(size_t rows, int d, size_t meta_rows = 0) {
   SplitLayout l;
   l.off_ml = round_up(rows * static_cast<size_t>(d) * 4, 256);
-  l.total = l.off_ml + rows * 2 * 4;
+  l.off_meta = round_up(l.off_ml + rows * 2 * 4, 16);
+  l.total = meta_rows ? l.off_meta + meta_rows * 8 : l.off_ml + rows * 2 * 4;
   return l;
+}
+// The workspace of B rows and num_splits (0: balanced partition).
+SplitLayout workspace_layout(int B, int H, int d, int num_splits) {
+  if (num_splits == 0)
+    return split_layout(static_cast<size_t>(mfa::kBalancedWorkgroups + B) * H, d,
+                        static_cast<size_t>(B));
+  return split_layout(static_cast<size_t>(B) * num_splits * H, d);
 }
 
 bool mfma_shape(int H, int d, int kv_dtype) {
@@ -484,9 +493,47 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, i
   return MFA_OK;
 }
 
+mfa_status mfa_decode_plan_lens(int B, int H, int d, const int32_t* seq_lens, int kv_dtype,
+                                int* num_splits, int* chunk_tokens) {
+  if (!num_splits || !chunk_tokens || !seq_lens) return MFA_ERR_NULL;
+  if (B < 1 || H < 1 || d < 1) return MFA_ERR_SHAPE;
+  int max_len = 0;
+  long long total = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0) return MFA_ERR_SHAPE;
+    max_len = seq_lens[b] > max_len ? seq_lens[b] : max_len;
+    total += (seq_lens[b] + kBlock - 1) / kBlock;
+  }
+  const mfa_status st = mfa_decode_plan(B, H, d, max_len, kv_dtype, num_splits, chunk_tokens);
+  if (st != MFA_OK) return st;
+  if (!mfma_shape(H, d, kv_dtype) || B > mfa::kBalancedMaxRows || total == 0 ||
+      static_cast<long long>(B) * ((max_len + kBlock - 1) / kBlock) > (1ll << 21))
+    return MFA_OK;
+  // longest split workgroup of the plan (in blocks); with more workgroups
+  // than compute units, at least the chip's share
+  const int per = *chunk_tokens / kBlock;
+  long long longest = 0;
+  for (int b = 0; b < B; ++b) {
+    const long long nb = (seq_lens[b] + kBlock - 1) / kBlock;
+    longest = nb < per ? (nb > longest ? nb : longest) : (per > longest ? per : longest);
+  }
+  constexpr int kUnits = mfa::kBalancedWorkgroups;
+  const long long wgs = static_cast<long long>(B) * *num_splits;
+  const double split_ms = wgs <= kUnits ? static_cast<double>(longest)
+                                        : static_cast<double>((total + kUnits - 1) / kUnits) + 0.5 * longest;
+  const double bal_ms = static_cast<double>((total + kUnits - 1) / kUnits);
+  const double margin = kv_dtype == MFA_FP8_E4M3 ? 1.15 : 1.05;
+  if (split_ms > margin * bal_ms + 1.0) {
+    *num_splits = MFA_SPLITS_BALANCED;
+    *chunk_tokens = 0;
+  }
+  return MFA_OK;
+}
+
 size_t mfa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
-  if (B < 1 || H < 1 || d < 1 || num_splits <= 1) return 0;
-  return split_layout(static_cast<size_t>(B) * num_splits * H, d).total;
+  if (B < 1 || H < 1 || d < 1 || num_splits == 1 || num_splits < 0) return 0;
+  if (num_splits == 0 && B > mfa::kBalancedMaxRows) return 0;
+  return workspace_layout(B, H, d, num_splits).total;
 }
 
 size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits) {
@@ -526,13 +573,22 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   if (!cache->block_table &&
       static_cast<long long>(B) * cache->max_blocks_per_seq > cache->num_blocks)
     return MFA_ERR_SHAPE;
-  if (num_splits < 1 || chunk_tokens < kBlock || chunk_tokens % kBlock) return MFA_ERR_SHAPE;
-  if (static_cast<long long>(num_splits) * chunk_tokens < max_seq_len) return MFA_ERR_SHAPE;
+  const bool balanced = num_splits == 0;
+  if (balanced) {
+    if (Bv > mfa::kBalancedMaxRows) return MFA_ERR_SHAPE;
+    // the partition's cost arithmetic is 32-bit: at most 2^21 blocks in all
+    if (static_cast<long long>(Bv) * ((max_seq_len + kBlock - 1) / kBlock) > (1ll << 21))
+      return MFA_ERR_SHAPE;
+  } else {
+    if (num_splits < 1 || chunk_tokens < kBlock || chunk_tokens % kBlock) return MFA_ERR_SHAPE;
+    if (static_cast<long long>(num_splits) * chunk_tokens < max_seq_len) return MFA_ERR_SHAPE;
+  }
   if (static_cast<long long>(Bv) * num_splits > 0x7fffffffll / 64) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return MFA_ERR_SHAPE;
   c->mfma = mfma_shape(H, d, cache->dtype);
   if (fp8_queries && !(c->mfma && cache->dtype == MFA_FP8_E4M3)) return MFA_ERR_UNSUPPORTED;
+  if (balanced && (!c->mfma || fp8_queries)) return MFA_ERR_UNSUPPORTED;
   if (c->mfma) {
     if (q_dtype != MFA_BF16) return MFA_ERR_DTYPE;
   } else if (valu_shape(H, d, cache->dtype)) {
@@ -569,11 +625,13 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.q_len = q_len;
   a.fp8_queries = fp8_queries ? 1 : 0;
-  if (num_splits > 1) {
-    const SplitLayout l = split_layout(static_cast<size_t>(Bv) * num_splits * H, d);
+  if (num_splits != 1) {
+    const SplitLayout l = workspace_layout(Bv, H, d, num_splits);
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + l.off_ml);
+    if (balanced) a.bal_meta = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + l.off_meta);
   }
+  a.bal_rows = Bv;
   a.out = out;
   a.out_f32 = out_dtype == MFA_F32;
   c->fp8 = cache->dtype == MFA_FP8_E4M3;
@@ -589,9 +647,9 @@ mfa_status launch_attn(const AttnCall& c, hipStream_t st) {
   const mfa::AttnArgs& a = c.a;
   hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st) : mfa::launch_decode_valu(a, c.B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
-  if (c.num_splits > 1 && c.out) {
-    e = mfa::launch_combine(a.part_o, a.part_ml, c.B, c.H, c.d, c.num_splits, c.out, a.out_f32,
-                            st);
+  if (c.num_splits != 1 && c.out) {
+    e = mfa::launch_combine(a.part_o, a.part_ml, a.bal_meta, c.B, c.H, c.d, c.num_splits, c.out,
+                            a.out_f32, st);
     if (e != hipSuccess) return MFA_ERR_HIP;
   }
   return MFA_OK;
@@ -649,12 +707,12 @@ mfa_status mfa_decode_attn_static(const void* q, int q_dtype, int B, int H,
                                   int max_seq_len, float sm_scale, int num_splits,
                                   int chunk_tokens, void* out, int out_dtype, void* stream) {
   if (!out) return MFA_ERR_NULL;
-  if (cache && num_splits > 1 && B > 0 && H > 0 &&
+  if (cache && (num_splits == 0 || num_splits > 1) && B > 0 && H > 0 &&
       mfa_decode_workspace_bytes(B, H, cache->head_dim, num_splits) > MFA_STATIC_SCRATCH)
     return MFA_ERR_TOO_LARGE;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if (num_splits > 1) {
+  if (num_splits == 0 || num_splits > 1) {
     const mfa_status ss = scratch_for_current_device(&ws);
     if (ss != MFA_OK) return ss;
     ws_bytes = MFA_STATIC_SCRATCH;
@@ -735,14 +793,16 @@ mfa_status mfa_combine(const void* workspace, size_t workspace_bytes, int B, int
                        int num_splits, void* out, int out_dtype, void* stream) {
   if (!workspace || !out) return MFA_ERR_NULL;
   if (!aligned16(workspace) || !aligned16(out)) return MFA_ERR_ALIGN;
-  if (B < 1 || H < 1 || num_splits < 2) return MFA_ERR_SHAPE;
+  if (B < 1 || H < 1 || num_splits == 1 || num_splits < 0) return MFA_ERR_SHAPE;
+  if (num_splits == 0 && B > mfa::kBalancedMaxRows) return MFA_ERR_SHAPE;
   if (d != 64 && d != 128 && d != 256) return MFA_ERR_SHAPE;
   if (out_dtype != MFA_BF16 && out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (workspace_bytes < mfa_decode_workspace_bytes(B, H, d, num_splits)) return MFA_ERR_WORKSPACE;
-  const SplitLayout l = split_layout(static_cast<size_t>(B) * num_splits * H, d);
+  const SplitLayout l = workspace_layout(B, H, d, num_splits);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const int* meta = num_splits == 0 ? reinterpret_cast<const int*>(ws + l.off_meta) : nullptr;
   return from_hip(mfa::launch_combine(reinterpret_cast<const float*>(ws),
-                                      reinterpret_cast<const float*>(ws + l.off_ml), B, H, d,
+                                      reinterpret_cast<const float*>(ws + l.off_ml), meta, B, H, d,
                                       num_splits, out, out_dtype == MFA_F32, as_stream(stream)));
 }
 

@@ -18,6 +18,8 @@ from ._lib import check
 
 class DecodeStep:
     """Pre-planned decode step for B sequences of at most ``max_seq_len`` tokens.
+    With ``seq_lens_host`` (the lengths the step will attend) and no
+    ``num_splits``, the library plans from the lengths (mfa_decode_plan_lens).
 
     Workspaces (query-path partials, split partials) and outputs are
     allocated once here, so calling the step allocates nothing.
@@ -28,7 +30,7 @@ class DecodeStep:
                  act_dtype: torch.dtype = torch.bfloat16, num_splits: Optional[int] = None,
                  chunk_tokens: Optional[int] = None, eps: float = 1e-6,
                  out_dtype: Optional[torch.dtype] = None, sm_scale: Optional[float] = None,
-                 packed_weights: bool = False, device="cuda"):
+                 packed_weights: bool = False, device="cuda", seq_lens_host=None):
         self.cache = cache
         self.B, self.H, self.d = batch, heads, cache.head_dim
         self.max_seq_len = int(max_seq_len)
@@ -37,12 +39,15 @@ class DecodeStep:
         self.eps = eps
         self.packed_weights = packed_weights
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(self.d)
-        if num_splits is None:
+        if num_splits is None and seq_lens_host is not None:
+            # the plan from the batch's lengths (balanced partition for mixed ones)
+            num_splits, chunk_tokens = api.decode_plan_lens(heads, self.d, seq_lens_host,
+                                                            cache.dtype)
+        elif num_splits is None:
             num_splits, chunk_tokens = api.decode_plan(batch, heads, self.d, self.max_seq_len,
                                                        cache.dtype)
         elif chunk_tokens is None:
-            per = -(-max(self.max_seq_len, 1) // num_splits)
-            chunk_tokens = -(-per // _lib.BLOCK_TOKENS) * _lib.BLOCK_TOKENS
+            chunk_tokens = api._chunk(self.max_seq_len, num_splits)
         self.num_splits, self.chunk_tokens = int(num_splits), int(chunk_tokens)
         self.out_dtype = out_dtype or act_dtype
         self.out = torch.empty((batch, heads, self.d), dtype=self.out_dtype, device=device)

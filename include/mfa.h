@@ -202,6 +202,22 @@ mfa_status mfa_kv_append(const void *k_new, const void *v_new, int in_dtype,
 mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
                            int *num_splits, int *chunk_tokens);
 
+/*
+ * Split plan from the batch's lengths (host array seq_lens[B], the values the
+ * call will attend, 0 .. capacity): as mfa_decode_plan for the longest row,
+ * or the balanced partition (*num_splits = MFA_SPLITS_BALANCED,
+ * *chunk_tokens = 0) when the lengths are mixed enough that the split plan's
+ * longest workgroup would walk clearly more blocks (5% plus one block; 15%
+ * for FP8 caches, whose split kernel takes two blocks per iteration) than
+ * the balanced partition gives each workgroup. The balanced partition is
+ * offered only for the matrix-core shapes, up to MFA_BALANCED_MAX_ROWS rows
+ * and 2^21 blocks in all. Host-only, no launch.
+ */
+#define MFA_SPLITS_BALANCED 0
+#define MFA_BALANCED_MAX_ROWS 1024
+mfa_status mfa_decode_plan_lens(int B, int H, int d, const int32_t *seq_lens, int kv_dtype,
+                                int *num_splits, int *chunk_tokens);
+
 /* Bytes of split workspace for mfa_decode_attn / mfa_combine (the split
  * partials of the long-context case, "Step-3 is Large yet Affordable"
  * summary page, §4 Cost Analysis for LLM Decoding: attention cost grows with
@@ -214,7 +230,12 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype,
  * Total round_up(R*d*4, 256) + R*8 bytes; 0 when num_splits == 1. The
  * partials are fp32 whatever the output type, so mfa_combine may write
  * either output type. The caller owns the workspace; the library keeps
- * nothing in it between calls. */
+ * nothing in it between calls.
+ * For the balanced partition (num_splits == MFA_SPLITS_BALANCED, B <=
+ * MFA_BALANCED_MAX_ROWS, else 0 bytes) there are 256 + B partial slots:
+ * R = (256 + B)*H rows of part_o and part_ml as above (slot w + b holds the
+ * piece of row b that workgroup w walked), then int32 [B][2] at offset
+ * round_up(off_ml + R*8, 16): row b's first slot and its number of slots. */
 size_t mfa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 /* The same function under its earlier name. */
 size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
@@ -231,10 +252,20 @@ size_t mfa_split_workspace_bytes(int B, int H, int d, int num_splits);
  * num_splits >= 1 KV splits per sequence; split j covers tokens
  *            [j*chunk_tokens, min((j+1)*chunk_tokens, seq_len)). Requires
  *            chunk_tokens % 64 == 0 and num_splits*chunk_tokens >= max_seq_len.
- * workspace  mfa_decode_workspace_bytes(...) bytes when num_splits > 1
- *            (receives the per-split partials), else may be NULL.
+ *            MFA_SPLITS_BALANCED (0) instead runs the balanced partition
+ *            (matrix-core shapes, B <= MFA_BALANCED_MAX_ROWS, at most 2^21
+ *            blocks of 64 tokens in all; chunk_tokens is ignored): the
+ *            batch's blocks, concatenated row after row, are cut evenly over
+ *            the chip's 256 compute units, so rows of mixed lengths cost one
+ *            equal share each instead of the longest split. A row start that
+ *            falls inside a share is charged 1.5 blocks of work (the piece
+ *            that ends there costs its workgroup that much). The same
+ *            softmax is computed: results equal the split plan's up to
+ *            rounding.
+ * workspace  mfa_decode_workspace_bytes(...) bytes when num_splits != 1
+ *            (receives the partials), else may be NULL.
  * out        [B][H][d] of out_dtype (MFA_BF16 or MFA_F32). With
- *            num_splits > 1, out may be NULL: only the partials are
+ *            num_splits != 1, out may be NULL: only the partials are
  *            written and the caller runs mfa_combine; otherwise the library
  *            merges the partials into out on the same stream.
  * Supported: H in 1..64 and d in {64,128,256} with F32 caches (VALU kernel);
@@ -328,7 +359,9 @@ mfa_status mfa_decode_attn_q8(const void *q, int q_dtype, int B, int q_len, int 
  *   m* = max_j m_j,  w_j = exp(m_j - m*),  out = sum_j w_j o_j / sum_j w_j l_j.
  * Splits with l_j == 0 (empty) get weight 0; a head whose splits are all
  * empty gives zeros. out [B][H][d] of out_dtype (MFA_BF16 or MFA_F32; the
- * partials are fp32 either way). num_splits >= 2; d in {64, 128, 256}.
+ * partials are fp32 either way). num_splits >= 2, or MFA_SPLITS_BALANCED
+ * for the balanced partition's workspace (each row's own slots, as the
+ * attention call listed them); d in {64, 128, 256}.
  * Host checks as for every call;
  * MFA_ERR_WORKSPACE when workspace_bytes is below the required size.
  */

@@ -63,7 +63,7 @@ def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=Tru
         num_splits = w.num_splits
     step = DecodeStep(cache, w.batch, w.heads, int(inp["seq_lens"].max()), hidden=w.hidden,
                       q_rank=w.q_rank, act_dtype=act, num_splits=num_splits,
-                      chunk_tokens=chunk_tokens)
+                      chunk_tokens=chunk_tokens, seq_lens_host=inp["seq_lens"])
     return T, cache, step
 
 

@@ -72,7 +72,8 @@ def test_decode_attn_validation(lib):
     assert _attn(lib, _cache(k=PM)) == ALIGN
     assert _attn(lib, _cache(dtype=7)) == DTYPE
     assert _attn(lib, c, maxlen=16 * 64 + 1) == SHAPE            # beyond capacity
-    assert _attn(lib, c, ns=0) == SHAPE
+    assert _attn(lib, c, ns=-1) == SHAPE
+    assert _attn(lib, c, ns=0) == WS                              # balanced: needs a workspace
     assert _attn(lib, c, chunk=100) == SHAPE                     # not a multiple of 64
     assert _attn(lib, c, ns=2, chunk=64, maxlen=512) == SHAPE    # splits do not cover
     assert _attn(lib, c, ns=8, chunk=64, ws=None) == WS
@@ -208,6 +209,28 @@ def test_static_scratch_refuses_oversize(lib):
                                       None, BF16, None) == NULL
 
 
+def test_balanced_partition_limits(lib):
+    """num_splits == 0 (balanced partition): workspace for 256 + B slots plus
+    per-row metadata; more than 1024 rows is a shape error, before any HIP
+    call."""
+    rows = (256 + 100) * 64
+    off_ml = rows * 256 * 4
+    off_meta = -(-(off_ml + rows * 8) // 16) * 16
+    assert lib.mfa_decode_workspace_bytes(100, 64, 256, 0) == off_meta + 100 * 8
+    assert lib.mfa_decode_workspace_bytes(1025, 64, 256, 0) == 0
+    desc = _lib.KVCacheDesc(k=P, v=P, num_blocks=1 << 20, max_blocks_per_seq=64, head_dim=256,
+                            dtype=BF16)
+    big = lib.mfa_decode_workspace_bytes(1024, 64, 256, 0)
+    assert lib.mfa_decode_attn(P, BF16, 1025, 64, ctypes.byref(desc), P, 100, 0.0625, 0, 0, P,
+                               big, P, BF16, None) == SHAPE
+    # the balanced partition needs the matrix-core kernel (64 heads of 256)
+    d64 = _lib.KVCacheDesc(k=P, v=P, num_blocks=1 << 20, max_blocks_per_seq=64, head_dim=64,
+                           dtype=F32)
+    assert lib.mfa_decode_attn(P, F32, 4, 4, ctypes.byref(d64), P, 100, 0.125, 0, 0, P,
+                               1 << 30, P, F32, None) == UNSUP
+    assert lib.mfa_combine(P, 16, 1025, 64, 256, 0, P, BF16, None) == SHAPE
+
+
 def _c_layout(struct, fields):
     """sizeof and offsetof of a struct of mfa.h, from a C program built by gcc."""
     import shutil
@@ -276,3 +299,29 @@ def test_decode_step_validation(lib):
     a.pos = P
     a.x = None
     assert ok() == NULL                                          # projection without x
+
+
+def test_plan_from_lengths(lib):
+    """mfa_decode_plan_lens: uniform lengths keep the split plan; mixed ones
+    whose longest split walks clearly more than the chip's even share get the
+    balanced partition; shapes without the matrix-core kernel never do."""
+    import numpy as np
+    ns, ch = ctypes.c_int(), ctypes.c_int()
+
+    def plan(lens, H=64, d=256, dt=BF16):
+        a = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+        rc = lib.mfa_decode_plan_lens(len(a), H, d, a.ctypes.data_as(ctypes.c_void_p), dt,
+                                      ctypes.byref(ns), ctypes.byref(ch))
+        assert rc == OK
+        return ns.value, ch.value
+    assert plan([4096] * 32) == (8, 512)                  # the 4K workload: as mfa_decode_plan
+    assert plan([32768] * 16, dt=FP8)[0] == 16
+    rng = np.random.default_rng(2)
+    mixed = rng.integers(1025, 8194, size=128)
+    assert plan(mixed) == (0, 0)                          # mixed lengths: balanced
+    assert plan(mixed, H=4, d=64, dt=F32)[0] >= 1         # VALU shapes: split plan only
+    assert plan([0] * 8)[0] >= 1                          # nothing to walk: split plan
+    big = np.full(1025, 3000)
+    assert plan(big)[0] >= 1                              # more rows than the balanced walk takes
+    assert lib.mfa_decode_plan_lens(4, 64, 256, None, BF16, ctypes.byref(ns),
+                                    ctypes.byref(ch)) == NULL

@@ -97,6 +97,147 @@ def test_poisoned_cache_tails(gpu_lib, name, base, over, lens, q8, splits):
     check_bf16(got, want, f"poisoned {name}/S={splits}")
 
 
+# ---------------------------------------------------------------- balanced partition
+# num_splits == 0: the rows' blocks are split evenly over 256 workgroups, so a
+# workgroup walks across row boundaries (pieces), and rows with 0 or 1 block
+# sit inside a workgroup's range.
+def _ragged(n, seed, top=1500, head=(0, 1, 63, 64, 65)):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, top, size=n).tolist()
+    lens[:len(head)] = list(head)
+    return lens
+
+
+BAL = [
+    # few blocks (fewer than workgroups): one block per workgroup
+    ("bf16-paged-few", 3, dict(), [1, 62, 65, 127, 300, 777]),
+    ("bf16-contig-few", 3, dict(paged=False), [0, 63, 200]),
+    # hundreds of blocks: ~3 blocks per workgroup, many boundaries
+    ("bf16-paged-64", 3, dict(batch=64), _ragged(64, 91)),
+    ("bf16-contig-48", 3, dict(batch=48, paged=False), _ragged(48, 92)),
+    ("fp8-paged-40", 4, dict(batch=40), _ragged(40, 93)),
+    ("fp8-contig-24", 4, dict(batch=24, paged=False), _ragged(24, 94, top=3000)),
+    # long rows next to 1-token rows: pieces of one block between long ones
+    ("bf16-paged-mix", 3, dict(batch=12), [5000, 0, 1, 3000, 63, 64, 1, 7000, 2, 130, 4000, 0]),
+]
+
+
+@pytest.mark.parametrize("name,base,over,lens", BAL, ids=[b[0] for b in BAL])
+def test_balanced_parity(gpu_lib, name, base, over, lens):
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=301 + base)
+    say(f"balanced {name} rows={len(lens)} blocks={int(np.sum((inp['seq_lens'] + 63) // 64))}")
+    T, cache, step = setup(inp, num_splits=0)
+    _, out = run(T, step)
+    check_bf16(to_np(out), orun.decode_step(inp)["o"], f"balanced {name}")
+
+
+@pytest.mark.parametrize("name,base,over,lens", [BAL[2], BAL[4], BAL[6]],
+                         ids=["bf16-paged-64", "fp8-paged-40", "bf16-paged-mix"])
+def test_balanced_poisoned(gpu_lib, name, base, over, lens):
+    """The balanced walk on caches whose unwritten slots hold NaNs."""
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=311 + base)
+    say(f"balanced poisoned {name}")
+    T, cache, step = setup(inp, num_splits=0, zero_cache=False, poison=True)
+    _, out = run(T, step)
+    got = to_np(out)
+    assert np.all(np.isfinite(got))
+    check_bf16(got, orun.decode_step(inp)["o"], f"balanced poisoned {name}")
+
+
+@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("base", [3, 4], ids=["bf16", "fp8"])
+def test_balanced_multi_token(gpu_lib, base, T):
+    """Virtual rows (sequence, query token) in the balanced walk."""
+    import decode_attention_02_amd as mfa
+    lens = _ragged(20, 95, head=(0, 1, 2, 63, 64))
+    w = small(base, batch=len(lens))
+    inp = workloads.make_inputs(base, workload=w, seed=321, prefill_lens=lens, q_len=T)
+    say(f"balanced multi-token base={base} T={T}")
+    T_, cache, step = setup(inp)
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    out = mfa.decode_attn_multi(T_["q_multi"], cache, T_["seq_lens"], maxlen, num_splits=0)
+    torch.cuda.synchronize()
+    check_bf16(to_np(out), orun.decode_step_multi(inp), f"balanced multi T={T}")
+
+
+def test_balanced_separate_combine(gpu_lib):
+    """Attention with out=NULL then mfa_combine(num_splits=0) equals the
+    call that merges itself, bit for bit, and the per-row metadata is the
+    partition's (every non-empty row's slots are consecutive, counts sum to
+    the pieces)."""
+    import decode_attention_02_amd as mfa
+    lens = _ragged(64, 96)
+    w = small(3, batch=len(lens))
+    inp = workloads.make_inputs(3, workload=w, seed=331, prefill_lens=lens)
+    T, cache, step = setup(inp, num_splits=0)
+    mfa.kv_append(cache, T["k_new"], T["v_new"], T["prefill_lens"])
+    maxlen = int(inp["seq_lens"].max())
+    B = len(lens)
+    ws = torch.empty(mfa.decode_workspace_bytes(B, 64, 256, 0), dtype=torch.uint8, device="cuda")
+    say("balanced: separate combine")
+    fused = mfa.decode_attn(T["q"], cache, T["seq_lens"], maxlen, num_splits=0, workspace=ws)
+    fused = fused.clone()
+    mfa.decode_attn(T["q"], cache, T["seq_lens"], maxlen, num_splits=0, workspace=ws,
+                    combine=False)
+    sep = mfa.combine_splits(ws, B, 64, 256, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
+    # metadata: (first slot, count) per row at the end of the workspace
+    rows = (256 + B) * 64
+    off_ml = -(-rows * 256 * 4 // 256) * 256
+    off_meta = -(-(off_ml + rows * 8) // 16) * 16
+    meta = ws[off_meta:off_meta + B * 8].cpu().numpy().view(np.int32).reshape(B, 2)
+    nblk = (inp["seq_lens"] + 63) // 64
+    NB = int(nblk.sum())
+    pfx = np.concatenate([[0], np.cumsum(nblk)])
+    for r in range(B):
+        if nblk[r] == 0:
+            assert meta[r, 1] == 0
+            continue
+        # workgroup of global block x: floor(w NB / 256) <= x < floor((w+1) NB / 256)
+        lo = np.array([wg * NB // 256 for wg in range(257)])
+        wf = int(np.searchsorted(lo, pfx[r], side="right") - 1)
+        wl = int(np.searchsorted(lo, pfx[r + 1] - 1, side="right") - 1)
+        assert (meta[r, 0], meta[r, 1]) == (wf + r, wl - wf + 1), r
+    check_bf16(to_np(fused), orun.decode_step(inp)["o"], "balanced separate combine")
+
+
+def test_balanced_static_and_graph(gpu_lib):
+    """The balanced partition through mfa_decode_attn_static, and the whole
+    step with it captured in a HIP graph (every replay bit-identical)."""
+    import decode_attention_02_amd as mfa
+    lens = _ragged(32, 97)
+    w = small(3, batch=len(lens))
+    inp = workloads.make_inputs(3, workload=w, seed=341, prefill_lens=lens)
+    T, cache, step = setup(inp, num_splits=0)
+    say("balanced: static scratch and graph replay")
+    _, eager = run(T, step)
+    eager = eager.clone()
+    maxlen = int(inp["seq_lens"].max())
+    st = mfa.decode_attn_static(T["q"], cache, T["seq_lens"], maxlen, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(st.view(torch.int16), eager.view(torch.int16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+    for r in range(3):
+        step.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+    check_bf16(to_np(eager), orun.decode_step(inp)["o"], "balanced graph step")
+
+
 def test_small_f32_generic(gpu_lib):
     """fp32 cache and q on the vector-ALU kernel, ragged lengths, 1 and 3 splits."""
     w = small(1, hidden=None, q_rank=None)
@@ -814,13 +955,29 @@ def test_full_step3_bf16(gpu_lib):
 
 
 def test_full_paged_mixed(gpu_lib):
+    """The full paged mixed-length workload on the split plan for its longest
+    row (the lengths-aware plan picks the balanced partition, tested below)."""
+    import decode_attention_02_amd as mfa
     inp = workloads.make_inputs(3)
-    say("full paged mixed")
-    T, cache, step = setup(inp)
+    say("full paged mixed, split plan")
+    ns, ch = mfa.decode_plan(128, 64, 256, int(inp["seq_lens"].max()), "bf16")
+    T, cache, step = setup(inp, num_splits=ns, chunk_tokens=ch)
     say(f"plan: splits={step.num_splits} chunk={step.chunk_tokens}")
     _, out = run(T, step)
     want = orun.decode_step(inp)
     check_bf16(to_np(out), want["o"], "paged mixed")
+
+
+def test_full_paged_mixed_balanced(gpu_lib):
+    """The full paged mixed-length workload with the plan from its lengths:
+    the balanced partition."""
+    inp = workloads.make_inputs(3)
+    say("full paged mixed, balanced")
+    T, cache, step = setup(inp)
+    assert step.num_splits == 0
+    _, out = run(T, step)
+    want = orun.decode_step(inp)
+    check_bf16(to_np(out), want["o"], "paged mixed balanced")
 
 
 def test_full_fp8_32k_sampled(gpu_lib):

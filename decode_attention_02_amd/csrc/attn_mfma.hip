@@ -112,8 +112,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 }  // namespace
 
 // RK, RV: ring depth (blocks of registers) of the QK and of the PV waves.
-// HT: 16-head tiles per workgroup (4: all 64 heads; 2: half of them, two
-// workgroups per (sequence, split) reading the same K/V blocks).
 // BAL: the balanced partition (num_splits == 0). The rows' 64-token blocks,
 // concatenated in row order, are cut into gridDim.x equal ranges, one per
 // workgroup (fewer when there are fewer blocks than workgroups). A workgroup
@@ -123,14 +121,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // piece ahead) behind one extra barrier that both roles pass, and the PV
 // waves write out the finished piece's o, then its (m, l) one iteration
 // later, once the four PV waves' row sums have met in LDS.
-template <bool FP8, int RK, int RV, int HT, bool Q8 = false, int BPI = 1, bool BAL = false>
+template <bool FP8, int RK, int RV, bool Q8 = false, int BPI = 1, bool BAL = false>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
+  constexpr int HT = 4;                 // 16-head tiles: every workgroup holds all 64 heads
   static_assert(!Q8 || FP8, "FP8 queries run against FP8 caches");
   static_assert(BPI == 1 || (BPI == 2 && !Q8), "two blocks per iteration: plain FP8 and bf16 only");
-  static_assert(!BAL || (BPI == 1 && HT == 4 && !Q8), "balanced walk: one block per unit, 64 heads");
+  static_assert(!BAL || (BPI == 1 && !Q8), "balanced walk: one block per unit");
   using C = Cfg<FP8>;
   constexpr int kHW = 16 * HT;                                          // heads of this workgroup
-  constexpr int kHS = kH / kHW;                                         // workgroups per split
   // Q in operand order: bf16 HT x 8 KB; Q8 codes HT x 4 KB, block (ht, k2),
   // lane (gg, cc), two uint4: codes of q[h0+16ht+cc][128k2 + 16gg .. +16]
   // and [128k2 + 64 + 16gg .. +16] (the K ring's unit pair for k2)
@@ -159,14 +157,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int ww = w & 3;                 // QK: token group; PV: feature group of 64
 
   // Workgroups are dispatched round-robin over the 8 XCDs (id % 8). Remap so
-  // that each XCD runs a contiguous range of (sequence, split, head group)
-  // triples: the head groups of a split then read the same K/V blocks
-  // through one L2 at about the same time, and the splits of a sequence
-  // share that L2 for their query reads.
+  // that each XCD runs a contiguous range of (sequence, split) pairs (of the
+  // balanced walk's ranges): the splits of a sequence then share that XCD's
+  // L2 for their query reads.
   int id = blockIdx.x;
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int ql = a.q_len > 0 ? a.q_len : 1;
-  int hg = 0, split = 0, b = 0, bs = 0, t1 = 0, blk0 = 0, N = 0;
+  int split = 0, b = 0, bs = 0, t1 = 0, blk0 = 0, N = 0;
   int lo = 0, hi = 0;                   // balanced walk: the workgroup's global block range
   if constexpr (BAL) {
     // rows 2 tid, 2 tid + 1: lengths (clamped like the split path), block
@@ -314,9 +311,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     hi = id + 1 < Geff ? __builtin_amdgcn_readfirstlane(bal_wsum[18]) : NB;
     N = hi - lo;
   } else {
-    hg = id % kHS;
-    split = (id / kHS) % a.num_splits;
-    b = id / kHS / a.num_splits;                                        // virtual row (q, partials, out)
+    split = id % a.num_splits;
+    b = id / a.num_splits;                                              // virtual row (q, partials, out)
     bs = b / ql;                                                        // its sequence (cache, lengths)
     const int jq = b - bs * ql;                                         // its query token
     // query token jq sees the sequence up to and including itself
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     blk0 = t0 >> 6;
     N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;            // blocks to walk
   }
-  const int h0 = hg * kHW;                                              // first head
+  constexpr int h0 = 0;                                                 // first head
   // iterations walk units of BPI consecutive blocks (a unit's second block
   // past the walk reads nothing and is masked out)
   const int NU = (N + BPI - 1) / BPI;
@@ -339,8 +335,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // barrier. The first requests of every compute unit are then the ones the
   // first iteration waits for (Q and K block 0), not V blocks needed two
   // iterations later.
-  constexpr int kQLoads = 2 * HT;                                       // 16-byte loads per QK thread
-  static_assert(kQLoads == 4 || kQLoads == 8, "Q staging covers two or four head tiles");
+  constexpr int kQLoads = 2 * HT;                                       // 16-byte loads per QK thread (8)
   // Q8 staging: kTPH adjacent threads share a head, each with kDPT
   // consecutive dims (so a head's amax is a reduction over kTPH lanes)
   constexpr int kTPH = 256 / kHW;
@@ -405,9 +400,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       // barriers below would be left in scratch memory
       uint4 q0, q1, q2, q3, q4, q5, q6, q7;
       q0 = *q_src(b, 0); q1 = *q_src(b, 1); q2 = *q_src(b, 2); q3 = *q_src(b, 3);
-      if constexpr (kQLoads == 8) {
-        q4 = *q_src(b, 4); q5 = *q_src(b, 5); q6 = *q_src(b, 6); q7 = *q_src(b, 7);
-      }
+      q4 = *q_src(b, 4); q5 = *q_src(b, 5); q6 = *q_src(b, 6); q7 = *q_src(b, 7);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
       __builtin_amdgcn_sched_barrier(0);
@@ -416,9 +409,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         stage_q8(qv);
       } else {
         q_lds[tid] = q0; q_lds[tid + 256] = q1; q_lds[tid + 512] = q2; q_lds[tid + 768] = q3;
-        if constexpr (kQLoads == 8) {
-          q_lds[tid + 1024] = q4; q_lds[tid + 1280] = q5; q_lds[tid + 1536] = q6; q_lds[tid + 1792] = q7;
-        }
+        q_lds[tid + 1024] = q4; q_lds[tid + 1280] = q5; q_lds[tid + 1536] = q6; q_lds[tid + 1792] = q7;
       }
     }
   };
@@ -664,7 +655,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
         }
       }
       // per-head max over the wave's 16 tokens of each block; lane row g
-      // ends with the max of tile g (HT 4) or g/2 (HT 2), so one store per
+      // ends with the max of tile g, so one store per
       // lane covers them all
       float mt[HT];
 #pragma unroll
@@ -677,11 +668,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int bb = 0; bb < BPI; ++bb) s_lds[par][((bb * 4 + ww) * HT + ht) * 64 + lane] = s_acc[bb][ht];
       }
-      if constexpr (HT == 4) {
-        red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
-      } else {
-        red[par][((g >> 1) * 16 + c) * 4 + ww] = rows4_max_t2(mt[0], mt[1]);
-      }
+      red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
     };
 
     // Every iteration issues the same loads (empty ones past the walk), so
@@ -1125,30 +1112,23 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream) {
-  // Two head groups per (sequence, split) while the grid stays within one
-  // workgroup per compute unit (256), and only when the XCD remap keeps both
-  // groups of a split on one XCD (pairs a multiple of 8): they then read the
-  // K/V blocks once from HBM and twice from that XCD's L2.
   if (a.num_splits == 0) {
     // balanced partition: one workgroup per compute unit
     const dim3 grid(kBalancedWorkgroups), block(512);
-    if (fp8) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4, false, 1, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, 4, false, 1, true>), grid, block, 0, stream, a);
+    if (fp8) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, false, 1, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, false, 1, true>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
-  const long long pairs = static_cast<long long>(B) * a.num_splits;
-  const bool half = pairs * 2 <= 256 && pairs % 8 == 0;
-  const dim3 grid(static_cast<unsigned>(pairs * (half ? 2 : 1))), block(512);
+  // one workgroup of 64 heads per (row, split); short plans already walk
+  // each split as two halves (the host doubles the split count)
+  const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * a.num_splits)), block(512);
   if (fp8 && a.fp8_queries) {
-    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 2, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, 4, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, true>), grid, block, 0, stream, a);
   } else if (fp8) {
     // two 32 KB FP8 blocks per iteration: the same bytes between barriers as one bf16 block
-    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, 2, false, 2>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, 4, false, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, false, 2>), grid, block, 0, stream, a);
   } else {
-    if (half) hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 4, 2>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -178,11 +178,6 @@ __device__ __forceinline__ float rows4_max_t4(float v0, float v1, float v2, floa
   const float y = swap32_max(v1, v3);     // rows: v1(0,2) v1(1,3) v3(0,2) v3(1,3)
   return swap16_max(x, y);                // rows: v0 v1 v2 v3, each over all rows
 }
-// Two values: lane (row g, column c) returns the column max of v[g / 2].
-__device__ __forceinline__ float rows4_max_t2(float v0, float v1) {
-  const float x = swap32_max(v0, v1);     // rows: v0(0,2) v0(1,3) v1(0,2) v1(1,3)
-  return swap16_max(x, x);                // rows: v0 v0 v1 v1
-}
 
 __device__ __forceinline__ float rows4_sum(float v) {
   const int iv = __float_as_int(v);

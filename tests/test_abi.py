@@ -183,7 +183,11 @@ def test_plan_and_split_workspace(lib):
         assert ns.value >= 1 and ch.value % 64 == 0 and ns.value * ch.value >= L
     assert lib.mfa_decode_plan(0, 64, 256, 10, BF16, ctypes.byref(ns), ctypes.byref(ch)) == SHAPE
     assert lib.mfa_decode_workspace_bytes(4, 64, 256, 1) == 0
-    rows = 4 * 32 * 64
+    rows = 16 * 16 * 64                          # 16 rows x 16 splits: one partial per split
+    assert lib.mfa_decode_workspace_bytes(16, 64, 256, 16) == rows * 256 * 4 + rows * 2 * 4
+    # 4 rows x 32 splits leave half the chip idle: each split is walked as two
+    # halves, so the workspace holds 64 partials per row
+    rows = 4 * 64 * 64
     assert lib.mfa_decode_workspace_bytes(4, 64, 256, 32) == rows * 256 * 4 + rows * 2 * 4
     rows = 3 * 5 * 7
     off_ml = -(-rows * 64 * 4 // 256) * 256

@@ -163,13 +163,53 @@ def test_balanced_multi_token(gpu_lib, base, T):
     check_bf16(to_np(out), orun.decode_step_multi(inp), f"balanced multi T={T}")
 
 
-def test_balanced_separate_combine(gpu_lib):
+def _balanced_partition(lens, G=256, row_cost=6):
+    """The balanced partition restated: rows' blocks (64 tokens) in row order,
+    a block costing U units and an interior row start (not a cut of the plain
+    even partition) row_cost more when there are at least 4 blocks per
+    workgroup; workgroup w takes the blocks whose cost start lies in
+    [floor(w TC / Geff), floor((w+1) TC / Geff)). Returns per row the
+    (first workgroup, number of workgroups) that walk it (None: no blocks)."""
+    nb = [(L + 63) // 64 for L in lens]
+    NB = sum(nb)
+    geff = min(G, NB)
+    weighted = NB >= 4 * G
+    U, RC = (4, row_cost) if weighted else (1, 0)
+    pfx = np.concatenate([[0], np.cumsum(nb)])
+
+    def interior(st):
+        v = -(-st * geff // NB)
+        return not (v < geff and v * NB // geff == st)
+    cost, c = [], 0
+    for r, n in enumerate(nb):
+        rc = RC if (n > 0 and interior(int(pfx[r]))) else 0
+        cost.append((c, rc))
+        c += U * n + rc
+    TC = c
+
+    def wg_of(x):
+        v = x * geff // TC
+        return v + 1 if (v + 1) * TC // geff <= x else v
+    out = []
+    for r, n in enumerate(nb):
+        if n == 0:
+            out.append(None)
+            continue
+        c0 = cost[r][0] + cost[r][1]
+        wf, wl = wg_of(c0), wg_of(c0 + U * (n - 1))
+        out.append((wf, wl - wf + 1))
+    return out
+
+
+@pytest.mark.parametrize("name,n,top,seed", [("plain", 64, 1500, 96), ("weighted", 96, 12000, 98)])
+def test_balanced_separate_combine(gpu_lib, name, n, top, seed):
     """Attention with out=NULL then mfa_combine(num_splits=0) equals the
-    call that merges itself, bit for bit, and the per-row metadata is the
-    partition's (every non-empty row's slots are consecutive, counts sum to
-    the pieces)."""
+    call that merges itself, bit for bit, and the per-row metadata (first
+    slot = first workgroup + row, slot count) is the restated partition's,
+    with fewer than 4 blocks per workgroup (plain cut) and with more
+    (cost-weighted cut)."""
     import decode_attention_02_amd as mfa
-    lens = _ragged(64, 96)
+    lens = _ragged(n, seed, top=top)
     w = small(3, batch=len(lens))
     inp = workloads.make_inputs(3, workload=w, seed=331, prefill_lens=lens)
     T, cache, step = setup(inp, num_splits=0)
@@ -177,7 +217,8 @@ def test_balanced_separate_combine(gpu_lib):
     maxlen = int(inp["seq_lens"].max())
     B = len(lens)
     ws = torch.empty(mfa.decode_workspace_bytes(B, 64, 256, 0), dtype=torch.uint8, device="cuda")
-    say("balanced: separate combine")
+    nblk = (inp["seq_lens"] + 63) // 64
+    say(f"balanced {name}: separate combine, {int(nblk.sum())} blocks")
     fused = mfa.decode_attn(T["q"], cache, T["seq_lens"], maxlen, num_splits=0, workspace=ws)
     fused = fused.clone()
     mfa.decode_attn(T["q"], cache, T["seq_lens"], maxlen, num_splits=0, workspace=ws,
@@ -185,24 +226,19 @@ def test_balanced_separate_combine(gpu_lib):
     sep = mfa.combine_splits(ws, B, 64, 256, 0)
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
+    assert (int(nblk.sum()) >= 1024) == (name == "weighted")
     # metadata: (first slot, count) per row at the end of the workspace
     rows = (256 + B) * 64
     off_ml = -(-rows * 256 * 4 // 256) * 256
     off_meta = -(-(off_ml + rows * 8) // 16) * 16
     meta = ws[off_meta:off_meta + B * 8].cpu().numpy().view(np.int32).reshape(B, 2)
-    nblk = (inp["seq_lens"] + 63) // 64
-    NB = int(nblk.sum())
-    pfx = np.concatenate([[0], np.cumsum(nblk)])
+    want = _balanced_partition([int(x) for x in inp["seq_lens"]])
     for r in range(B):
-        if nblk[r] == 0:
-            assert meta[r, 1] == 0
-            continue
-        # workgroup of global block x: floor(w NB / 256) <= x < floor((w+1) NB / 256)
-        lo = np.array([wg * NB // 256 for wg in range(257)])
-        wf = int(np.searchsorted(lo, pfx[r], side="right") - 1)
-        wl = int(np.searchsorted(lo, pfx[r + 1] - 1, side="right") - 1)
-        assert (meta[r, 0], meta[r, 1]) == (wf + r, wl - wf + 1), r
-    check_bf16(to_np(fused), orun.decode_step(inp)["o"], "balanced separate combine")
+        if want[r] is None:
+            assert meta[r, 1] == 0, r
+        else:
+            assert (meta[r, 0], meta[r, 1]) == (want[r][0] + r, want[r][1]), (r, meta[r], want[r])
+    check_bf16(to_np(fused), orun.decode_step(inp)["o"], f"balanced {name} separate combine")
 
 
 def test_balanced_static_and_graph(gpu_lib):

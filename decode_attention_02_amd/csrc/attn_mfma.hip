@@ -145,8 +145,13 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // finished inside the walk, by piece parity
   __shared__ int bal_pfx[BAL ? kBalancedMaxRows + 1 : 1];
   __shared__ int bal_len[BAL ? kBalancedMaxRows : 1];
-  __shared__ int bal_cpfx[BAL ? kBalancedMaxRows + 1 : 1];
-  __shared__ int bal_rc[BAL ? kBalancedMaxRows : 1];
+  // balanced walk: o of the first piece that ends inside the walk, held here
+  // until the end ([head][64 chunks of 4 features], rows padded to 65 chunks
+  // so that the 16 heads of a write fall in different banks); before the
+  // walk its first 8 KB hold the setup's cost prefix sums and row-start costs
+  __shared__ __attribute__((aligned(16))) float4 bal_hold[BAL ? kHW * 65 : 1];
+  int* const bal_cpfx = reinterpret_cast<int*>(bal_hold);
+  int* const bal_rc = bal_cpfx + kBalancedMaxRows + 4;
   __shared__ int bal_wsum[20];
   __shared__ __attribute__((aligned(16))) float lred2[2][BAL ? kHW * 4 : 4];
 
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   const int ql = a.q_len > 0 ? a.q_len : 1;
   int split = 0, b = 0, bs = 0, t1 = 0, blk0 = 0, N = 0;
   int lo = 0, hi = 0;                   // balanced walk: the workgroup's global block range
+  bool hold_first = false;              // balanced walk: its first piece ends inside the walk
   if constexpr (BAL) {
     // rows 2 tid, 2 tid + 1: lengths (clamped like the split path), block
     // counts and costs; exclusive scans of both over all rows.
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     lo = __builtin_amdgcn_readfirstlane(bal_wsum[17]);
     hi = id + 1 < Geff ? __builtin_amdgcn_readfirstlane(bal_wsum[18]) : NB;
     N = hi - lo;
+    hold_first = __builtin_amdgcn_readfirstlane(bal_pfx[b + 1]) < hi;
   } else {
     split = id % a.num_splits;
     b = id / a.num_splits;                                              // virtual row (q, partials, out)
@@ -754,6 +761,17 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       }
     });
     __syncthreads();   // row sums staged (by the PV waves)
+    // balanced walk: the held first piece leaves LDS as whole 1 KB head rows
+    // while the PV waves store the last piece. Written out inside the walk,
+    // these stores slowed every workgroup's reads.
+    if (BAL && hold_first) {
+      float* dst = a.part_o + static_cast<size_t>(id + b) * kH * kD;
+#pragma unroll 4
+      for (int k = 0; k < kHW / 4; ++k) {
+        const int h = 4 * k + w;
+        *reinterpret_cast<float4*>(dst + h * kD + 4 * lane) = bal_hold[h * 65 + lane];
+      }
+    }
   } else {
     // ================= PV waves: online softmax, O^T += V^T . P^T
     constexpr int R = RV;
@@ -949,15 +967,29 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     int ml_slot = 0, ml_par = 0, piece_par = 0;
     auto finish_piece = [&](int row) __attribute__((always_inline)) {
       const size_t slot = static_cast<size_t>(id + row);
+      if (row == b) {                     // the first piece waits in LDS (QK waves store it)
+        float4* hb = bal_hold + c * 65 + 16 * ww + g;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const f32x4_t v = acc[dt][ht];
+            hb[16 * 65 * ht + 4 * dt] = make_float4(v[0], v[1], v[2], v[3]);
+          }
+      } else {
+        float* pb = a.part_o + (slot * kH + c) * kD + 64 * ww + 4 * g;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const f32x4_t v = acc[dt][ht];
+            *reinterpret_cast<float4*>(pb + 16 * ht * kD + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+      }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const f32x4_t v = acc[dt][ht];
-          float* dst = a.part_o + (slot * kH + 16 * ht + c) * kD + 64 * ww + 16 * dt + 4 * g;
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-          acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int dt = 0; dt < 4; ++dt) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const float l = rows4_sum(l_run[ht]);
         if (g == 0) lred2[piece_par][(ht * 16 + c) * 4 + ww] = l;
         m_done[ht] = m_run[ht];

@@ -233,6 +233,13 @@ def test_balanced_separate_combine(gpu_lib, name, n, top, seed):
     off_meta = -(-(off_ml + rows * 8) // 16) * 16
     meta = ws[off_meta:off_meta + B * 8].cpu().numpy().view(np.int32).reshape(B, 2)
     want = _balanced_partition([int(x) for x in inp["seq_lens"]])
+    # pieces per workgroup: the first piece that ends inside a walk is held in
+    # LDS to the end, later ones are stored at once; both cases are present
+    per_wg = {}
+    for p in want:
+        for wg in (range(p[0], p[0] + p[1]) if p else ()):
+            per_wg[wg] = per_wg.get(wg, 0) + 1
+    assert max(per_wg.values()) >= (3 if name == "weighted" else 2)
     for r in range(B):
         if want[r] is None:
             assert meta[r, 1] == 0, r

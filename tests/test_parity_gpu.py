@@ -38,8 +38,8 @@ SMALL = [
     ("bf16-paged", 3, dict(), [1, 62, 63, 64, 65, 127, 300, 777]),
     ("fp8-paged", 4, dict(), [0, 63, 64, 190, 513]),
     ("fp8-contig", 4, dict(paged=False), [255, 70, 3]),
-    # 8 sequences: batch x splits is a multiple of 8, which runs the
-    # two-head-group attention launch (as do the 8 bf16-paged sequences)
+    # 8 sequences: batch x splits is a multiple of 8 and at most 128, so every
+    # split is walked as two halves (as for the 8 bf16-paged sequences)
     ("fp8-paged-8", 4, dict(), [0, 1, 63, 64, 65, 190, 513, 1000]),
 ]
 
@@ -779,6 +779,56 @@ def test_multi_token_decode(gpu_lib, name, base, over, lens, T, splits):
         assert r <= REL_L2_F32
     else:
         check_bf16(got, want, f"multi-token {name} T={T}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_sweep(gpu_lib, seed):
+    """Seeded random configurations against the oracle: cache type (bf16 or
+    FP8), layout (paged or contiguous), 1..24 sequences with a length mix
+    that includes empty, one-token, one-block and block-edge rows, the plan
+    (the library's from the lengths, the balanced partition, or a fixed
+    split count) and 1..3 query tokens."""
+    import decode_attention_02_amd as mfa
+    rng = np.random.default_rng(7000 + seed)
+    base = int(rng.choice([3, 4]))
+    paged = bool(rng.integers(0, 2))
+    B = int(rng.integers(1, 25))
+    top = int(rng.choice([200, 1500, 3000]))
+    lens = [int(x) for x in rng.integers(0, top, size=B)]
+    for e in (0, 1, 63, 64, 65):
+        if rng.random() < 0.3:
+            lens[int(rng.integers(0, B))] = e
+    plan = str(rng.choice(["lib", "balanced", "fixed"]))
+    T = int(rng.choice([1, 1, 2, 3]))
+    w = small(base, batch=B, **({} if paged else dict(paged=False)))
+    inp = workloads.make_inputs(base, workload=w, seed=7100 + seed, prefill_lens=lens, q_len=T)
+    maxlen = int(inp["seq_lens"].max())
+    if plan == "balanced":
+        ns, chunk = 0, None
+    elif plan == "fixed":
+        ns = int(rng.choice([1, 2, 3, 5, 8]))
+        chunk = -(-(-(-max(maxlen, 1) // ns)) // 64) * 64
+    else:
+        ns, chunk = None, None
+    say(f"sweep seed={seed}: base={base} paged={paged} B={B} T={T} plan={plan} ns={ns} "
+        f"lens={lens}")
+    if T == 1:
+        T_, cache, step = setup(inp, num_splits=ns, chunk_tokens=chunk)
+        _, out = run(T_, step)
+        got, want = to_np(out), orun.decode_step(inp)["o"]
+    else:
+        T_, cache, step = setup(inp)
+        mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+        if ns is None:
+            vl = (np.asarray(inp["seq_lens"]).reshape(B, 1) - (T - 1) + np.arange(T)).reshape(-1)
+            ns, chunk = mfa.decode_plan_lens(64, 256, np.maximum(vl, 0), w.kv_dtype)
+            chunk = chunk or None
+        out = mfa.decode_attn_multi(T_["q_multi"], cache, T_["seq_lens"], maxlen,
+                                    num_splits=ns, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        got, want = to_np(out), orun.decode_step_multi(inp)
+    assert np.all(np.isfinite(got))
+    check_bf16(got, want, f"sweep seed={seed}")
 
 
 def test_multi_token_max_query_tokens(gpu_lib):

@@ -1160,7 +1160,8 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
     // two 32 KB FP8 blocks per iteration: the same bytes between barriers as one bf16 block
     hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, false, 2>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2>), grid, block, 0, stream, a);
+    // five K blocks in flight: 4K attention 28.0-28.3 -> 27.3-27.7 us (64K unchanged)
+    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 5, 2>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

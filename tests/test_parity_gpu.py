@@ -875,7 +875,7 @@ def test_multi_token_one_is_single_token(gpu_lib):
 
 # ---------------------------------------------------------------- FP8 queries
 # FP8 caches; 5 and 3 sequences run one workgroup per split, 8 sequences (and
-# 4 x q_len 2) the two-head-group launch; q_len 1, 2 and 4; 1 and 3 splits.
+# 4 x q_len 2) walk each split as two halves; q_len 1, 2 and 4; 1 and 3 splits.
 Q8_CASES = [
     ("paged", dict(), [0, 63, 64, 190, 513], 1),
     ("contig", dict(paged=False), [255, 70, 3], 1),

@@ -221,10 +221,14 @@ mfa_status mfa_decode_plan_lens(int B, int H, int d, const int32_t *seq_lens, in
 /* Bytes of split workspace for mfa_decode_attn / mfa_combine (the split
  * partials of the long-context case, "Step-3 is Large yet Affordable"
  * summary page, §4 Cost Analysis for LLM Decoding: attention cost grows with
- * context and dominates from 8K on). With R = B*num_splits*H rows:
- *   part_o  fp32 [B][num_splits][H][d] unnormalised partial outputs at
- *           offset 0
- *   part_ml fp32 [B][num_splits][H][2] at offset round_up(R*d*4, 256): the
+ * context and dominates from 8K on). Short plans walk every split as two
+ * halves with a partial each: with S = 2*num_splits when B*num_splits*2 <=
+ * 256 and B*num_splits is a multiple of 8, else S = num_splits, and
+ * R = B*S*H rows:
+ *   part_o  fp32 [B][S][H][d] unnormalised partial outputs at offset 0
+ *           (with halves, partial k covers tokens [k*h, (k+1)*h) with
+ *           h = 64*ceil(chunk_tokens/128))
+ *   part_ml fp32 [B][S][H][2] at offset round_up(R*d*4, 256): the
  *           running max m in natural-log units of the scaled logits, then
  *           l = sum_t exp(s_t - m)
  * Total round_up(R*d*4, 256) + R*8 bytes; 0 when num_splits == 1. The

@@ -21,7 +21,9 @@ template <int D, int KT>
 __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
   constexpr int kPer = KT * D / 256;           // K (and V) elements per thread per tile
   __shared__ float q_s[kMaxHD];
-  __shared__ float k_s[KT][D];
+  // K rows padded by one float: the score loop reads k_s[t][j] for the KT
+  // tokens of a wave at once, which without the pad all fall in one bank
+  __shared__ float k_s[KT][D + 1];
   __shared__ float v_s[KT][D];
   __shared__ float p_s[64][KT];
   __shared__ float alpha_s[64], m_s[64], l_s[64];
@@ -102,20 +104,28 @@ __global__ __launch_bounds__(256) void mfa_decode_valu_kernel(AttnArgs a) {
       p_s[h][t] = s;
     }
     __syncthreads();
-    if (tid < H) {
-      const int h = tid;
-      float mx = m_s[h];
-      for (int t = 0; t < n; ++t) mx = fmaxf(mx, p_s[h][t]);
-      const float al = expf(m_s[h] - mx);
-      float sum = 0.f;
-      for (int t = 0; t < KT; ++t) {
-        const float p = t < n ? expf(p_s[h][t] - mx) : 0.f;
-        p_s[h][t] = p;
-        sum += p;
+    // online softmax of the tile, one thread per (head, token): the KT
+    // threads of a head are adjacent lanes of one wave (KT divides 64), so
+    // the tile's max and sum are butterfly reductions over them
+    for (int i = tid; i < H * KT; i += 256) {
+      const int h = i / KT, t = i % KT;
+      const float s = p_s[h][t];                      // -inf past the end
+      float mx = s;
+#pragma unroll
+      for (int off = 1; off < KT; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mold = m_s[h];
+      mx = fmaxf(mx, mold);
+      const float p = t < n ? expf(s - mx) : 0.f;
+      float sum = p;
+#pragma unroll
+      for (int off = 1; off < KT; off <<= 1) sum += __shfl_xor(sum, off);
+      p_s[h][t] = p;
+      if (t == 0) {
+        const float al = expf(mold - mx);
+        l_s[h] = l_s[h] * al + sum;
+        m_s[h] = mx;
+        alpha_s[h] = al;
       }
-      l_s[h] = l_s[h] * al + sum;
-      m_s[h] = mx;
-      alpha_s[h] = al;
     }
     __syncthreads();
 #pragma unroll

@@ -489,17 +489,19 @@ mfa_status mfa_decode_plan(int B, int H, int d, int max_seq_len, int kv_dtype, i
                            int* chunk_tokens) {
   if (!num_splits || !chunk_tokens) return MFA_ERR_NULL;
   if (B < 1 || H < 1 || d < 1 || max_seq_len < 0) return MFA_ERR_SHAPE;
-  (void)kv_dtype;
   const int blocks = (max_seq_len + kBlock - 1) / kBlock;
   // One 8-wave attention workgroup per compute unit of an MI355X (256 CUs):
   // split each sequence so that the grid covers the chip once, with splits
-  // of whole 128-token tiles (two cache blocks).
+  // of whole 128-token tiles (two cache blocks) for the matrix-core kernel
+  // and of single blocks for the vector kernel (whose workgroups walk their
+  // tokens 16 or 32 at a time: a short sequence is better spread out).
+  const int gran = mfma_shape(H, d, kv_dtype) ? 2 : 1;
   constexpr int kTargetWorkgroups = 256;
   int splits = kTargetWorkgroups / B;
   if (splits < 1) splits = 1;
-  if (splits > blocks / 2) splits = blocks / 2 > 0 ? blocks / 2 : 1;
-  int per = blocks > 0 ? (blocks + splits - 1) / splits : 2;
-  per = (per + 1) / 2 * 2;
+  if (splits > blocks / gran) splits = blocks / gran > 0 ? blocks / gran : 1;
+  int per = blocks > 0 ? (blocks + splits - 1) / splits : gran;
+  per = (per + gran - 1) / gran * gran;
   splits = blocks > 0 ? (blocks + per - 1) / per : 1;
   *num_splits = splits;
   *chunk_tokens = per * kBlock;

@@ -182,6 +182,11 @@ def test_plan_and_split_workspace(lib):
         assert lib.mfa_decode_plan(B, 64, 256, L, BF16, ctypes.byref(ns), ctypes.byref(ch)) == OK
         assert ns.value >= 1 and ch.value % 64 == 0 and ns.value * ch.value >= L
     assert lib.mfa_decode_plan(0, 64, 256, 10, BF16, ctypes.byref(ns), ctypes.byref(ch)) == SHAPE
+    # the matrix-core kernel gets splits of two blocks, the vector kernel of one
+    for B, L, H, d, dt, want in ((2, 129, 4, 64, F32, (3, 64)), (2, 129, 64, 256, BF16, (1, 256)),
+                                 (1, 4096, 64, 256, BF16, (32, 128)), (1, 4096, 8, 128, F32, (64, 64))):
+        assert lib.mfa_decode_plan(B, H, d, L, dt, ctypes.byref(ns), ctypes.byref(ch)) == OK
+        assert (ns.value, ch.value) == want, (B, L, H, d, dt, ns.value, ch.value)
     assert lib.mfa_decode_workspace_bytes(4, 64, 256, 1) == 0
     rows = 16 * 16 * 64                          # 16 rows x 16 splits: one partial per split
     assert lib.mfa_decode_workspace_bytes(16, 64, 256, 16) == rows * 256 * 4 + rows * 2 * 4

@@ -831,6 +831,46 @@ def test_random_sweep(gpu_lib, seed):
     check_bf16(got, want, f"sweep seed={seed}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_sweep_vector_kernel(gpu_lib, seed):
+    """Seeded random configurations of the fp32 path (the vector-ALU kernel):
+    head count and width, paged or contiguous, 1..12 sequences with planted
+    edge lengths, the library's plan or fixed splits, 1..2 query tokens;
+    fp32 bar against the oracle."""
+    import decode_attention_02_amd as mfa
+    rng = np.random.default_rng(7500 + seed)
+    H, d = [(4, 64), (8, 128), (64, 64), (16, 256), (32, 256)][int(rng.integers(0, 5))]
+    paged = bool(rng.integers(0, 2))
+    B = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, int(rng.choice([150, 700])), size=B)]
+    for e in (0, 1, 31, 32, 63, 64, 65):
+        if rng.random() < 0.3:
+            lens[int(rng.integers(0, B))] = e
+    T = int(rng.choice([1, 2]))
+    fixed = bool(rng.integers(0, 2))
+    w = small(3, batch=B, kv_dtype="f32", act_dtype="f32", heads=H, head_dim=d,
+              **({} if paged else dict(paged=False)))
+    inp = workloads.make_inputs(3, workload=w, seed=7600 + seed, prefill_lens=lens, q_len=T)
+    maxlen = int(inp["seq_lens"].max())
+    ns, chunk = None, None
+    if fixed:
+        ns = int(rng.choice([2, 3, 5]))
+        chunk = -(-(-(-max(maxlen, 1) // ns)) // 64) * 64
+    say(f"vector sweep seed={seed}: H={H} d={d} paged={paged} B={B} T={T} ns={ns} lens={lens}")
+    T_, cache, step = setup(inp)
+    mfa.kv_append(cache, T_["k_new"], T_["v_new"], T_["prefill_lens"])
+    if ns is None:
+        ns, chunk = mfa.decode_plan(B * T, H, d, max(maxlen, 1), "f32")
+    out = mfa.decode_attn_multi(T_["q_multi"] if T > 1 else T_["q"].unsqueeze(1), cache,
+                                T_["seq_lens"], maxlen, num_splits=ns, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    want = orun.decode_step_multi(inp) if T > 1 else orun.decode_step(inp)["o"][:, None]
+    r = rel_l2(got, want)
+    say(f"vector sweep seed={seed}: rel_l2={r:.3e}")
+    assert np.all(np.isfinite(got)) and r <= REL_L2_F32, (seed, r)
+
+
 def test_multi_token_max_query_tokens(gpu_lib):
     """q_len = 16, the most the library takes, with sequences shorter than
     q_len (their first queries see nothing), 2 splits."""

@@ -119,8 +119,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // with its own partial (o, m, l) in slot (workgroup + row). At the first
 // block of a new piece the QK waves switch Q (loaded into registers one
 // piece ahead) behind one extra barrier that both roles pass, and the PV
-// waves write out the finished piece's o, then its (m, l) one iteration
-// later, once the four PV waves' row sums have met in LDS.
+// waves put the finished piece's o into LDS (the workgroup's first piece,
+// stored by the QK waves at the end: partials written during the walk slow
+// the reads of every workgroup) or store it (later pieces, rare), then its
+// (m, l) one iteration later, once the four PV waves' row sums have met.
 template <bool FP8, int RK, int RV, bool Q8 = false, int BPI = 1, bool BAL = false>
 __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   constexpr int HT = 4;                 // 16-head tiles: every workgroup holds all 64 heads

@@ -119,6 +119,10 @@ BAL = [
     ("fp8-contig-24", 4, dict(batch=24, paged=False), _ragged(24, 94, top=3000)),
     # long rows next to 1-token rows: pieces of one block between long ones
     ("bf16-paged-mix", 3, dict(batch=12), [5000, 0, 1, 3000, 63, 64, 1, 7000, 2, 130, 4000, 0]),
+    # the most rows the partition takes (1024, two per setup thread), short
+    # rows with empty ones, and one long row that spans many workgroups
+    ("bf16-paged-1024", 3, dict(batch=1024), _ragged(1023, 95, top=300) + [9000]),
+    ("fp8-paged-1024", 4, dict(batch=1024), [9000] + _ragged(1023, 96, top=300)),
 ]
 
 

@@ -364,13 +364,16 @@ def test_split_counts_agree(gpu_lib):
         assert rel_l2(res[s], res[1]) <= 2 * REL_L2_BF16
 
 
-@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-def test_combine_standalone(gpu_lib, out_dtype):
+@pytest.mark.parametrize("out_dtype,S", [("f32", 20), ("bf16", 20), ("f32", 2), ("f32", 9),
+                                         ("bf16", 64)])
+def test_combine_standalone(gpu_lib, out_dtype, S):
     """mfa_combine on drawn fp32 partials (some splits empty) against the
-    oracle's log-sum-exp merge, into fp32 and bf16 outputs."""
+    oracle's log-sum-exp merge, into fp32 and bf16 outputs. Three rows fill
+    few workgroups, so 9 and more splits are shared by four thread groups
+    per head (9: runs of 3, 3, 3 and none; 20: 5 each; 64: 16 each)."""
     import decode_attention_02_amd as mfa
-    rng = np.random.default_rng(77)
-    B, S, H, d = 3, 20, 64, 256                # 20 splits: two load batches
+    rng = np.random.default_rng(77 + S)
+    B, H, d = 3, 64, 256
     o = rng.standard_normal((B, S, H, d)).astype(np.float32)
     m = (rng.standard_normal((B, S, H)) * 3).astype(np.float32)
     l = rng.uniform(0.5, 40, size=(B, S, H)).astype(np.float32)

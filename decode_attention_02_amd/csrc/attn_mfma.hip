@@ -183,6 +183,15 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     // than 4 blocks per workgroup the cost is the block count alone (U = 1,
     // no row-start charge) and only min(blocks, workgroups) workgroups run.
     const int rows = a.bal_rows;
+    // both lengths are read before either is stored: a store to LDS between
+    // them kept the second read waiting for the first (a generic pointer
+    // may alias LDS), two memory latencies instead of one
+    int sl[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * tid + e;
+      sl[e] = r < rows ? a.seq_lens[r / ql] : 0;
+    }
     int nb2[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       int Lr = 0;
       if (r < rows) {
         const int sq = r / ql;
-        Lr = a.seq_lens[sq] - (ql - 1 - (r - sq * ql));
+        Lr = sl[e] - (ql - 1 - (r - sq * ql));
         Lr = Lr < 0 ? 0 : (Lr > a.max_seq_len ? a.max_seq_len : Lr);
         bal_len[r] = Lr;
       }

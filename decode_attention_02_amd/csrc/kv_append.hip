@@ -120,17 +120,22 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
 }
 
 // Decode-step append (one new token per sequence): one wave per sequence.
-template <int CACHE, int EPT>   // CACHE: 0 f32, 1 bf16, 2 fp8
+template <int CACHE, int EPT, bool INF32>   // CACHE: 0 f32, 1 bf16, 2 fp8
 __global__ __launch_bounds__(64) void kv_append_one_kernel(AppendArgs a) {
-  append_token_wave<CACHE, EPT>(a, blockIdx.x, threadIdx.x);
+  append_token_wave<CACHE, EPT, INF32>(a, blockIdx.x, threadIdx.x);
 }
 
+template <int CACHE, bool INF32>
+static void launch_one_in(const AppendArgs& a, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(a.B)), block(64);
+  if (a.d == 64) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 1, INF32>), grid, block, 0, stream, a);
+  else if (a.d == 128) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 2, INF32>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 4, INF32>), grid, block, 0, stream, a);
+}
 template <int CACHE>
 static void launch_one(const AppendArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.B)), block(64);
-  if (a.d == 64) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 1>), grid, block, 0, stream, a);
-  else if (a.d == 128) hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 2>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((kv_append_one_kernel<CACHE, 4>), grid, block, 0, stream, a);
+  if (a.in_f32) launch_one_in<CACHE, true>(a, stream);
+  else launch_one_in<CACHE, false>(a, stream);
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {

@@ -676,6 +676,56 @@ def test_fused_step_matches_staged(gpu_lib, idx, shrink):
         assert np.array_equal(a, b)
 
 
+# The step without a query path (KV append, then attention and combine)
+# against the separate calls, with the new token either the last attended
+# one ("next": seq_len = pos + 1) or not attended ("behind": seq_len = pos,
+# so the token lands in a walked block past the length, or, when pos is a
+# multiple of 64 or the row is empty, in a block no workgroup reads).
+STEP_POSITIONS = [
+    ("bf16-paged-bal", 3, dict(batch=12), [5000, 0, 1, 3000, 63, 64, 1, 7000, 2, 130, 4000, 0],
+     "next", 0),
+    ("bf16-paged-bal-behind", 3, dict(batch=12),
+     [5000, 0, 1, 3000, 63, 64, 1, 7000, 2, 128, 4000, 0], "behind", 0),
+    ("bf16-paged-bal-1024", 3, dict(batch=1024), _ragged(1023, 97, top=300) + [9000], "next", 0),
+    ("bf16-paged-bal-empty", 3, dict(batch=5), [0, 0, 0, 0, 0], "behind", 0),
+    ("bf16-contig-split", 3, dict(paged=False), [0, 63, 200], "next", 3),
+    ("bf16-contig-split-behind", 3, dict(paged=False), [0, 64, 200], "behind", 3),
+    ("bf16-paged-unsplit", 3, dict(), [1, 62, 63, 64, 65, 127, 300, 777], "next", 1),
+    ("fp8-paged-split", 4, dict(), [0, 63, 64, 190, 513], "next", 3),
+    ("fp8-paged-bal", 4, dict(batch=40), _ragged(40, 98), "next", 0),
+    ("fp8-contig-split-behind", 4, dict(paged=False), [64, 70, 3, 128], "behind", 2),
+]
+
+
+@pytest.mark.parametrize("name,base,over,lens,mode,splits", STEP_POSITIONS,
+                         ids=[c[0] for c in STEP_POSITIONS])
+def test_step_positions_match_staged(gpu_lib, name, base, over, lens, mode, splits):
+    """mfa_decode_step without a query path against the separate calls
+    (mfa_kv_append, then attention and combine): bit-identical outputs and
+    cache contents (codes and scales); with the token attended, also within
+    the bars of the oracle step."""
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=331 + base)
+    say(f"step positions {name} mode={mode} splits={splits}")
+    outs, caches = [], []
+    for fused in (True, False):
+        T, cache, step = setup(inp, num_splits=splits)
+        seq = T["seq_lens"] if mode == "next" else T["prefill_lens"].clone()
+        fn = step if fused else step.staged
+        out = fn(T["k_new"], T["v_new"], T["prefill_lens"], seq, q=T["q"])
+        torch.cuda.synchronize()
+        outs.append(out.detach().cpu().clone())
+        rows = list(cache_rows(cache))
+        if cache.dtype == "fp8":
+            rows += [cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()]
+        caches.append(rows)
+    assert torch.equal(outs[0].view(torch.uint8), outs[1].view(torch.uint8))
+    for a, b in zip(*caches):
+        assert np.array_equal(a, b)
+    if mode == "next":
+        check_bf16(to_np(outs[0]), orun.decode_step(inp)["o"], f"step positions {name}")
+
+
 @pytest.mark.parametrize("idx,shrink,packed", [
     (2, dict(batch=6, hidden=1024, q_rank=512, context=300), False),
     (2, dict(batch=6, hidden=1024, q_rank=512, context=300), True),

@@ -364,16 +364,19 @@ def test_split_counts_agree(gpu_lib):
         assert rel_l2(res[s], res[1]) <= 2 * REL_L2_BF16
 
 
-@pytest.mark.parametrize("out_dtype,S", [("f32", 20), ("bf16", 20), ("f32", 2), ("f32", 9),
-                                         ("bf16", 64)])
-def test_combine_standalone(gpu_lib, out_dtype, S):
+@pytest.mark.parametrize("out_dtype,S,H,d", [("f32", 20, 64, 256), ("bf16", 20, 64, 256),
+                                             ("f32", 2, 64, 256), ("f32", 9, 64, 256),
+                                             ("bf16", 64, 64, 256), ("f32", 20, 4, 64),
+                                             ("f32", 9, 8, 128), ("f32", 33, 32, 256)])
+def test_combine_standalone(gpu_lib, out_dtype, S, H, d):
     """mfa_combine on drawn fp32 partials (some splits empty) against the
     oracle's log-sum-exp merge, into fp32 and bf16 outputs. Three rows fill
     few workgroups, so 9 and more splits are shared by four thread groups
-    per head (9: runs of 3, 3, 3 and none; 20: 5 each; 64: 16 each)."""
+    per head (9: runs of 3, 3, 3 and none; 20: 5 each; 33: 9, 9, 9, 6; 64: 16
+    each), also at head widths 64 and 128 (16 and 32 threads per head)."""
     import decode_attention_02_amd as mfa
-    rng = np.random.default_rng(77 + S)
-    B, H, d = 3, 64, 256
+    rng = np.random.default_rng(77 + S + d)
+    B = 3
     o = rng.standard_normal((B, S, H, d)).astype(np.float32)
     m = (rng.standard_normal((B, S, H)) * 3).astype(np.float32)
     l = rng.uniform(0.5, 40, size=(B, S, H)).astype(np.float32)

@@ -245,6 +245,31 @@ __device__ __forceinline__ void append_token_wave(const AppendArgs& a, int b, in
   store_token_v<CACHE, EPT>(a, ts, xv, sv, lane);
 }
 
+// Token pos[b] of sequence b (n_new == 1) from k_new / v_new, no
+// projection: the same reads, arithmetic and stores as append_token_wave.
+template <int CACHE, int EPT, bool INF32>
+__device__ __forceinline__ void append_token_plain(const AppendArgs& a, int b, int lane) {
+  const RowPiece<EPT, INF32> rk = load_row_piece<EPT, INF32>(a.k_new, b, a.d, lane);
+  const RowPiece<EPT, INF32> rv = load_row_piece<EPT, INF32>(a.v_new, b, a.d, lane);
+  const int p0 = a.pos[b];
+  const TokenSlot ts = token_slot_of(a, token_block_raw(a, b, p0), p0);
+  if (ts.id < 0) return;
+  float xk[EPT], xv[EPT];
+  row_piece_f32(rk, xk);
+  row_piece_f32(rv, xv);
+  float sk = 1.f, sv = 1.f;
+  if constexpr (CACHE == 2) {
+    sk = token_scale(xk);
+    sv = token_scale(xv);
+    if (lane == 0) {
+      a.k_scale[static_cast<size_t>(ts.id) * kBlockTokens + ts.off] = sk;
+      a.v_scale[static_cast<size_t>(ts.id) * kBlockTokens + ts.off] = sv;
+    }
+  }
+  store_token_k<CACHE, EPT>(a, ts, xk, sk, lane);
+  store_token_v<CACHE, EPT>(a, ts, xv, sv, lane);
+}
+
 // Runtime dispatch over cache dtype, head dim and input dtype.
 template <bool INF32>
 __device__ __forceinline__ void append_token_in(const AppendArgs& a, int b, int lane) {

@@ -53,6 +53,7 @@
 // logits are scaled by the K and q scales. The PV side is unchanged.
 #include <type_traits>
 
+#include "append_one.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -123,10 +124,26 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
 // stored by the QK waves at the end: partials written during the walk slow
 // the reads of every workgroup) or store it (later pieces, rare), then its
 // (m, l) one iteration later, once the four PV waves' row sums have met.
-template <bool FP8, int RK, int RV, bool Q8 = false, int BPI = 1, bool BAL = false>
-__global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
+// APP (split walk): the decode step's KV append (one new token per row,
+// bf16 input) in the same launch. The workgroup whose split walks the
+// token's block writes the token before its waves read the block: the QK
+// wave that loads the token's K rows reads the token together with Q,
+// stores K (and the FP8 scales) before it issues the ring unit holding the
+// block, and passes V (with its slot and scale) through LDS to the PV
+// waves, which store their features of it after the Q barrier, before their
+// first V loads. A wave's memory operations take effect in its program
+// order, so its later loads of the block see its own stores. A token in a
+// block past the row's length has no reader in the launch; the row's first
+// split writes it whole. (The balanced walk keeps the separate append: there
+// the extra work at the start of the owning workgroups cost more than the
+// launch it saves.)
+template <bool FP8, int RK, int RV, bool Q8 = false, int BPI = 1, bool BAL = false,
+          bool APP = false>
+__global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(
+    std::conditional_t<APP, AttnAppArgs, AttnArgs> a) {
   constexpr int HT = 4;                 // 16-head tiles: every workgroup holds all 64 heads
   static_assert(!Q8 || FP8, "FP8 queries run against FP8 caches");
+  static_assert(!APP || (!Q8 && !BAL), "in-launch append: split walk, bf16 queries");
   static_assert(BPI == 1 || (BPI == 2 && !Q8), "two blocks per iteration: plain FP8 and bf16 only");
   static_assert(!BAL || (BPI == 1 && !Q8), "balanced walk: one block per unit");
   using C = Cfg<FP8>;
@@ -154,6 +171,9 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float4 bal_hold[BAL ? kHW * 65 : 1];
   int* const bal_cpfx = reinterpret_cast<int*>(bal_hold);
   int* const bal_rc = bal_cpfx + kBalancedMaxRows + 4;
+  // APP: the V hand-off slot (QK wave -> PV waves): the token's block id,
+  // offset and FP8 V scale, then its 256 bf16 V values
+  __shared__ __attribute__((aligned(16))) uint32_t app_lds[APP ? 4 + kD / 2 : 1];
   __shared__ int bal_wsum[20];
   __shared__ __attribute__((aligned(16))) float lred2[2][BAL ? kHW * 4 : 4];
 
@@ -171,6 +191,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int ql = a.q_len > 0 ? a.q_len : 1;
   int split = 0, b = 0, bs = 0, t1 = 0, blk0 = 0, N = 0;
+  int nbl = 0, app_p = -1;              // APP: the row's blocks, its new token's position
   int lo = 0, hi = 0;                   // balanced walk: the workgroup's global block range
   bool hold_first = false;              // balanced walk: its first piece ends inside the walk
   if constexpr (BAL) {
@@ -340,6 +361,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     t1 = min(t0 + a.chunk_tokens, L);
     blk0 = t0 >> 6;
     N = t0 < t1 ? ((t1 + kBlockTokens - 1) >> 6) - blk0 : 0;            // blocks to walk
+    nbl = (L + kBlockTokens - 1) >> 6;
+    if constexpr (APP) app_p = ((const __attribute__((address_space(4))) int*)a.app.pos)[bs];
   }
   constexpr int h0 = 0;                                                 // first head
   // iterations walk units of BPI consecutive blocks (a unit's second block
@@ -411,7 +434,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   };
   // prologue of either role: the QK waves load Q, then ring blocks 0 .. R-1,
   // then stage Q; the PV waves fill their ring after the Q barrier
-  auto prologue_qk = [&](auto r_c, auto&& issue) __attribute__((always_inline)) {
+  auto prologue_qk = [&](auto r_c, auto&& issue, auto&& pre, auto&& mid) __attribute__((always_inline)) {
     constexpr int RR = decltype(r_c)::value;
     if (N > 0) {
       // named registers, not an array: an array held across the scheduling
@@ -419,8 +442,12 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       uint4 q0, q1, q2, q3, q4, q5, q6, q7;
       q0 = *q_src(b, 0); q1 = *q_src(b, 1); q2 = *q_src(b, 2); q3 = *q_src(b, 3);
       q4 = *q_src(b, 4); q5 = *q_src(b, 5); q6 = *q_src(b, 6); q7 = *q_src(b, 7);
+      pre();
       __builtin_amdgcn_sched_barrier(0);
-      static_for<0, RR>([&](auto rc) { issue(rc, decltype(rc)::value); });
+      static_for<0, RR>([&](auto rc) {
+        mid(decltype(rc)::value);
+        issue(rc, decltype(rc)::value);
+      });
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (Q8) {
         const uint4 qv[8] = {q0, q1, q2, q3, q4, q5, q6, q7};
@@ -512,6 +539,18 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   // bf16 outputs leave through LDS as whole 512-byte head rows (end of the
   // kernel); fp32 outputs and the fp32 split partials are stored directly
   const bool stage_out = !partial && !a.out_f32;
+
+  // In-launch append (APP): f(r, p, n) for the workgroup's row when its new
+  // token (position p) lies in block n of this split's walk; g(r) for the
+  // row in the row's first split when the token lies in no walked block.
+  constexpr int kCache = FP8 ? 2 : 1;
+  auto for_owned = [&](auto&& f) __attribute__((always_inline)) {
+    const int j = app_p >> 6;
+    if (app_p >= 0 && j >= blk0 && j < blk0 + N) f(b, app_p, j - blk0);
+  };
+  auto for_orphans = [&](auto&& g) __attribute__((always_inline)) {
+    if (split == 0 && app_p >= 0 && (app_p >> 6) >= nbl) g(b);
+  };
 
   // Every wave passes the same barriers: one after staging Q, one per
   // iteration i = 0 .. NU+1 (NU units of BPI blocks), one before the epilogue (and one more before the
@@ -689,10 +728,96 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
       red[par][(g * 16 + c) * 4 + ww] = rows4_max_t4(mt[0], mt[1], mt[2], mt[3]);
     };
 
+    // APP: the new token, when this wave loads its K row (token rows 16ww ..
+    // 16ww+15 of the block). Its K, V and table entry are read together
+    // with Q, as raw words (any use of them before the ring loads would hold
+    // those behind their latency); the table entry by a scalar load (a
+    // vector one would be waited for at once to move the uniform value into
+    // a scalar register). The wave stores K before it issues the ring unit
+    // holding the token.
+    auto own_k = [&](auto&& f) __attribute__((always_inline)) {
+      for_owned([&](int r, int p, int n) {
+        if (((p & 63) >> 4) == ww) f(r, p, n);
+      });
+    };
+    uint2 akw = make_uint2(0u, 0u), avw = make_uint2(0u, 0u);
+    int a_r = -1, a_u = 0, a_p = 0, a_tab = 0;
+    bool a_done = true;
+    auto app_pre = [&]() __attribute__((always_inline)) {
+      if constexpr (APP) {
+        int n0 = 0;
+        own_k([&](int r, int p, int n) {
+          a_r = r;
+          a_p = p;
+          n0 = n;
+        });
+        // issued whether or not the wave owns a token (row 0 then): no branch
+        a_done = a_r < 0;
+        a_u = n0 / BPI;
+        const int rr = a_r >= 0 ? a_r : 0;
+        const size_t i = static_cast<size_t>(rr) * kD + 4 * lane;
+        akw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.app.k_new) + i);
+        avw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.app.v_new) + i);
+        // an owner walks the token's block, so (a_p >> 6) is a block of the table row
+        const int* tp = a.app.block_table
+                            ? a.app.block_table + static_cast<size_t>(rr) * a.app.max_blocks_per_seq +
+                                  (a_r >= 0 ? (a_p >> 6) : 0)
+                            : a.app.pos;
+        a_tab = *(const __attribute__((address_space(4))) int*)tp;
+      }
+    };
+    // the token: K (FP8: codes and both scales) to the cache; V, its slot
+    // and its FP8 scale to the hand-off slot (the PV waves store V)
+    auto app_store = [&]() __attribute__((always_inline)) {
+      if constexpr (APP) {
+        {
+          const int r = a_r, p = a_p;
+          RowPiece<4, false> rk, rv;
+          rk.w[0] = akw.x; rk.w[1] = akw.y;
+          rv.w[0] = avw.x; rv.w[1] = avw.y;
+          const TokenSlot ts =
+              token_slot_of(a.app, a.app.block_table ? a_tab : r * a.app.max_blocks_per_seq + (p >> 6), p);
+          float sv = 1.f;
+          if (ts.id >= 0) {
+            float xk[4];
+            row_piece_f32(rk, xk);
+            float sk = 1.f;
+            if constexpr (FP8) {
+              float xv[4];
+              row_piece_f32(rv, xv);
+              sk = token_scale(xk);
+              sv = token_scale(xv);
+              if (lane == 0) {
+                a.app.k_scale[static_cast<size_t>(ts.id) * kBlockTokens + ts.off] = sk;
+                a.app.v_scale[static_cast<size_t>(ts.id) * kBlockTokens + ts.off] = sv;
+              }
+            }
+            store_token_k<kCache, 4>(a.app, ts, xk, sk, lane);
+          }
+          if (lane == 0) {
+            app_lds[0] = static_cast<uint32_t>(ts.id);
+            app_lds[1] = static_cast<uint32_t>(ts.off);
+            app_lds[2] = __float_as_uint(sv);
+          }
+          app_lds[4 + 2 * lane] = rv.w[0];
+          app_lds[5 + 2 * lane] = rv.w[1];
+        }
+        a_done = true;
+      }
+    };
+    auto app_mid = [&](int u) __attribute__((always_inline)) {
+      if constexpr (APP) {
+        if (!a_done && u == a_u) app_store();
+      }
+    };
+
     // Every iteration issues the same loads (empty ones past the walk), so
     // every path into a consumer has the same loads in flight and the wait
     // before it leaves R-1 blocks outstanding.
-    prologue_qk(std::integral_constant<int, R>{}, issue);
+    prologue_qk(std::integral_constant<int, R>{}, issue, app_pre, app_mid);
+    if constexpr (APP) {
+      if (!a_done) app_store();          // the first unit holding one comes after the prologue
+    }
     __syncthreads();   // Q staged
     if constexpr (Q8) {
 #pragma unroll
@@ -1044,6 +1169,25 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
     };
 
     __syncthreads();   // Q staged
+    if constexpr (APP) {
+      // V features 64ww .. 64ww+63 of the workgroup's new token (this
+      // wave's own V columns), from the hand-off slot, stored before this
+      // wave's first V loads. A token in no walked block is written whole by
+      // wave 4 (nothing in the launch reads it).
+      for_owned([&](int, int, int) {
+        float xv[4];
+        TokenSlot ts;
+        ts.id = static_cast<int>(app_lds[0]);
+        ts.off = static_cast<int>(app_lds[1]);
+        const float sv = __uint_as_float(app_lds[2]);
+        RowPiece<4, false> rv;
+        rv.w[0] = app_lds[4 + 2 * lane];
+        rv.w[1] = app_lds[5 + 2 * lane];
+        row_piece_f32(rv, xv);
+        if (ts.id >= 0 && (lane >> 4) == ww) store_token_v<kCache, 4>(a.app, ts, xv, sv, lane);
+      });
+      if (ww == 0) for_orphans([&](int r) { append_token_plain<kCache, 4, false>(a.app, r, lane); });
+    }
     prologue_pv(std::integral_constant<int, R>{}, issue);
     __syncthreads();   // iteration 0 (S of unit 0 on the QK waves)
     piece_barrier(1);
@@ -1154,12 +1298,21 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream) {
+hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream,
+                              const AppendArgs* app) {
+  if (app && (a.num_splits == 0 || a.q_len != 1 || a.fp8_queries || app->in_f32 || app->n_new != 1 ||
+              app->kv_part || app->d != kD))
+    return hipErrorInvalidValue;
+  AttnAppArgs aa;
+  static_cast<AttnArgs&>(aa) = a;
+  if (app) aa.app = *app;
   if (a.num_splits == 0) {
     // balanced partition: one workgroup per compute unit
     const dim3 grid(kBalancedWorkgroups), block(512);
-    if (fp8) hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, false, 1, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, false, 1, true>), grid, block, 0, stream, a);
+    if (fp8)
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, false, 1, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 3, 2, false, 1, true>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
   // one workgroup of 64 heads per (row, split); short plans already walk
@@ -1169,10 +1322,16 @@ hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t st
     hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 4, 4, true>), grid, block, 0, stream, a);
   } else if (fp8) {
     // two 32 KB FP8 blocks per iteration: the same bytes between barriers as one bf16 block
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, false, 2>), grid, block, 0, stream, a);
+    if (app)
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, false, 2, false, true>), grid, block, 0, stream, aa);
+    else
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<true, 2, 2, false, 2>), grid, block, 0, stream, a);
   } else {
     // five K blocks in flight: 4K attention 28.0-28.3 -> 27.3-27.7 us (64K unchanged)
-    hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 5, 2>), grid, block, 0, stream, a);
+    if (app)
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 5, 2, false, 1, false, true>), grid, block, 0, stream, aa);
+    else
+      hipLaunchKernelGGL((mfa_decode_mfma_kernel<false, 5, 2>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -54,8 +54,7 @@ struct AttnArgs {
   int fp8_queries;
 };
 
-// B: virtual rows (sequences x q_len).
-hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream);
+
 hipError_t launch_decode_valu(const AttnArgs& a, int B, hipStream_t stream);
 
 // meta (nullable): per row (first partial slot, slot count), the balanced
@@ -98,6 +97,19 @@ struct AppendArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
+// Matrix-core kernel with the decode step's KV append in the same launch
+// (q_len == 1, one token per row, app.n_new == 1, bf16 k_new / v_new, no
+// projection): the workgroup that walks a token's block writes the token
+// before its waves read that block.
+struct AttnAppArgs : AttnArgs {
+  AppendArgs app;
+};
+
+// B: virtual rows (sequences x q_len). app (nullable): the decode step's KV
+// append, done in the same launch.
+hipError_t launch_decode_mfma(const AttnArgs& a, bool fp8, int B, hipStream_t stream,
+                              const AppendArgs* app = nullptr);
 
 // Query path.
 // bf16: C[m][n] = A[M][K] . W[N][K]^T, M <= 128. With ksplit > 1 writes fp32

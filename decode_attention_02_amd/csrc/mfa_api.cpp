@@ -662,9 +662,11 @@ mfa_status prepare_attn(const void* q, int q_dtype, int B, int H, const mfa_kv_c
   return MFA_OK;
 }
 
-mfa_status launch_attn(const AttnCall& c, hipStream_t st) {
+// app (nullable, matrix-core kernel only): the decode step's KV append,
+// done inside the attention launch.
+mfa_status launch_attn(const AttnCall& c, hipStream_t st, const mfa::AppendArgs* app = nullptr) {
   const mfa::AttnArgs& a = c.a;
-  hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st) : mfa::launch_decode_valu(a, c.B, st);
+  hipError_t e = c.mfma ? mfa::launch_decode_mfma(a, c.fp8, c.B, st, app) : mfa::launch_decode_valu(a, c.B, st);
   if (e != hipSuccess) return MFA_ERR_HIP;
   if (c.num_splits != 1 && c.out) {
     e = mfa::launch_combine(a.part_o, a.part_ml, a.bal_meta, c.B, c.H, c.d, c.num_splits, c.out,
@@ -802,6 +804,8 @@ mfa_status mfa_decode_step(const mfa_step_args* s, void* stream) {
   if (has_qproj) {
     st = launch_qproj(qc, &ap, hs);            // the append rides in the RMSNorm launch
     if (st != MFA_OK) return st;
+  } else if (ac.mfma && !ap.in_f32 && ac.a.num_splits != 0) {
+    return launch_attn(ac, hs, &ap);           // split walk: the append rides in the attention launch
   } else if (mfa::launch_kv_append(ap, hs) != hipSuccess) {
     return MFA_ERR_HIP;
   }

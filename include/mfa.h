@@ -409,7 +409,10 @@ mfa_status mfa_out_proj(const void *o, const void *w_o, int weight_layout, int B
  * with the same arguments, in that order, and with the same results.
  * It exists so the stages can share launches: with a query path, the KV
  * append runs inside the query path's normalisation launch instead of on
- * its own.
+ * its own; without one, with bf16 k_new / v_new and a split plan
+ * (num_splits >= 1) on the matrix-core kernel (H = 64, d = 256), inside
+ * the attention launch (the workgroup that reads the token's block writes
+ * the token first). The balanced plan keeps its own append launch.
  * Every stage's arguments are checked (as by the separate calls) before
  * anything is launched.
  *   B, H, d      batch, query heads, head dim (d must equal cache->head_dim)

@@ -697,6 +697,9 @@ STEP_POSITIONS = [
     ("fp8-paged-split", 4, dict(), [0, 63, 64, 190, 513], "next", 3),
     ("fp8-paged-bal", 4, dict(batch=40), _ragged(40, 98), "next", 0),
     ("fp8-contig-split-behind", 4, dict(paged=False), [64, 70, 3, 128], "behind", 2),
+    ("bf16-paged-split-behind", 3, dict(), [0, 64, 128, 200, 4095, 4096], "behind", 4),
+    ("bf16-paged-split-8", 3, dict(), [5, 1000, 3000, 9000], "next", 8),
+    ("fp8-paged-split-8", 4, dict(), [1, 700, 4000, 8191], "next", 8),
 ]
 
 

@@ -42,7 +42,7 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=True,
-          poison=False):
+          poison=False, out_dtype=None):
     """Upload inputs, allocate + prefill the cache, build the decode step.
     ``poison``: fill every byte of the cache (and FP8 scales) with 0xFF
     before the prefill, so slots no token was written to hold NaNs."""
@@ -63,7 +63,8 @@ def setup(inp, device="cuda", num_splits=None, chunk_tokens=None, zero_cache=Tru
         num_splits = w.num_splits
     step = DecodeStep(cache, w.batch, w.heads, int(inp["seq_lens"].max()), hidden=w.hidden,
                       q_rank=w.q_rank, act_dtype=act, num_splits=num_splits,
-                      chunk_tokens=chunk_tokens, seq_lens_host=inp["seq_lens"])
+                      chunk_tokens=chunk_tokens, seq_lens_host=inp["seq_lens"],
+                      out_dtype=out_dtype)
     return T, cache, step
 
 

@@ -700,6 +700,12 @@ STEP_POSITIONS = [
     ("bf16-paged-split-behind", 3, dict(), [0, 64, 128, 200, 4095, 4096], "behind", 4),
     ("bf16-paged-split-8", 3, dict(), [5, 1000, 3000, 9000], "next", 8),
     ("fp8-paged-split-8", 4, dict(), [1, 700, 4000, 8191], "next", 8),
+    # balanced: workgroups holding many whole rows, rows shared by several
+    # workgroups, empty rows among the others (the combine in the attention
+    # launch against the separate combine)
+    ("bf16-paged-bal-short-rows", 3, dict(batch=1024), [20000] + [1, 0, 70] * 341, "next", 0),
+    ("bf16-paged-bal-empty-mix", 3, dict(batch=300), [0, 5000, 0, 64, 1] * 60, "behind", 0),
+    ("fp8-paged-bal-1024", 4, dict(batch=1024), _ragged(1023, 97, top=300) + [9000], "next", 0),
 ]
 
 
@@ -730,6 +736,25 @@ def test_step_positions_match_staged(gpu_lib, name, base, over, lens, mode, spli
         assert np.array_equal(a, b)
     if mode == "next":
         check_bf16(to_np(outs[0]), orun.decode_step(inp)["o"], f"step positions {name}")
+
+
+def test_step_balanced_f32_out(gpu_lib):
+    """The balanced step with an fp32 output (the combine in the attention
+    launch writes fp32) against the separate calls, bit for bit, and within
+    the bars of the oracle."""
+    lens = _ragged(48, 97, top=3000) + [0, 1, 64]
+    w = small(3, batch=len(lens))
+    inp = workloads.make_inputs(3, workload=w, prefill_lens=lens, seed=353)
+    say("balanced step, fp32 output")
+    outs = []
+    for fused in (True, False):
+        T, cache, step = setup(inp, num_splits=0, out_dtype=torch.float32)
+        fn = step if fused else step.staged
+        outs.append(fn(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"]).clone())
+        torch.cuda.synchronize()
+    assert outs[0].dtype == torch.float32
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    check_bf16(to_np(outs[0]), orun.decode_step(inp)["o"], "balanced step fp32 out")
 
 
 @pytest.mark.parametrize("idx,shrink,packed", [

@@ -758,7 +758,8 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(
         const size_t i = static_cast<size_t>(rr) * kD + 4 * lane;
         akw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.app.k_new) + i);
         avw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.app.v_new) + i);
-        // an owner walks the token's block, so (a_p >> 6) is a block of the table row
+        // an owner walks the token's block, so (a_p >> 6) is a block of the
+        // table row; a contiguous cache needs no entry (pos[0] is read instead)
         const int* tp = a.app.block_table
                             ? a.app.block_table + static_cast<size_t>(rr) * a.app.max_blocks_per_seq +
                                   (a_r >= 0 ? (a_p >> 6) : 0)
@@ -816,7 +817,7 @@ __global__ __launch_bounds__(512) void mfa_decode_mfma_kernel(
     // before it leaves R-1 blocks outstanding.
     prologue_qk(std::integral_constant<int, R>{}, issue, app_pre, app_mid);
     if constexpr (APP) {
-      if (!a_done) app_store();          // the first unit holding one comes after the prologue
+      if (!a_done) app_store();          // the token's unit is issued after the prologue
     }
     __syncthreads();   // Q staged
     if constexpr (Q8) {

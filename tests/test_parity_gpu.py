@@ -285,6 +285,42 @@ def test_balanced_static_and_graph(gpu_lib):
     check_bf16(to_np(eager), orun.decode_step(inp)["o"], "balanced graph step")
 
 
+@pytest.mark.parametrize("base,over,lens,splits", [
+    (3, dict(), [1, 62, 64, 300, 777, 2000], 3),
+    (4, dict(), [0, 63, 190, 513, 1500], 4),
+], ids=["bf16-split", "fp8-split"])
+def test_graph_replay_append_in_attention(gpu_lib, base, over, lens, splits):
+    """The step without a query path on a split plan (the KV append inside
+    the attention launch) captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, equals the eager step bit for bit,
+    output and cache."""
+    w = small(base, **over)
+    inp = workloads.make_inputs(base, workload=w, prefill_lens=lens, seed=359 + base)
+    T, cache, step = setup(inp, num_splits=splits)
+    say(f"graph replay, append in the attention launch, base={base} splits={splits}")
+    _, eager = run(T, step)
+    eager = eager.clone()
+    rows = [r.copy() for r in cache_rows(cache)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step(T["k_new"], T["v_new"], T["prefill_lens"], T["seq_lens"], q=T["q"])
+    for r in range(3):
+        step.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        for a_, b_ in zip(cache_rows(cache), rows):
+            assert np.array_equal(a_, b_), f"replay {r} cache"
+    check_bf16(to_np(eager), orun.decode_step(inp)["o"], "graph step, append in attention")
+
+
 def test_small_f32_generic(gpu_lib):
     """fp32 cache and q on the vector-ALU kernel, ragged lengths, 1 and 3 splits."""
     w = small(1, hidden=None, q_rank=None)
